@@ -1,0 +1,181 @@
+/*
+ * sttd.h - C ABI of the MI355X (gfx950) Qwen3-style decoder-block library.
+ *
+ * The operation is the shared causal-LM block that transcribe.cpp's
+ * Qwen3-ASR and Canary-Qwen handlers drive in a prefill and a per-token
+ * step loop (Qwen3-ASR decoder page, transcribe-cpp-sys 0.2.0,
+ * src/arch/qwen3_asr/decoder.cpp: file header, build_prefill_graph,
+ * build_step_graph). One block is pre-LN RMSNorm, grouped-query attention
+ * with per-head Q/K RMSNorm, NeoX RoPE, a KV-cache write then read, the
+ * output projection with a residual add, and SwiGLU on one packed gate_up
+ * projection followed by the down projection with a residual add. After
+ * the stack: a final RMSNorm, the tied lm_head and a greedy argmax.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless marked (host). Structs passed by
+ *    pointer are host structs; sttd_block_weights holds device pointers.
+ *  - The caller owns weights, activations, positions, ids and logits.
+ *    The library owns what sttd_kv_cache_alloc / sttd_workspace_alloc
+ *    allocate until the matching free.
+ *  - Calls enqueue work on `stream` (a hipStream_t; NULL = the default
+ *    stream) and return without synchronising. They make no host read of
+ *    device data, so the block, step and head calls can be captured in a
+ *    HIP graph.
+ *  - Host-visible arguments are validated before anything is enqueued.
+ *    Invalid arguments return an error and enqueue nothing. Device-resident
+ *    values (positions, slab ids, token ids) cannot be checked on the host:
+ *    kernels check them, skip the out-of-range row, and record an error
+ *    code in the workspace (sttd_workspace_error reads it).
+ *  - A launch failure returns STTD_ERR_BACKEND. No C++ exception crosses
+ *    the ABI. Two calls that touch one KV cache or one workspace must be
+ *    ordered (same stream); distinct handles are independent.
+ *
+ * Weight layout (row-major, [out, in]; no biases - the block's ten weight
+ * slots, to_block_view on the decoder page):
+ *   attn_norm[H]  wq[nq*d, H]  wk[nkv*d, H]  wv[nkv*d, H]
+ *   q_norm[d]  k_norm[d]  (one gain vector shared by all heads)
+ *   wo[H, nq*d]  ffn_norm[H]
+ *   w_gate_up[2*I, H]: rows 0..I-1 are the gate, rows I..2I-1 the up
+ *     projection (the packed tensor of pack_gate_up, Qwen3-ASR model page,
+ *     load(); the row order is this ABI's contract)
+ *   w_down[H, I]
+ * Every matrix and gain has the storage type `wtype` (STTD_BF16 or STTD_F32).
+ * Hidden states x are fp32 [rows, H], row-major.
+ */
+#ifndef STTD_H
+#define STTD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    STTD_OK = 0,
+    STTD_ERR_INVALID_ARG = 1,  /* null pointer, bad size, layer/slab out of range */
+    STTD_ERR_OOM = 2,          /* device allocation failed */
+    STTD_ERR_BACKEND = 3,      /* a HIP call or kernel launch failed */
+    STTD_ERR_CONTEXT_FULL = 4, /* positions would pass the cache's n_ctx */
+    STTD_ERR_UNSUPPORTED = 5   /* shape or dtype combination not built */
+} sttd_status;
+
+typedef enum { STTD_F32 = 0, STTD_BF16 = 1, STTD_F16 = 2 } sttd_dtype;
+
+/* Block shape (to_block_params on the decoder page). head_dim must be 64 or
+ * 128; n_heads a multiple of n_kv_heads; hidden and ffn multiples of 128. */
+typedef struct {
+    int32_t hidden, n_heads, n_kv_heads, head_dim, ffn;
+    float rms_eps;    /* RMSNorm epsilon, inside the square root */
+    float rope_theta; /* NeoX RoPE base: pair i turns by pos * theta^(-2i/d) */
+    sttd_dtype wtype; /* STTD_BF16 or STTD_F32 */
+} sttd_block_params;
+
+/* Host struct of device pointers to one block's ten weight tensors. */
+typedef struct {
+    const void *attn_norm, *wq, *wk, *wv, *q_norm, *k_norm, *wo, *ffn_norm, *w_gate_up, *w_down;
+} sttd_block_weights;
+
+typedef struct sttd_kv_cache sttd_kv_cache;   /* opaque */
+typedef struct sttd_workspace sttd_workspace; /* opaque */
+
+/* Device-side error codes recorded in a workspace (sttd_workspace_error). */
+#define STTD_DEVERR_POSITION 1u /* a position was < 0 or >= the cache's n_ctx */
+#define STTD_DEVERR_SLAB 2u     /* a slab id was < 0 or >= the cache's n_seq */
+#define STTD_DEVERR_TOKEN 4u    /* a token id was < 0 or >= vocab */
+
+/* block_prefill flag: the FFN (and so the block output) is computed for the
+ * last row only; rows 0..T-2 of x are left holding the attention residual
+ * h = x + o * Wo^T. The slice_last_before_ffn option of the decoder page's
+ * build_prefill_graph, for the stack's last block. */
+#define STTD_LAST_ROW_FFN_ONLY 1u
+
+const char *sttd_status_string(sttd_status s);
+
+/* ---------------------------------------------------------------- KV cache
+ * One K and one V slab per (layer, sequence): kv_init / kv_init_batched on
+ * the Qwen3-ASR model page (run(), run_batch()) size it as n_ctx rows of
+ * n_kv_heads * head_dim per layer; one token holds
+ * n_kv_heads * head_dim * n_layers * 2 elements (load(), session limits).
+ * Layout: [layer][seq][kv_head][n_ctx][head_dim], K and V in two buffers.
+ * The row index of a token is its position. kv_type: STTD_F16 or STTD_F32.
+ * The memory is zeroed at allocation. */
+sttd_status sttd_kv_cache_alloc(int n_layers, int n_seq, int n_ctx, int n_kv_heads, int head_dim,
+                                sttd_dtype kv_type, sttd_kv_cache **out /* host */);
+sttd_status sttd_kv_cache_free(sttd_kv_cache *kv);
+/* Zero every slab (the buffer clear before a fresh prefill, run() on the
+ * Qwen3-ASR model page). Enqueued as a fill kernel on `stream`. */
+sttd_status sttd_kv_cache_clear(sttd_kv_cache *kv, void *stream);
+/* Device pointers to the K and V slab of (layer, seq) and its element strides
+ * between kv heads and between positions. For tests and fills. */
+sttd_status sttd_kv_cache_view(const sttd_kv_cache *kv, int layer, int seq, void **k /* host */,
+                               void **v /* host */, int64_t *head_stride /* host */,
+                               int64_t *pos_stride /* host */);
+
+/* ---------------------------------------------------------------- workspace
+ * Scratch for the block and head calls (projections, attention partials,
+ * argmax slots, the RoPE table), sized for up to max_rows rows per call,
+ * positions < max_pos and a vocabulary of up to `vocab` rows (0: no head).
+ * The RoPE table is computed on the host in fp64 and stored in fp32:
+ * cos and sin of pos * theta^(-2i/d) for i < d/2. Allocating it is a
+ * synchronous call. */
+sttd_status sttd_workspace_alloc(const sttd_block_params *p /* host */, int max_rows, int max_pos, int vocab,
+                                 sttd_workspace **out /* host */);
+sttd_status sttd_workspace_free(sttd_workspace *ws);
+/* Synchronising read of the device error bits (STTD_DEVERR_*) recorded since
+ * the last call, which also clears them. Not for use under graph capture. */
+sttd_status sttd_workspace_error(sttd_workspace *ws, uint32_t *bits /* host */);
+
+/* ---------------------------------------------------------------- calls */
+
+/* Token-embedding gather (ggml_get_rows on the tied table in the decoder
+ * page's build_step_graph): x[b, :] = fp32(embed[ids[b], :]) for b < B.
+ * embed [vocab, hidden] of storage type wtype; ids [B] int32; x [B, hidden].
+ * A device id outside [0, vocab) writes a zero row and records
+ * STTD_DEVERR_TOKEN when ws is non-NULL. */
+sttd_status sttd_embed_gather(const void *embed, sttd_dtype wtype, int vocab, int hidden, int B,
+                              const int32_t *ids, float *x, sttd_workspace *ws, void *stream);
+
+/* Causal prefill of T rows of one sequence through one block
+ * (causal_lm::block_prefill as called by build_prefill_graph).
+ * Row t sits at position pos0 + t; its K and V are written at cache row
+ * pos0 + t of slab `seq` in layer `layer`; it attends cache rows
+ * [0, pos0 + t] (rows below pos0 must hold earlier positions, e.g. an
+ * earlier chunk). x [T, hidden] fp32 is read and overwritten with the
+ * block output (see STTD_LAST_ROW_FFN_ONLY). Requires 1 <= T <= the
+ * workspace's max_rows; pos0 + T > n_ctx returns STTD_ERR_CONTEXT_FULL. */
+sttd_status sttd_block_prefill(const sttd_block_params *p, const sttd_block_weights *w, sttd_workspace *ws,
+                               sttd_kv_cache *kv, int layer, int seq, int pos0, int T, float *x, uint32_t flags,
+                               void *stream);
+
+/* One decode step of B rows through one block (causal_lm::block_step and
+ * block_step_batched in build_step_graph / build_step_graph_batched).
+ * Row b is at position pos[b] (device int32 [B]) of slab seq[b] (device
+ * int32 [B], or NULL for slab b); rows must name distinct slabs. Its K, V
+ * go to cache row pos[b]; it attends rows [0, pos[b]]. pos_bound (host) is
+ * an upper bound on every pos[b] + 1 (<= n_ctx) used to size the launch;
+ * the work done follows the actual pos[b]. x [B, hidden] fp32 in/out.
+ * 1 <= B <= max_rows. */
+sttd_status sttd_block_step(const sttd_block_params *p, const sttd_block_weights *w, sttd_workspace *ws,
+                            sttd_kv_cache *kv, int layer, int B, const int32_t *seq, const int32_t *pos,
+                            int pos_bound, float *x, void *stream);
+
+/* Final RMSNorm, tied lm_head and greedy argmax over B rows (the tail of
+ * build_step_graph; the host argmax in run() on the Qwen3-ASR model page
+ * keeps the lowest index on ties, and so does this call; a NaN logit never
+ * wins). x rows are read at x + b * x_row_stride (floats), so the last
+ * prefill row can be passed directly. final_norm [hidden], embed
+ * [vocab, hidden] (storage wtype). Outputs: ids [B] int32; optional logits
+ * [B, vocab] fp32 (NULL: not written); optional next_x [B, hidden] fp32 =
+ * embed[ids[b]] (the next step's input rows); optional pos [B] int32
+ * incremented by one after the step (device-resident step counter). */
+sttd_status sttd_lm_head_argmax(const void *final_norm, const void *embed, sttd_dtype wtype, int vocab, int hidden,
+                                float rms_eps, sttd_workspace *ws, int B, const float *x, int64_t x_row_stride,
+                                int32_t *ids, float *logits, float *next_x, int32_t *pos, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STTD_H */

@@ -1,0 +1,418 @@
+// abi.hip - the C ABI of include/sttd.h: validation, allocation, and the
+// kernel sequences of one block call.
+#include <math.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "launch.h"
+#include "sttd.h"
+
+using namespace sttd;
+
+struct sttd_kv_cache {
+    int n_layers, n_seq, n_ctx, n_kv, d;
+    sttd_dtype type;
+    size_t elem;
+    void* k;
+    void* v;
+};
+
+struct sttd_workspace {
+    sttd_block_params p;
+    int max_rows, max_pos, vocab;
+    int part_cap;  // (row, split) slots of the attention partials
+    void* base;
+    size_t bytes;
+    float* rope;        // [max_pos][d/2][2]
+    uint16_t* xn;       // [max_rows][hidden] bf16 (normed rows for the MFMA GEMMs)
+    float* qkv;         // [max_rows][(nq + 2 nkv) d]
+    void* qbuf;         // [max_rows][nq d] fp32 (or f16)
+    float* attn_o;      // [max_rows][nq d] fp32 (or bf16)
+    float* act;         // [max_rows][ffn] fp32 (or bf16)
+    float* part;        // [part_cap][nq][d + 2]
+    unsigned long long* slots;  // [max_rows]
+    uint32_t* counters;         // [max_rows / 4 + 1]
+    uint32_t* err;              // [1]
+};
+
+namespace {
+
+constexpr int kGemvMaxRows = 4;  // rows beyond this take the MFMA GEMMs (bf16 weights)
+constexpr int kMaxSplits = 64;
+
+sttd_status from_hip(hipError_t e) {
+    if (e == hipSuccess) return STTD_OK;
+    if (e == hipErrorOutOfMemory) return STTD_ERR_OOM;
+    return STTD_ERR_BACKEND;
+}
+
+#define TRY(expr)                                  \
+    do {                                           \
+        hipError_t e_ = (expr);                    \
+        if (e_ != hipSuccess) return from_hip(e_); \
+    } while (0)
+
+bool params_ok(const sttd_block_params* p) {
+    if (!p) return false;
+    if (p->hidden <= 0 || p->n_heads <= 0 || p->n_kv_heads <= 0 || p->ffn <= 0) return false;
+    if (p->n_heads % p->n_kv_heads) return false;
+    if (!(p->rms_eps >= 0.f) || !(p->rope_theta > 0.f)) return false;
+    return true;
+}
+
+sttd_status params_supported(const sttd_block_params* p) {
+    if (p->head_dim != 64 && p->head_dim != 128) return STTD_ERR_UNSUPPORTED;
+    if (p->hidden % 64 || p->ffn % 64) return STTD_ERR_UNSUPPORTED;
+    const int g = p->n_heads / p->n_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8) return STTD_ERR_UNSUPPORTED;
+    if (p->wtype != STTD_BF16 && p->wtype != STTD_F32) return STTD_ERR_UNSUPPORTED;
+    return STTD_OK;
+}
+
+bool same_shape(const sttd_block_params* a, const sttd_block_params* b) {
+    return a->hidden == b->hidden && a->n_heads == b->n_heads && a->n_kv_heads == b->n_kv_heads &&
+           a->head_dim == b->head_dim && a->ffn == b->ffn && a->wtype == b->wtype;
+}
+
+bool weights_ok(const sttd_block_weights* w) {
+    return w && w->attn_norm && w->wq && w->wk && w->wv && w->q_norm && w->k_norm && w->wo && w->ffn_norm &&
+           w->w_gate_up && w->w_down;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+KVLayer kv_layer(const sttd_kv_cache* kv, int layer) {
+    KVLayer l;
+    const size_t per_layer = (size_t)kv->n_seq * kv->n_kv * kv->n_ctx * kv->d * kv->elem;
+    l.k = (char*)kv->k + per_layer * layer;
+    l.v = (char*)kv->v + per_layer * layer;
+    l.n_seq = kv->n_seq;
+    l.n_kv = kv->n_kv;
+    l.n_ctx = kv->n_ctx;
+    l.d = kv->d;
+    l.type = kv->type == STTD_F16 ? KV_F16 : KV_F32;
+    return l;
+}
+
+int choose_splits(int rows, int pos_bound, int part_cap) {
+    int s = (pos_bound + 63) / 64;
+    if (s > kMaxSplits) s = kMaxSplits;
+    if (s > part_cap / rows) s = part_cap / rows;
+    return s < 1 ? 1 : s;
+}
+
+// One block over R rows. prefill_seq >= 0: a causal prefill of one slab at
+// positions rm.pos0.. (may use the MFMA flash kernel); otherwise decode rows.
+sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, sttd_workspace* ws,
+                      const sttd_kv_cache* kv, int layer, int R, RowMap rm, int pos_bound, bool prefill,
+                      bool last_row_only, float* x, hipStream_t s) {
+    const WType wt = p->wtype == STTD_BF16 ? W_BF16 : W_F32;
+    const int H = p->hidden, nq = p->n_heads, nkv = p->n_kv_heads, d = p->head_dim, I = p->ffn;
+    const int qd = nq * d, kvd = nkv * d, qkv_cols = qd + 2 * kvd;
+    const float eps = p->rms_eps;
+    const KVLayer kl = kv_layer(kv, layer);
+    const bool mfma = wt == W_BF16 && R > kGemvMaxRows;
+    const bool flash = mfma && prefill && kl.type == KV_F16;
+
+    // --- attention half: norm + QKV projection
+    if (mfma) {
+        TRY(launch_rmsnorm_rows_bf16(x, H, w->attn_norm, wt, ws->xn, H, R, H, eps, s));
+        GemmArgs g{};
+        g.A = ws->xn; g.lda = H; g.M = R; g.K = H;
+        g.w[0] = (const uint16_t*)w->wq; g.w[1] = (const uint16_t*)w->wk; g.w[2] = (const uint16_t*)w->wv;
+        g.seg_end[0] = qd; g.seg_end[1] = qd + kvd; g.seg_end[2] = qkv_cols;
+        g.N = qkv_cols; g.C = ws->qkv; g.ldc = qkv_cols;
+        TRY(launch_gemm(g, GEMM_STORE, s));
+    } else {
+        GemvArgs a{};
+        a.w[0] = w->wq; a.w[1] = w->wk; a.w[2] = w->wv;
+        a.seg_end[0] = qd; a.seg_end[1] = qd + kvd; a.seg_end[2] = qkv_cols;
+        a.N = qkv_cols; a.K = H; a.x = x; a.ldx = H; a.rows = R; a.gain = w->attn_norm; a.eps = eps;
+        a.y = ws->qkv; a.ldy = qkv_cols;
+        TRY(launch_gemv(a, wt, GEMV_STORE, s));
+    }
+    // --- per-head Q/K norm, RoPE, cache write
+    TRY(launch_qk_norm_rope_kv(ws->qkv, qkv_cols, R, nq, nkv, d, w->q_norm, w->k_norm, wt, eps, ws->rope,
+                               ws->max_pos, rm, kl, ws->qbuf, flash, qd, ws->err, s));
+    // --- attention
+    if (flash) {
+        TRY(launch_attn_prefill((const uint16_t*)ws->qbuf, qd, R, rm.pos0, rm.seq0, nq, kl, (uint16_t*)ws->attn_o,
+                                qd, s));
+    } else {
+        const int splits = choose_splits(R, pos_bound, ws->part_cap);
+        TRY(launch_attn_rows((const float*)ws->qbuf, qd, R, nq, rm, kl, splits, ws->part,
+                             mfma ? nullptr : ws->attn_o, mfma ? (uint16_t*)ws->attn_o : nullptr, qd, ws->err, s));
+    }
+    // --- O projection + residual
+    if (mfma) {
+        GemmArgs g{};
+        g.A = (const uint16_t*)ws->attn_o; g.lda = qd; g.M = R; g.K = qd;
+        g.w[0] = (const uint16_t*)w->wo; g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = H;
+        g.N = H; g.C = x; g.ldc = H;
+        TRY(launch_gemm(g, GEMM_RESID, s));
+    } else {
+        GemvArgs a{};
+        a.w[0] = w->wo; a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = H;
+        a.N = H; a.K = qd; a.x = ws->attn_o; a.ldx = qd; a.rows = R; a.y = x; a.ldy = H; a.resid = x; a.ldr = H;
+        TRY(launch_gemv(a, wt, GEMV_RESID, s));
+    }
+    // --- FFN: norm, packed gate_up + SwiGLU, down + residual
+    const int r0 = last_row_only ? R - 1 : 0;
+    const int nr = last_row_only ? 1 : R;
+    float* xf = x + (int64_t)r0 * H;
+    if (mfma && nr > kGemvMaxRows) {
+        TRY(launch_rmsnorm_rows_bf16(xf, H, w->ffn_norm, wt, ws->xn, H, nr, H, eps, s));
+        GemmArgs g{};
+        g.A = ws->xn; g.lda = H; g.M = nr; g.K = H;
+        g.w[0] = (const uint16_t*)w->w_gate_up; g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = 2 * I;
+        g.N = I; g.Cb = (uint16_t*)ws->act; g.ldcb = I;
+        TRY(launch_gemm(g, GEMM_SWIGLU, s));
+        GemmArgs g2{};
+        g2.A = (const uint16_t*)ws->act; g2.lda = I; g2.M = nr; g2.K = I;
+        g2.w[0] = (const uint16_t*)w->w_down; g2.seg_end[0] = g2.seg_end[1] = g2.seg_end[2] = H;
+        g2.N = H; g2.C = xf; g2.ldc = H;
+        TRY(launch_gemm(g2, GEMM_RESID, s));
+    } else {
+        GemvArgs a{};
+        a.w[0] = w->w_gate_up; a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = I;
+        a.N = I; a.K = H; a.x = xf; a.ldx = H; a.rows = nr; a.gain = w->ffn_norm; a.eps = eps;
+        a.y = ws->act; a.ldy = I;
+        TRY(launch_gemv(a, wt, GEMV_SWIGLU, s));
+        GemvArgs b{};
+        b.w[0] = w->w_down; b.seg_end[0] = b.seg_end[1] = b.seg_end[2] = H;
+        b.N = H; b.K = I; b.x = ws->act; b.ldx = I; b.rows = nr; b.y = xf; b.ldy = H; b.resid = xf; b.ldr = H;
+        TRY(launch_gemv(b, wt, GEMV_RESID, s));
+    }
+    return STTD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sttd_status_string(sttd_status s) {
+    switch (s) {
+        case STTD_OK: return "ok";
+        case STTD_ERR_INVALID_ARG: return "invalid argument";
+        case STTD_ERR_OOM: return "out of device memory";
+        case STTD_ERR_BACKEND: return "HIP call or kernel launch failed";
+        case STTD_ERR_CONTEXT_FULL: return "positions pass the KV cache's n_ctx";
+        case STTD_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    }
+    return "unknown status";
+}
+
+sttd_status sttd_kv_cache_alloc(int n_layers, int n_seq, int n_ctx, int n_kv_heads, int head_dim, sttd_dtype kv_type,
+                                sttd_kv_cache** out) {
+    if (!out) return STTD_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (n_layers <= 0 || n_seq <= 0 || n_ctx <= 0 || n_kv_heads <= 0 || head_dim <= 0) return STTD_ERR_INVALID_ARG;
+    if (kv_type != STTD_F16 && kv_type != STTD_F32) return STTD_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return STTD_ERR_UNSUPPORTED;
+    const size_t elem = kv_type == STTD_F16 ? 2 : 4;
+    const double total = (double)n_layers * n_seq * n_ctx * n_kv_heads * head_dim * elem;
+    if (total > 1e15) return STTD_ERR_OOM;
+    const size_t bytes = (size_t)n_layers * n_seq * n_ctx * n_kv_heads * head_dim * elem;
+    sttd_kv_cache* kv = new (std::nothrow) sttd_kv_cache();
+    if (!kv) return STTD_ERR_OOM;
+    kv->n_layers = n_layers; kv->n_seq = n_seq; kv->n_ctx = n_ctx; kv->n_kv = n_kv_heads; kv->d = head_dim;
+    kv->type = kv_type; kv->elem = elem;
+    if (hipMalloc(&kv->k, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        delete kv;
+        return STTD_ERR_OOM;
+    }
+    if (hipMalloc(&kv->v, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipFree(kv->k);
+        delete kv;
+        return STTD_ERR_OOM;
+    }
+    if (hipMemset(kv->k, 0, bytes) != hipSuccess || hipMemset(kv->v, 0, bytes) != hipSuccess) {
+        (void)hipFree(kv->k);
+        (void)hipFree(kv->v);
+        delete kv;
+        return STTD_ERR_BACKEND;
+    }
+    *out = kv;
+    return STTD_OK;
+}
+
+sttd_status sttd_kv_cache_free(sttd_kv_cache* kv) {
+    if (!kv) return STTD_ERR_INVALID_ARG;
+    const hipError_t a = hipFree(kv->k), b = hipFree(kv->v);
+    delete kv;
+    return (a == hipSuccess && b == hipSuccess) ? STTD_OK : STTD_ERR_BACKEND;
+}
+
+sttd_status sttd_kv_cache_clear(sttd_kv_cache* kv, void* stream) {
+    if (!kv) return STTD_ERR_INVALID_ARG;
+    const size_t bytes = (size_t)kv->n_layers * kv->n_seq * kv->n_ctx * kv->n_kv * kv->d * kv->elem;
+    TRY(launch_fill_zero(kv->k, bytes, (hipStream_t)stream));
+    TRY(launch_fill_zero(kv->v, bytes, (hipStream_t)stream));
+    return STTD_OK;
+}
+
+sttd_status sttd_kv_cache_view(const sttd_kv_cache* kv, int layer, int seq, void** k, void** v, int64_t* head_stride,
+                               int64_t* pos_stride) {
+    if (!kv || !k || !v || !head_stride || !pos_stride) return STTD_ERR_INVALID_ARG;
+    if (layer < 0 || layer >= kv->n_layers || seq < 0 || seq >= kv->n_seq) return STTD_ERR_INVALID_ARG;
+    const KVLayer l = kv_layer(kv, layer);
+    const size_t off = (size_t)seq * kv->n_kv * kv->n_ctx * kv->d * kv->elem;
+    *k = (char*)l.k + off;
+    *v = (char*)l.v + off;
+    *head_stride = (int64_t)kv->n_ctx * kv->d;
+    *pos_stride = kv->d;
+    return STTD_OK;
+}
+
+sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int max_pos, int vocab,
+                                 sttd_workspace** out) {
+    if (!out) return STTD_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (!params_ok(p) || max_rows <= 0 || max_pos <= 0 || vocab < 0) return STTD_ERR_INVALID_ARG;
+    const sttd_status sup = params_supported(p);
+    if (sup != STTD_OK) return sup;
+    const int H = p->hidden, nq = p->n_heads, nkv = p->n_kv_heads, d = p->head_dim, I = p->ffn;
+    const size_t R = (size_t)max_rows;
+    const int part_cap = max_rows > 64 * kMaxSplits ? max_rows : 64 * kMaxSplits;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    const size_t o_rope = take((size_t)max_pos * d * sizeof(float));
+    const size_t o_xn = take(R * H * 2);
+    const size_t o_qkv = take(R * (nq + 2 * nkv) * d * sizeof(float));
+    const size_t o_q = take(R * nq * d * sizeof(float));
+    const size_t o_ao = take(R * nq * d * sizeof(float));
+    const size_t o_act = take(R * I * sizeof(float));
+    const size_t o_part = take((size_t)part_cap * nq * (d + 2) * sizeof(float));
+    const size_t o_slots = take(R * sizeof(unsigned long long));
+    const size_t o_cnt = take((R / 4 + 1) * sizeof(uint32_t));
+    const size_t o_err = take(sizeof(uint32_t));
+    sttd_workspace* ws = new (std::nothrow) sttd_workspace();
+    if (!ws) return STTD_ERR_OOM;
+    ws->p = *p;
+    ws->max_rows = max_rows;
+    ws->max_pos = max_pos;
+    ws->vocab = vocab;
+    ws->part_cap = part_cap;
+    ws->bytes = off;
+    if (hipMalloc(&ws->base, off) != hipSuccess) {
+        (void)hipGetLastError();
+        delete ws;
+        return STTD_ERR_OOM;
+    }
+    char* b = (char*)ws->base;
+    ws->rope = (float*)(b + o_rope);
+    ws->xn = (uint16_t*)(b + o_xn);
+    ws->qkv = (float*)(b + o_qkv);
+    ws->qbuf = b + o_q;
+    ws->attn_o = (float*)(b + o_ao);
+    ws->act = (float*)(b + o_act);
+    ws->part = (float*)(b + o_part);
+    ws->slots = (unsigned long long*)(b + o_slots);
+    ws->counters = (uint32_t*)(b + o_cnt);
+    ws->err = (uint32_t*)(b + o_err);
+    // RoPE table in fp64 on the host: pair i of position pos turns by pos * theta^(-2i/d)
+    std::vector<float> table((size_t)max_pos * d);
+    const int half = d / 2;
+    for (int i = 0; i < half; ++i) {
+        const double omega = pow((double)p->rope_theta, -2.0 * i / d);
+        for (int pos = 0; pos < max_pos; ++pos) {
+            const double a = pos * omega;
+            table[((size_t)pos * half + i) * 2] = (float)cos(a);
+            table[((size_t)pos * half + i) * 2 + 1] = (float)sin(a);
+        }
+    }
+    if (hipMemset(ws->base, 0, off) != hipSuccess ||
+        hipMemcpy(ws->rope, table.data(), table.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(ws->base);
+        delete ws;
+        return STTD_ERR_BACKEND;
+    }
+    *out = ws;
+    return STTD_OK;
+}
+
+sttd_status sttd_workspace_free(sttd_workspace* ws) {
+    if (!ws) return STTD_ERR_INVALID_ARG;
+    const hipError_t e = hipFree(ws->base);
+    delete ws;
+    return e == hipSuccess ? STTD_OK : STTD_ERR_BACKEND;
+}
+
+sttd_status sttd_workspace_error(sttd_workspace* ws, uint32_t* bits) {
+    if (!ws || !bits) return STTD_ERR_INVALID_ARG;
+    TRY(hipDeviceSynchronize());
+    TRY(hipMemcpy(bits, ws->err, sizeof(uint32_t), hipMemcpyDeviceToHost));
+    TRY(hipMemset(ws->err, 0, sizeof(uint32_t)));
+    return STTD_OK;
+}
+
+sttd_status sttd_embed_gather(const void* embed, sttd_dtype wtype, int vocab, int hidden, int B, const int32_t* ids,
+                              float* x, sttd_workspace* ws, void* stream) {
+    if (!embed || !ids || !x || vocab <= 0 || hidden <= 0 || B <= 0) return STTD_ERR_INVALID_ARG;
+    if (wtype != STTD_BF16 && wtype != STTD_F32) return STTD_ERR_UNSUPPORTED;
+    TRY(launch_embed_gather(embed, wtype == STTD_BF16 ? W_BF16 : W_F32, vocab, hidden, B, ids, x,
+                            ws ? ws->err : nullptr, (hipStream_t)stream));
+    return STTD_OK;
+}
+
+static sttd_status check_block(const sttd_block_params* p, const sttd_block_weights* w, const sttd_workspace* ws,
+                               const sttd_kv_cache* kv, int layer, int rows, const float* x) {
+    if (!params_ok(p) || !weights_ok(w) || !ws || !kv || !x) return STTD_ERR_INVALID_ARG;
+    const sttd_status sup = params_supported(p);
+    if (sup != STTD_OK) return sup;
+    if (!same_shape(p, &ws->p)) return STTD_ERR_INVALID_ARG;
+    if (kv->n_kv != p->n_kv_heads || kv->d != p->head_dim) return STTD_ERR_INVALID_ARG;
+    if (layer < 0 || layer >= kv->n_layers) return STTD_ERR_INVALID_ARG;
+    if (rows <= 0 || rows > ws->max_rows) return STTD_ERR_INVALID_ARG;
+    return STTD_OK;
+}
+
+sttd_status sttd_block_prefill(const sttd_block_params* p, const sttd_block_weights* w, sttd_workspace* ws,
+                               sttd_kv_cache* kv, int layer, int seq, int pos0, int T, float* x, uint32_t flags,
+                               void* stream) {
+    const sttd_status st = check_block(p, w, ws, kv, layer, T, x);
+    if (st != STTD_OK) return st;
+    if (seq < 0 || seq >= kv->n_seq || pos0 < 0) return STTD_ERR_INVALID_ARG;
+    if ((int64_t)pos0 + T > kv->n_ctx || (int64_t)pos0 + T > ws->max_pos) return STTD_ERR_CONTEXT_FULL;
+    if (flags & ~(uint32_t)STTD_LAST_ROW_FFN_ONLY) return STTD_ERR_INVALID_ARG;
+    RowMap rm{nullptr, nullptr, pos0, seq};
+    return run_block(p, w, ws, kv, layer, T, rm, pos0 + T, true, (flags & STTD_LAST_ROW_FFN_ONLY) != 0, x,
+                     (hipStream_t)stream);
+}
+
+sttd_status sttd_block_step(const sttd_block_params* p, const sttd_block_weights* w, sttd_workspace* ws,
+                            sttd_kv_cache* kv, int layer, int B, const int32_t* seq, const int32_t* pos,
+                            int pos_bound, float* x, void* stream) {
+    const sttd_status st = check_block(p, w, ws, kv, layer, B, x);
+    if (st != STTD_OK) return st;
+    if (!pos || pos_bound <= 0) return STTD_ERR_INVALID_ARG;
+    if (pos_bound > kv->n_ctx || pos_bound > ws->max_pos) return STTD_ERR_CONTEXT_FULL;
+    if (!seq && B > kv->n_seq) return STTD_ERR_INVALID_ARG;
+    RowMap rm{pos, seq, 0, -1};
+    return run_block(p, w, ws, kv, layer, B, rm, pos_bound, false, false, x, (hipStream_t)stream);
+}
+
+sttd_status sttd_lm_head_argmax(const void* final_norm, const void* embed, sttd_dtype wtype, int vocab, int hidden,
+                                float rms_eps, sttd_workspace* ws, int B, const float* x, int64_t x_row_stride,
+                                int32_t* ids, float* logits, float* next_x, int32_t* pos, void* stream) {
+    if (!final_norm || !embed || !ws || !x || !ids || vocab <= 0 || hidden <= 0 || B <= 0) return STTD_ERR_INVALID_ARG;
+    if (wtype != STTD_BF16 && wtype != STTD_F32) return STTD_ERR_UNSUPPORTED;
+    if (hidden % 64) return STTD_ERR_UNSUPPORTED;
+    if (B > ws->max_rows || vocab > ws->vocab || x_row_stride < hidden) return STTD_ERR_INVALID_ARG;
+    HeadArgs a{};
+    a.gain = final_norm; a.embed = embed; a.vocab = vocab; a.hidden = hidden; a.eps = rms_eps;
+    a.x = x; a.ldx = x_row_stride; a.rows = B; a.ids = ids; a.logits = logits; a.next_x = next_x; a.pos = pos;
+    a.slots = ws->slots; a.counters = ws->counters; a.err = ws->err;
+    TRY(launch_lm_head_argmax(a, wtype == STTD_BF16 ? W_BF16 : W_F32, (hipStream_t)stream));
+    return STTD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// common.h - device helpers shared by the gfx950 kernels of the decoder block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define WAVE 64
+
+// ------------------------------------------------------------ conversions
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    __bf16 h = (__bf16)f;  // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// Storage-type tags: loads widen to fp32, stores round to nearest even.
+struct F32 {
+    typedef float T;
+    static __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
+    static __device__ __forceinline__ void st(float* p, int64_t i, float v) { p[i] = v; }
+};
+struct BF16 {
+    typedef uint16_t T;
+    static __device__ __forceinline__ float ld(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+    static __device__ __forceinline__ void st(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+};
+struct F16 {
+    typedef uint16_t T;
+    static __device__ __forceinline__ float ld(const uint16_t* p, int64_t i) { return f16_bits_to_f32(p[i]); }
+    static __device__ __forceinline__ void st(uint16_t* p, int64_t i, float v) { p[i] = f32_to_f16_bits(v); }
+};
+
+// 8 consecutive elements widened to fp32 (16-byte or 2x16-byte aligned loads).
+__device__ __forceinline__ void load8(const uint16_t* p, float* o /*[8]*/, BF16) {
+    u32x4 u = *reinterpret_cast<const u32x4*>(p);
+    o[0] = __uint_as_float(u.x << 16); o[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    o[2] = __uint_as_float(u.y << 16); o[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    o[4] = __uint_as_float(u.z << 16); o[5] = __uint_as_float(u.z & 0xFFFF0000u);
+    o[6] = __uint_as_float(u.w << 16); o[7] = __uint_as_float(u.w & 0xFFFF0000u);
+}
+__device__ __forceinline__ void load8(const uint16_t* p, float* o, F16) {
+    u32x4 u = *reinterpret_cast<const u32x4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = f16_bits_to_f32((uint16_t)(w[i] & 0xFFFFu));
+        o[2 * i + 1] = f16_bits_to_f32((uint16_t)(w[i] >> 16));
+    }
+}
+__device__ __forceinline__ void load8(const float* p, float* o, F32) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+
+// ------------------------------------------------------------ reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+    return v;
+}
+
+// Sum over a block of NW waves through LDS; every thread gets the result.
+template <int NW>
+__device__ __forceinline__ float block_sum(float v, float* lds /*[NW]*/) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
+    __syncthreads();
+    if (lane == 0) lds[w] = v;
+    __syncthreads();
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) s += lds[i];
+    return s;
+}
+
+// Order-preserving map of a float to uint32 (larger float -> larger key);
+// NaN maps to 0 so that it never wins a maximum.
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+    if (f != f) return 0u;
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ------------------------------------------------------------ device error word
+__device__ __forceinline__ void record_error(uint32_t* err, uint32_t bit) {
+    if (err) atomicOr(err, bit);
+}

@@ -1,0 +1,110 @@
+// launch.h - host-side launchers of the gfx950 kernels (internal to libsttd).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sttd {
+
+enum WType { W_F32 = 0, W_BF16 = 1 };
+enum KVType { KV_F32 = 0, KV_F16 = 2 };
+
+// Where a row of a block call sits: position and KV slab, either per row from
+// device arrays or pos0 + row / seq0 for a prefill.
+struct RowMap {
+    const int32_t* pos;  // device [rows] or nullptr: row r at pos0 + r
+    const int32_t* seq;  // device [rows] or nullptr: seq0, or row r's own slab r when seq0 < 0
+    int pos0, seq0;
+};
+
+__device__ __forceinline__ int row_pos(const RowMap& m, int r) { return m.pos ? m.pos[r] : m.pos0 + r; }
+__device__ __forceinline__ int row_seq(const RowMap& m, int r) { return m.seq ? m.seq[r] : (m.seq0 < 0 ? r : m.seq0); }
+
+// KV slab addressing for one layer: slab s, head j, row c at
+// base + ((s * n_kv + j) * n_ctx + c) * d elements.
+struct KVLayer {
+    void* k;
+    void* v;
+    int n_seq, n_kv, n_ctx, d;
+    KVType type;
+};
+
+// ---- norms, rotary, gathers (kernels_misc.hip)
+// out[r, :] = x[r, :] / sqrt(mean(x[r]^2) + eps) * gain, rows r < R; out bf16.
+hipError_t launch_rmsnorm_rows_bf16(const float* x, int64_t ldx, const void* gain, WType gt, uint16_t* out,
+                                    int64_t ldo, int R, int H, float eps, hipStream_t s);
+// Per-head Q/K RMSNorm + NeoX RoPE (table) + K/V cache write; q written to q_out
+// as fp32 (q_f16 false) or f16 (q_f16 true) with row stride ldq.
+hipError_t launch_qk_norm_rope_kv(const float* qkv, int64_t ldqkv, int R, int n_heads, int n_kv, int d,
+                                  const void* q_gain, const void* k_gain, WType gt, float eps, const float* rope,
+                                  int max_pos, RowMap rm, KVLayer kv, void* q_out, bool q_f16, int64_t ldq,
+                                  uint32_t* err, hipStream_t s);
+hipError_t launch_embed_gather(const void* embed, WType wt, int vocab, int hidden, int B, const int32_t* ids,
+                               float* x, uint32_t* err, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+// ---- GEMV family (kernels_gemv.hip): rows <= 4 per group, fp32 activations.
+enum GemvEpi { GEMV_STORE = 0, GEMV_RESID = 1, GEMV_SWIGLU = 2 };
+struct GemvArgs {
+    const void* w[3];    // up to three weight segments stacked along the output
+    int seg_end[3];      // cumulative output-row ends of the segments
+    int N;               // output columns (SWIGLU: I, the gate rows; up row of n is n + I)
+    int K;               // reduction length
+    const float* x;      // activation rows [rows, K] (ldx)
+    int64_t ldx;
+    int rows;
+    const void* gain;    // fused RMSNorm gain over K (nullptr: no norm)
+    float eps;
+    float* y;            // output rows (ldy)
+    int64_t ldy;
+    const float* resid;  // RESID: y = resid + x W^T (may equal y)
+    int64_t ldr;
+};
+hipError_t launch_gemv(const GemvArgs& a, WType wt, GemvEpi epi, hipStream_t s);
+
+// Final RMSNorm + tied head + argmax (kernels_gemv.hip).
+struct HeadArgs {
+    const void* gain;
+    const void* embed;
+    int vocab, hidden;
+    float eps;
+    const float* x;
+    int64_t ldx;
+    int rows;
+    int32_t* ids;
+    float* logits;       // optional [rows, vocab]
+    float* next_x;       // optional [rows, hidden]
+    int32_t* pos;        // optional, += 1
+    unsigned long long* slots;  // [rows], zero between calls
+    uint32_t* counters;         // [ceil(rows / 4)], zero between calls
+    uint32_t* err;
+};
+hipError_t launch_lm_head_argmax(const HeadArgs& a, WType wt, hipStream_t s);
+
+// ---- MFMA GEMM (kernels_gemm.hip): C = A W^T, A bf16 [M, K], W bf16 [N, K].
+enum GemmEpi { GEMM_STORE = 0, GEMM_RESID = 1, GEMM_SWIGLU = 2 };
+struct GemmArgs {
+    const uint16_t* A;
+    int64_t lda;
+    int M, K;
+    const uint16_t* w[3];
+    int seg_end[3];
+    int N;               // STORE/RESID: output columns; SWIGLU: I (act columns)
+    float* C;            // STORE / RESID output (fp32, ldc)
+    int64_t ldc;
+    uint16_t* Cb;        // SWIGLU output (bf16, ldcb)
+    int64_t ldcb;
+};
+hipError_t launch_gemm(const GemmArgs& g, GemmEpi epi, hipStream_t s);
+
+// ---- attention (kernels_attn.hip)
+// Split-K GQA attention of independent rows (decode, and prefill on f32 caches):
+// row r attends slab rows [0, pos_r] of its head group; partials then combine.
+hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, RowMap rm, KVLayer kv, int n_splits,
+                            float* part, float* out_f32, uint16_t* out_bf16, int64_t ldo, uint32_t* err,
+                            hipStream_t s);
+// Causal flash attention (MFMA, f16 cache) of T rows of one slab at positions pos0..
+hipError_t launch_attn_prefill(const uint16_t* q16, int64_t ldq, int T, int pos0, int seq, int n_heads, KVLayer kv,
+                               uint16_t* out_bf16, int64_t ldo, hipStream_t s);
+
+}  // namespace sttd
