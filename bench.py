@@ -1,0 +1,499 @@
+"""Decoder throughput on one MI355X: prefill and decode tokens/s, the roofline
+fraction of the dominant kernel, and the CPU oracle timed as a baseline.
+
+Default workload (one "step" = one whole greedy job): the 28-block
+1.7B-shaped stack with random bf16 weights; a 153-row causal prefill of N(0,1)
+rows (last-block FFN on the final row only), the tied head's argmax gives the
+first token, then 255 decode steps each run the 28 blocks and the head, with
+the chosen token's embedding row fed back on the device. Decode steps replay
+one captured HIP graph; no host sync per token. Inputs are resident in HBM
+before the timed region.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--no-kernel-profile]
+
+Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
+
+KERNEL_NAMES = ["rmsnorm", "qkv_gemv", "qkv_gemm", "qk_rope_kv", "attn_rows", "attn_prefill", "o_gemv", "o_gemm",
+                "gateup_gemv", "gateup_gemm", "down_gemv", "down_gemm", "lm_head"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="qwen3_1p7b_stack28_greedy256")
+    ap.add_argument("--replicas", type=int, default=8,
+                    help="independent weight/KV replicas stacked for single-block workloads (MALL honesty)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-profile", action="store_true")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- algorithmic cost model (per launch)
+def kernel_cost(name, sh, rows, mean_keys=0.0):
+    """(bytes, flops) of one launch, algorithmic: each weight byte once, activations in/out once."""
+    wb = 2 if sh.wdtype == "bf16" else 4
+    kvb = 2 if sh.kvdtype == "f16" else 4
+    H, I, qd, kvd = sh.hidden, sh.ffn, sh.q_dim, sh.kv_dim
+    qkv = qd + 2 * kvd
+    if name in ("qkv_gemv", "qkv_gemm"):
+        return qkv * H * wb + H * wb + rows * (H * 4 + qkv * 4), 2.0 * rows * H * qkv
+    if name in ("o_gemv", "o_gemm"):
+        return H * qd * wb + rows * (qd * 4 + 2 * H * 4), 2.0 * rows * qd * H
+    if name in ("gateup_gemv", "gateup_gemm"):
+        return 2 * I * H * wb + H * wb + rows * (H * 4 + I * 4), 2.0 * rows * H * 2 * I
+    if name in ("down_gemv", "down_gemm"):
+        return H * I * wb + rows * (I * 4 + 2 * H * 4), 2.0 * rows * I * H
+    if name == "attn_rows":
+        return rows * (mean_keys * kvd * 2 * kvb + 2 * qd * 4), rows * 4.0 * qd * mean_keys
+    if name == "qk_rope_kv":
+        return rows * (qkv * 4 + qd * 4 + 2 * kvd * kvb), 0.0
+    if name == "lm_head":
+        return sh.vocab * H * wb + rows * H * 4, 2.0 * rows * sh.vocab * H
+    return 0, 0.0
+
+
+def decode_step_bytes(sh, n_layers, rows, mean_keys, with_head):
+    """Algorithmic HBM bytes of one decode step: weights once, KV rows read, x and the new KV rows."""
+    kvb = 2 if sh.kvdtype == "f16" else 4
+    wb = 2 if sh.wdtype == "bf16" else 4
+    per_block = sh.block_weight_bytes() + rows * (mean_keys * sh.kv_dim * 2 * kvb + 2 * sh.kv_dim * kvb)
+    head = (sh.vocab * sh.hidden * wb + sh.hidden * wb) if with_head else 0
+    return n_layers * per_block + head + rows * sh.hidden * 4 * 2
+
+
+# ---------------------------------------------------------------- helpers
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads") for i in threadpool_info() if i.get("internal_api") in ("openblas", "mkl")]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def profile_table(binding, sh, rows_of, keys_of, launches_ms=None):
+    """Read the per-kernel event timings; attach algorithmic bytes and rates."""
+    import ctypes
+    L = binding.lib()
+    out = {}
+    for k, name in enumerate(KERNEL_NAMES):
+        n = ctypes.c_int64()
+        ms = ctypes.c_double()
+        L.sttd_profile_read(k, ctypes.byref(n), ctypes.byref(ms))
+        if n.value == 0:
+            continue
+        avg_us = ms.value * 1e3 / n.value
+        b, f = kernel_cost(name, sh, rows_of(name), keys_of(name))
+        out[name] = {"launches": n.value, "avg_us": round(avg_us, 3), "bytes": int(b),
+                     "gbs": round(b / (avg_us * 1e-6) / 1e9, 1) if b else None,
+                     "tflops": round(f / (avg_us * 1e-6) / 1e12, 2) if f else None}
+    return out
+
+
+def roofline_entry(table, name, bound):
+    e = table.get(name)
+    if not e:
+        return None
+    if bound == "hbm":
+        return {"kernel": name, "bound": "hbm", "achieved": e["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(e["gbs"] / HBM_PEAK_GBS, 4), "traffic": None, "avg_us": e["avg_us"],
+                "bytes_per_launch": e["bytes"]}
+    return {"kernel": name, "bound": "mfma", "achieved": e["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(e["tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": None, "avg_us": e["avg_us"]}
+
+
+# ---------------------------------------------------------------- greedy stack (prefill + greedy decode)
+def bench_greedy_stack(args, wl):
+    import torch
+    from speech_text_decoder_amd import binding, synth
+    from speech_text_decoder_amd.device import DecoderSession
+
+    sh = wl.shape
+    T, n_steps = wl.prefill_rows, wl.steps
+    layers = [synth.block_weights(wl.cfg_id, l, sh) for l in range(sh.n_layers)]
+    E = synth.embedding(wl.cfg_id, sh)
+    g = synth.final_norm(wl.cfg_id, sh)
+    x_host = synth.prefill_rows(wl.cfg_id, T, sh.hidden)
+    sess = DecoderSession(sh, layers, embed=E, final_norm=g, n_ctx=wl.n_ctx, max_rows=T)
+    x0 = torch.from_numpy(x_host).cuda()
+    x = torch.empty_like(x0)
+    xs = torch.zeros(1, sh.hidden, device="cuda")
+    ids = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pos = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pos0 = torch.full((1,), T, dtype=torch.int32, device="cuda")
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            sess.step(xs, pos, pos_bound=wl.n_ctx)
+            sess.head(xs, ids, next_x=xs, pos=pos)
+    torch.cuda.synchronize()
+
+    def prefill_part(s):
+        with torch.cuda.stream(s):
+            x.copy_(x0)
+            sess.prefill(x, slice_last=True)
+            sess.head(x[T - 1:], ids, next_x=xs)
+            pos.copy_(pos0)
+
+    def job(ev=None):
+        with torch.cuda.stream(stream):
+            if ev:
+                ev[0].record(stream)
+            prefill_part(stream)
+            if ev:
+                ev[1].record(stream)
+            for _ in range(n_steps):
+                graph.replay()
+            if ev:
+                ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        job()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        job(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    job_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    assert int(pos.item()) == T + n_steps, "step loop did not advance the device position"
+    last_token = int(ids.item())
+
+    ms = float(np.median(job_ms))
+    new_tokens = n_steps + 1
+    mean_keys = T + (n_steps + 1) / 2.0
+    step_bytes = decode_step_bytes(sh, sh.n_layers, 1, mean_keys, True)
+    dec_step_ms = float(np.median(dec_ms)) / n_steps
+    res = {
+        "value": round(new_tokens / (ms * 1e-3), 2),
+        "ms_per_step": round(ms, 3),
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "prefill_ms": round(float(np.median(pre_ms)), 4),
+        "prefill_tok_s": round(T / (float(np.median(pre_ms)) * 1e-3), 1),
+        "decode_ms_per_token": round(dec_step_ms, 5),
+        "decode_tok_s": round(1e3 / dec_step_ms, 2),
+        "decode_step_bytes": int(step_bytes),
+        "decode_step_hbm_frac": round(step_bytes / (dec_step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "last_token": last_token,
+        "config": {"workload": wl.name, "layers": sh.n_layers, "hidden": sh.hidden, "heads": sh.n_heads,
+                   "kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim, "ffn": sh.ffn, "vocab": sh.vocab,
+                   "prefill_rows": T, "new_tokens": new_tokens, "batch": 1, "kv_dtype": sh.kvdtype,
+                   "n_ctx": wl.n_ctx, "parallelism": "none (1 GPU)"},
+    }
+    if not args.no_kernel_profile:
+        # per-kernel event timing on one eager job (same kernels, same shapes)
+        binding.lib().sttd_profile_enable((1 << len(KERNEL_NAMES)) - 1)
+        with torch.cuda.stream(stream):
+            prefill_part(stream)
+            for _ in range(min(n_steps, 32)):
+                sess.step(xs, pos, pos_bound=wl.n_ctx)
+                sess.head(xs, ids, next_x=xs, pos=pos)
+        torch.cuda.synchronize()
+        binding.lib().sttd_profile_enable(0)
+        rows = lambda n: T if n.endswith("gemm") or n in ("rmsnorm", "attn_prefill") else 1
+        keys = lambda n: mean_keys
+        table = profile_table(binding, sh, rows, keys)
+        res["kernels"] = table
+        res["roofline"] = roofline_entry(table, "gateup_gemv", "hbm")
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_greedy(wl, layers, E, g, x_host, new_tokens)
+    sess.close()
+    return res
+
+
+def cpu_baseline_greedy(wl, layers, E, g, x_host, new_tokens):
+    """The oracle on the host: prefill + 2 greedy steps of the same stack, extrapolated to the job."""
+    import oracle as O
+    from speech_text_decoder_amd import synth
+
+    sh = wl.shape
+    T = wl.prefill_rows
+    ol = [{k: synth.widen(v).astype(np.float64) for k, v in w.items()} for w in layers]
+    Ef = synth.widen(E).astype(np.float64)
+    gf = synth.widen(g)
+    cache = O.KVCache(sh.n_layers, 1, T + 4, sh.n_kv_heads, sh.head_dim)
+    t0 = time.perf_counter()
+    last = O.prefill_stack(x_host, ol, sh, cache, slice_last=True)
+    tok = O.greedy_token(O.final_logits(last, gf, Ef, sh.rms_eps)[0])
+    t1 = time.perf_counter()
+    n = 2
+    for k in range(n):
+        xo = O.step_stack(Ef[tok][None], [T + k], [0], ol, sh, cache)
+        tok = O.greedy_token(O.final_logits(xo, gf, Ef, sh.rms_eps)[0])
+    t2 = time.perf_counter()
+    step_s = (t2 - t1) / n
+    job_s = (t1 - t0) + (new_tokens - 1) * step_s
+    return {"value": round(new_tokens / job_s, 4), "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle: {T}-row prefill of the 28-block stack + head ({t1 - t0:.1f} s), then {n} greedy "
+                      f"steps ({step_s:.2f} s each); job time extrapolated to {new_tokens} new tokens",
+            "prefill_tok_s": round(T / (t1 - t0), 2), "decode_tok_s": round(1.0 / step_s, 4)}
+
+
+# ---------------------------------------------------------------- single-block workloads (replicated)
+def bench_block(args, wl):
+    """One 1.7B-shaped block, timed as R independent replicas (distinct weights and KV)
+    chained per step, so the weights stream from HBM rather than the 256 MB MALL; per-block
+    figures are totals / R."""
+    import torch
+    from speech_text_decoder_amd import binding, synth
+    from speech_text_decoder_amd.device import DecoderSession
+
+    sh = wl.shape
+    R = max(1, args.replicas)
+    T, n_steps = wl.prefill_rows, wl.steps
+    layers = [synth.block_weights(wl.cfg_id, r, sh) for r in range(R)]
+    x_host = synth.prefill_rows(wl.cfg_id, T, sh.hidden)
+    rows_host = np.stack([synth.step_rows(wl.cfg_id, k, 1, sh.hidden)[0] for k in range(n_steps)])
+    sess = DecoderSession(sh, layers, n_ctx=wl.n_ctx, max_rows=T)
+    x0 = torch.from_numpy(x_host).cuda()
+    x = torch.empty_like(x0)
+    r0 = torch.from_numpy(rows_host).cuda()
+    rows = torch.empty_like(r0)
+    pos_all = torch.arange(T, T + n_steps, dtype=torch.int32, device="cuda").view(n_steps, 1)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def decode_loop():
+        for k in range(n_steps):
+            sess.step(rows[k:k + 1], pos_all[k], pos_bound=T + k + 1)
+
+    with torch.cuda.stream(stream):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            decode_loop()
+    torch.cuda.synchronize()
+
+    def job(ev=None):
+        with torch.cuda.stream(stream):
+            x.copy_(x0)
+            rows.copy_(r0)
+            if ev:
+                ev[0].record(stream)
+            sess.prefill(x)
+            if ev:
+                ev[1].record(stream)
+            graph.replay()
+            if ev:
+                ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        job()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        job(evs[i])
+    torch.cuda.synchronize()
+    pre_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs])) / R
+    dec_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs])) / R / n_steps
+    mean_keys = T + (n_steps + 1) / 2.0
+    step_bytes = decode_step_bytes(sh, 1, 1, mean_keys, False)
+    H, I, qd, kvd = sh.hidden, sh.ffn, sh.q_dim, sh.kv_dim
+    gemm_flops = 2.0 * T * H * (qd + 2 * kvd + I * 2) + 2.0 * T * (qd * H + I * H)
+    attn_flops = 4.0 * sh.n_heads * sh.head_dim * T * (T + 1) / 2
+    pre_flops = gemm_flops + attn_flops
+    res = {
+        "value": round((T + n_steps) / ((pre_ms + dec_ms * n_steps) * 1e-3), 1),
+        "ms_per_step": round((pre_ms + dec_ms * n_steps) * R, 4),
+        "prefill_ms_per_block": round(pre_ms, 5),
+        "prefill_tok_s_per_block": round(T / (pre_ms * 1e-3), 1),
+        "prefill_tflops": round(pre_flops / (pre_ms * 1e-3) / 1e12, 2),
+        "prefill_mfma_frac": round(pre_flops / (pre_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "decode_us_per_block_step": round(dec_ms * 1e3, 3),
+        "decode_tok_s_per_block": round(1e3 / dec_ms, 1),
+        "decode_step_bytes": int(step_bytes),
+        "decode_hbm_frac": round(step_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "config": {"workload": wl.name, "replicas": R, "hidden": sh.hidden, "heads": sh.n_heads,
+                   "kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim, "ffn": sh.ffn, "prefill_rows": T,
+                   "decode_steps": n_steps, "batch": 1, "kv_dtype": sh.kvdtype, "wdtype": sh.wdtype,
+                   "parallelism": "none (1 GPU)"},
+    }
+    if not args.no_kernel_profile:
+        binding.lib().sttd_profile_enable((1 << len(KERNEL_NAMES)) - 1)
+        with torch.cuda.stream(stream):
+            x.copy_(x0)
+            rows.copy_(r0)
+            sess.prefill(x)
+            for k in range(min(n_steps, 16)):
+                sess.step(rows[k:k + 1], pos_all[k], pos_bound=T + k + 1)
+        torch.cuda.synchronize()
+        binding.lib().sttd_profile_enable(0)
+        rw = lambda n: T if n.endswith("gemm") or n in ("rmsnorm", "attn_prefill") else 1
+        table = profile_table(binding, sh, rw, lambda n: mean_keys)
+        res["kernels"] = table
+        if T >= 1024 and sh.wdtype == "bf16":
+            res["roofline"] = roofline_entry(table, "gateup_gemm", "mfma")
+        else:
+            res["roofline"] = roofline_entry(table, "gateup_gemv", "hbm")
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_block(wl, layers[0], x_host, rows_host)
+    sess.close()
+    return res
+
+
+def cpu_baseline_block(wl, w, x_host, rows_host):
+    import oracle as O
+    from speech_text_decoder_amd import synth
+
+    sh = wl.shape
+    T = wl.prefill_rows
+    ow = {k: synth.widen(v).astype(np.float64) for k, v in w.items()}
+    cache = O.KVCache(1, 1, T + 8, sh.n_kv_heads, sh.head_dim)
+    Ts = min(T, 512)
+    t0 = time.perf_counter()
+    O.block(x_host[:Ts], np.arange(Ts), np.zeros(Ts, int), ow, sh, cache, 0)
+    t1 = time.perf_counter()
+    n = 4
+    for k in range(n):
+        O.block(rows_host[k:k + 1], [Ts + k], [0], ow, sh, cache, 0)
+    t2 = time.perf_counter()
+    return {"value": round((Ts + n) / (t2 - t0), 3), "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle, one block: {Ts}-row prefill ({t1 - t0:.2f} s) + {n} decode steps "
+                      f"({(t2 - t1) / n:.3f} s each)",
+            "prefill_tok_s": round(Ts / (t1 - t0), 2), "decode_tok_s": round(n / (t2 - t1), 3)}
+
+
+# ---------------------------------------------------------------- batched decode
+def bench_batched(args, wl):
+    import torch
+    from speech_text_decoder_amd import binding, synth
+    from speech_text_decoder_amd.device import DecoderSession
+
+    sh = wl.shape
+    Bn, n_steps, n_ctx = wl.batch, wl.steps, wl.n_ctx
+    lens = synth.context_lengths(wl.cfg_id, Bn, *wl.ctx_len_range)
+    layers = [synth.block_weights(wl.cfg_id, l, sh) for l in range(sh.n_layers)]
+    E = synth.embedding(wl.cfg_id, sh)
+    g = synth.final_norm(wl.cfg_id, sh)
+    sess = DecoderSession(sh, layers, embed=E, final_norm=g, n_ctx=n_ctx, n_seq=Bn, max_rows=Bn)
+    for l in range(sh.n_layers):
+        for b in range(Bn):
+            k, v = synth.kv_fill(wl.cfg_id, l, b, int(lens[b]), sh, n_ctx)
+            gk, gv = sess.kv_slab(l, b)
+            gk[:, :lens[b], :] = torch.from_numpy(synth.kv_stored(k, sh.kvdtype).view(np.int16)).cuda().permute(1, 0, 2)
+            gv[:, :lens[b], :] = torch.from_numpy(synth.kv_stored(v, sh.kvdtype).view(np.int16)).cuda().permute(1, 0, 2)
+    x0 = torch.from_numpy(synth.step_rows(wl.cfg_id, 0, Bn, sh.hidden)).cuda()
+    x = torch.empty_like(x0)
+    pos0 = torch.from_numpy(lens.astype(np.int32)).cuda()
+    pos = torch.empty_like(pos0)
+    ids = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    bound = int(lens.max()) + n_steps + 1
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            sess.step(x, pos, pos_bound=bound)
+            sess.head(x, ids, next_x=x, pos=pos)
+    torch.cuda.synchronize()
+
+    def job(ev=None):
+        with torch.cuda.stream(stream):
+            x.copy_(x0)
+            pos.copy_(pos0)
+            if ev:
+                ev[0].record(stream)
+            for _ in range(n_steps):
+                graph.replay()
+            if ev:
+                ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        job()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        job(evs[i])
+    torch.cuda.synchronize()
+    ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    mean_keys = float(lens.mean()) + (n_steps + 1) / 2.0
+    step_bytes = decode_step_bytes(sh, sh.n_layers, Bn, mean_keys, True)
+    step_ms = ms / n_steps
+    res = {
+        "value": round(Bn * n_steps / (ms * 1e-3), 1),
+        "ms_per_step": round(ms, 3),
+        "decode_ms_per_step": round(step_ms, 4),
+        "decode_step_bytes": int(step_bytes),
+        "decode_step_hbm_frac": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "config": {"workload": wl.name, "layers": sh.n_layers, "batch": Bn, "steps": n_steps,
+                   "ctx_len_range": list(wl.ctx_len_range), "mean_ctx": float(lens.mean()), "n_ctx": n_ctx,
+                   "kv_dtype": sh.kvdtype, "parallelism": "none (1 GPU)"},
+    }
+    if not args.no_kernel_profile:
+        binding.lib().sttd_profile_enable((1 << len(KERNEL_NAMES)) - 1)
+        with torch.cuda.stream(stream):
+            x.copy_(x0)
+            pos.copy_(pos0)
+            for _ in range(4):
+                sess.step(x, pos, pos_bound=bound)
+                sess.head(x, ids, next_x=x, pos=pos)
+        torch.cuda.synchronize()
+        binding.lib().sttd_profile_enable(0)
+        table = profile_table(binding, sh, lambda n: Bn, lambda n: mean_keys)
+        res["kernels"] = table
+        res["roofline"] = roofline_entry(table, "gateup_gemm" if "gateup_gemm" in table else "gateup_gemv", "hbm")
+    sess.close()
+    return res
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the decoder block is not sharded; "
+                                   "run with --gpus 1", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    from speech_text_decoder_amd import binding
+    from speech_text_decoder_amd.workloads import WORKLOADS
+
+    binding.lib()  # fails loudly when the HIP library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = WORKLOADS[args.workload]
+    if wl.greedy and wl.prefill_rows > 0:
+        res = bench_greedy_stack(args, wl)
+        unit = "tokens/s"
+    elif wl.batch > 1:
+        res = bench_batched(args, wl)
+        unit = "tokens/s"
+    else:
+        res = bench_block(args, wl)
+        unit = "tokens/s"
+    out = {"metric": "decoder tokens/sec (prefill, decode) + % of MFMA/HBM roofline, 1 MI355X",
+           "value": res.pop("value"), "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if wl.shape.wdtype == "bf16" else "f32", "data": "synthetic (seeded N(0,1) rows, "
+           "N(0,0.02) weights, 1+N(0,0.02) gains)", "config": res.pop("config")}
+    out.update(res)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -174,6 +174,35 @@ sttd_status sttd_lm_head_argmax(const void *final_norm, const void *embed, sttd_
                                 float rms_eps, sttd_workspace *ws, int B, const float *x, int64_t x_row_stride,
                                 int32_t *ids, float *logits, float *next_x, int32_t *pos, void *stream);
 
+/* ---------------------------------------------------------------- per-kernel timing
+ * The per-op profiler of the MOSS-Transcribe-Diarize page (src/arch/moss/
+ * model.cpp, run() and its OpProf table: wall time per graph node), as HIP
+ * event pairs: while a kernel family's bit (1 << kind) is set in the mask,
+ * each of its launches is bracketed by two events on the launch stream.
+ * Launches on a capturing stream are not timed. sttd_profile_read
+ * synchronises on the recorded events and returns the number of timed
+ * launches and their summed milliseconds, then clears that family. The
+ * attention-rows family spans the split kernel and its combine. */
+typedef enum {
+    STTD_KERN_RMSNORM = 0,      /* RMSNorm rows to bf16 (prefill) */
+    STTD_KERN_QKV_GEMV = 1,     /* fused RMSNorm + Q|K|V projection, decode rows */
+    STTD_KERN_QKV_GEMM = 2,     /* Q|K|V projection, MFMA */
+    STTD_KERN_QK_ROPE_KV = 3,   /* per-head Q/K RMSNorm + RoPE + KV write */
+    STTD_KERN_ATTN_ROWS = 4,    /* split-K attention of independent rows + combine */
+    STTD_KERN_ATTN_PREFILL = 5, /* causal flash prefill attention, MFMA */
+    STTD_KERN_O_GEMV = 6,       /* O projection + residual, decode rows */
+    STTD_KERN_O_GEMM = 7,
+    STTD_KERN_GATEUP_GEMV = 8,  /* fused RMSNorm + gate_up + SwiGLU, decode rows */
+    STTD_KERN_GATEUP_GEMM = 9,
+    STTD_KERN_DOWN_GEMV = 10,   /* down projection + residual, decode rows */
+    STTD_KERN_DOWN_GEMM = 11,
+    STTD_KERN_LM_HEAD = 12,     /* final RMSNorm + tied head + argmax */
+    STTD_KERN_COUNT = 13
+} sttd_kernel;
+
+sttd_status sttd_profile_enable(uint32_t mask);
+sttd_status sttd_profile_read(int kernel, int64_t *launches /* host */, double *total_ms /* host */);
+
 #ifdef __cplusplus
 }
 #endif

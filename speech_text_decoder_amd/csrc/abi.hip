@@ -3,7 +3,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
+#include <utility>
 #include <vector>
 
 #include "launch.h"
@@ -26,11 +28,11 @@ struct sttd_workspace {
     void* base;
     size_t bytes;
     float* rope;        // [max_pos][d/2][2]
-    uint16_t* xn;       // [max_rows][hidden] bf16 (normed rows for the MFMA GEMMs)
+    uint16_t* xn;       // [2][max_rows][hidden] bf16: normed rows for the MFMA GEMMs, then their low parts
     float* qkv;         // [max_rows][(nq + 2 nkv) d]
     void* qbuf;         // [max_rows][nq d] fp32 (or f16)
-    float* attn_o;      // [max_rows][nq d] fp32 (or bf16)
-    float* act;         // [max_rows][ffn] fp32 (or bf16)
+    float* attn_o;      // [max_rows][nq d] fp32, or two bf16 planes (high, low)
+    float* act;         // [max_rows][ffn] fp32, or two bf16 planes (high, low)
     float* part;        // [part_cap][nq][d + 2]
     unsigned long long* slots;  // [max_rows]
     uint32_t* counters;         // [max_rows / 4 + 1]
@@ -39,7 +41,53 @@ struct sttd_workspace {
 
 namespace {
 
-constexpr int kGemvMaxRows = 4;  // rows beyond this take the MFMA GEMMs (bf16 weights)
+// ------------------------------------------------------------ per-kernel timing
+struct Profiler {
+    std::mutex mu;
+    uint32_t mask = 0;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> timed[STTD_KERN_COUNT];
+    std::vector<hipEvent_t> pool;
+
+    hipEvent_t get() {
+        if (!pool.empty()) {
+            hipEvent_t e = pool.back();
+            pool.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+};
+Profiler g_prof;
+
+// Brackets the launches of one kernel family with an event pair when timing is on.
+class ProfScope {
+  public:
+    ProfScope(int kind, hipStream_t s) : kind_(kind), s_(s) {
+        if (!(g_prof.mask & (1u << kind))) return;
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        b_ = g_prof.get();
+        e_ = g_prof.get();
+        if (b_ && e_ && hipEventRecord(b_, s) != hipSuccess) b_ = nullptr;
+    }
+    ~ProfScope() {
+        if (!b_ || !e_) return;
+        if (hipEventRecord(e_, s_) != hipSuccess) return;
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        g_prof.timed[kind_].emplace_back(b_, e_);
+    }
+
+  private:
+    int kind_;
+    hipStream_t s_;
+    hipEvent_t b_ = nullptr, e_ = nullptr;
+};
+
+constexpr int kGemvMaxRows = 4;    // rows beyond this take the MFMA GEMMs (bf16 weights)
+constexpr int kSplitMaxRows = 512; // up to here the GEMMs are HBM-bound: split activations (hi + lo)
 constexpr int kMaxSplits = 64;
 
 sttd_status from_hip(hipError_t e) {
@@ -115,15 +163,25 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
     const KVLayer kl = kv_layer(kv, layer);
     const bool mfma = wt == W_BF16 && R > kGemvMaxRows;
     const bool flash = mfma && prefill && kl.type == KV_F16;
+    const bool split = R <= kSplitMaxRows;
+    uint16_t* xn_lo = split ? ws->xn + (size_t)ws->max_rows * H : nullptr;
+    uint16_t* ao = (uint16_t*)ws->attn_o;
+    uint16_t* ao_lo = split ? ao + (size_t)ws->max_rows * qd : nullptr;
+    uint16_t* act = (uint16_t*)ws->act;
+    uint16_t* act_lo = split ? act + (size_t)ws->max_rows * I : nullptr;
 
     // --- attention half: norm + QKV projection
     if (mfma) {
-        TRY(launch_rmsnorm_rows_bf16(x, H, w->attn_norm, wt, ws->xn, H, R, H, eps, s));
+        {
+            ProfScope ps(STTD_KERN_RMSNORM, s);
+            TRY(launch_rmsnorm_rows_bf16(x, H, w->attn_norm, wt, ws->xn, xn_lo, H, R, H, eps, s));
+        }
         GemmArgs g{};
-        g.A = ws->xn; g.lda = H; g.M = R; g.K = H;
+        g.A = ws->xn; g.A_lo = xn_lo; g.lda = H; g.M = R; g.K = H;
         g.w[0] = (const uint16_t*)w->wq; g.w[1] = (const uint16_t*)w->wk; g.w[2] = (const uint16_t*)w->wv;
         g.seg_end[0] = qd; g.seg_end[1] = qd + kvd; g.seg_end[2] = qkv_cols;
         g.N = qkv_cols; g.C = ws->qkv; g.ldc = qkv_cols;
+        ProfScope ps(STTD_KERN_QKV_GEMM, s);
         TRY(launch_gemm(g, GEMM_STORE, s));
     } else {
         GemvArgs a{};
@@ -131,31 +189,39 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
         a.seg_end[0] = qd; a.seg_end[1] = qd + kvd; a.seg_end[2] = qkv_cols;
         a.N = qkv_cols; a.K = H; a.x = x; a.ldx = H; a.rows = R; a.gain = w->attn_norm; a.eps = eps;
         a.y = ws->qkv; a.ldy = qkv_cols;
+        ProfScope ps(STTD_KERN_QKV_GEMV, s);
         TRY(launch_gemv(a, wt, GEMV_STORE, s));
     }
     // --- per-head Q/K norm, RoPE, cache write
-    TRY(launch_qk_norm_rope_kv(ws->qkv, qkv_cols, R, nq, nkv, d, w->q_norm, w->k_norm, wt, eps, ws->rope,
-                               ws->max_pos, rm, kl, ws->qbuf, flash, qd, ws->err, s));
+    {
+        ProfScope ps(STTD_KERN_QK_ROPE_KV, s);
+        TRY(launch_qk_norm_rope_kv(ws->qkv, qkv_cols, R, nq, nkv, d, w->q_norm, w->k_norm, wt, eps, ws->rope,
+                                   ws->max_pos, rm, kl, ws->qbuf, flash, qd, ws->err, s));
+    }
     // --- attention
     if (flash) {
-        TRY(launch_attn_prefill((const uint16_t*)ws->qbuf, qd, R, rm.pos0, rm.seq0, nq, kl, (uint16_t*)ws->attn_o,
-                                qd, s));
+        ProfScope ps(STTD_KERN_ATTN_PREFILL, s);
+        TRY(launch_attn_prefill((const uint16_t*)ws->qbuf, qd, R, rm.pos0, rm.seq0, nq, kl, ao, ao_lo, qd, s));
     } else {
         const int splits = choose_splits(R, pos_bound, ws->part_cap);
+        ProfScope ps(STTD_KERN_ATTN_ROWS, s);
         TRY(launch_attn_rows((const float*)ws->qbuf, qd, R, nq, rm, kl, splits, ws->part,
-                             mfma ? nullptr : ws->attn_o, mfma ? (uint16_t*)ws->attn_o : nullptr, qd, ws->err, s));
+                             mfma ? nullptr : ws->attn_o, mfma ? ao : nullptr, mfma ? ao_lo : nullptr, qd, ws->err,
+                             s));
     }
     // --- O projection + residual
     if (mfma) {
         GemmArgs g{};
-        g.A = (const uint16_t*)ws->attn_o; g.lda = qd; g.M = R; g.K = qd;
+        g.A = ao; g.A_lo = ao_lo; g.lda = qd; g.M = R; g.K = qd;
         g.w[0] = (const uint16_t*)w->wo; g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = H;
         g.N = H; g.C = x; g.ldc = H;
+        ProfScope ps(STTD_KERN_O_GEMM, s);
         TRY(launch_gemm(g, GEMM_RESID, s));
     } else {
         GemvArgs a{};
         a.w[0] = w->wo; a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = H;
         a.N = H; a.K = qd; a.x = ws->attn_o; a.ldx = qd; a.rows = R; a.y = x; a.ldy = H; a.resid = x; a.ldr = H;
+        ProfScope ps(STTD_KERN_O_GEMV, s);
         TRY(launch_gemv(a, wt, GEMV_RESID, s));
     }
     // --- FFN: norm, packed gate_up + SwiGLU, down + residual
@@ -163,26 +229,37 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
     const int nr = last_row_only ? 1 : R;
     float* xf = x + (int64_t)r0 * H;
     if (mfma && nr > kGemvMaxRows) {
-        TRY(launch_rmsnorm_rows_bf16(xf, H, w->ffn_norm, wt, ws->xn, H, nr, H, eps, s));
+        {
+            ProfScope ps(STTD_KERN_RMSNORM, s);
+            TRY(launch_rmsnorm_rows_bf16(xf, H, w->ffn_norm, wt, ws->xn, xn_lo, H, nr, H, eps, s));
+        }
         GemmArgs g{};
-        g.A = ws->xn; g.lda = H; g.M = nr; g.K = H;
+        g.A = ws->xn; g.A_lo = xn_lo; g.lda = H; g.M = nr; g.K = H;
         g.w[0] = (const uint16_t*)w->w_gate_up; g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = 2 * I;
-        g.N = I; g.Cb = (uint16_t*)ws->act; g.ldcb = I;
-        TRY(launch_gemm(g, GEMM_SWIGLU, s));
+        g.N = I; g.Cb = act; g.Cb_lo = act_lo; g.ldcb = I;
+        {
+            ProfScope ps(STTD_KERN_GATEUP_GEMM, s);
+            TRY(launch_gemm(g, GEMM_SWIGLU, s));
+        }
         GemmArgs g2{};
-        g2.A = (const uint16_t*)ws->act; g2.lda = I; g2.M = nr; g2.K = I;
+        g2.A = act; g2.A_lo = act_lo; g2.lda = I; g2.M = nr; g2.K = I;
         g2.w[0] = (const uint16_t*)w->w_down; g2.seg_end[0] = g2.seg_end[1] = g2.seg_end[2] = H;
         g2.N = H; g2.C = xf; g2.ldc = H;
+        ProfScope ps(STTD_KERN_DOWN_GEMM, s);
         TRY(launch_gemm(g2, GEMM_RESID, s));
     } else {
         GemvArgs a{};
         a.w[0] = w->w_gate_up; a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = I;
         a.N = I; a.K = H; a.x = xf; a.ldx = H; a.rows = nr; a.gain = w->ffn_norm; a.eps = eps;
         a.y = ws->act; a.ldy = I;
-        TRY(launch_gemv(a, wt, GEMV_SWIGLU, s));
+        {
+            ProfScope ps(STTD_KERN_GATEUP_GEMV, s);
+            TRY(launch_gemv(a, wt, GEMV_SWIGLU, s));
+        }
         GemvArgs b{};
         b.w[0] = w->w_down; b.seg_end[0] = b.seg_end[1] = b.seg_end[2] = H;
         b.N = H; b.K = I; b.x = ws->act; b.ldx = I; b.rows = nr; b.y = xf; b.ldy = H; b.resid = xf; b.ldr = H;
+        ProfScope ps(STTD_KERN_DOWN_GEMV, s);
         TRY(launch_gemv(b, wt, GEMV_RESID, s));
     }
     return STTD_OK;
@@ -285,7 +362,7 @@ sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int m
         return o;
     };
     const size_t o_rope = take((size_t)max_pos * d * sizeof(float));
-    const size_t o_xn = take(R * H * 2);
+    const size_t o_xn = take(R * H * 2 * 2);
     const size_t o_qkv = take(R * (nq + 2 * nkv) * d * sizeof(float));
     const size_t o_q = take(R * nq * d * sizeof(float));
     const size_t o_ao = take(R * nq * d * sizeof(float));
@@ -411,8 +488,42 @@ sttd_status sttd_lm_head_argmax(const void* final_norm, const void* embed, sttd_
     a.gain = final_norm; a.embed = embed; a.vocab = vocab; a.hidden = hidden; a.eps = rms_eps;
     a.x = x; a.ldx = x_row_stride; a.rows = B; a.ids = ids; a.logits = logits; a.next_x = next_x; a.pos = pos;
     a.slots = ws->slots; a.counters = ws->counters; a.err = ws->err;
+    ProfScope ps(STTD_KERN_LM_HEAD, (hipStream_t)stream);
     TRY(launch_lm_head_argmax(a, wtype == STTD_BF16 ? W_BF16 : W_F32, (hipStream_t)stream));
     return STTD_OK;
+}
+
+sttd_status sttd_profile_enable(uint32_t mask) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    g_prof.mask = mask & ((1u << STTD_KERN_COUNT) - 1);
+    return STTD_OK;
+}
+
+sttd_status sttd_profile_read(int kernel, int64_t* launches, double* total_ms) {
+    if (kernel < 0 || kernel >= STTD_KERN_COUNT || !launches || !total_ms) return STTD_ERR_INVALID_ARG;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> pairs;
+    {
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        pairs.swap(g_prof.timed[kernel]);
+    }
+    double sum = 0.0;
+    sttd_status st = STTD_OK;
+    for (auto& pr : pairs) {
+        float ms = 0.f;
+        if (hipEventSynchronize(pr.second) != hipSuccess || hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess)
+            st = STTD_ERR_BACKEND;
+        sum += ms;
+    }
+    {
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        for (auto& pr : pairs) {
+            g_prof.pool.push_back(pr.first);
+            g_prof.pool.push_back(pr.second);
+        }
+    }
+    *launches = (int64_t)pairs.size();
+    *total_ms = sum;
+    return st;
 }
 
 }  // extern "C"

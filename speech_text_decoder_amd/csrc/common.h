@@ -21,6 +21,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// v = hi + lo to about 16 significant bits: hi = bf16(v), lo = bf16(v - hi).
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+    hi = f32_to_bf16_bits(v);
+    lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const float* __restrict_
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict__ part, int n_heads, int n_splits,
                                                          float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16,
-                                                         int64_t ldo) {
+                                                         uint16_t* __restrict__ out_lo, int64_t ldo) {
     const int r = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
     const float* pp = part + ((int64_t)r * n_heads + h) * n_splits * (D + 2);
     float M = -INFINITY;
@@ -134,8 +134,14 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
     }
     const float v = L > 0.f ? O / L : 0.f;
     const int64_t idx = (int64_t)r * ldo + h * D + e;
-    if (out_f32) out_f32[idx] = v;
-    else out_bf16[idx] = f32_to_bf16_bits(v);
+    if (out_f32) {
+        out_f32[idx] = v;
+    } else {
+        uint16_t hi, lo;
+        split_bf16(v, hi, lo);
+        out_bf16[idx] = hi;
+        if (out_lo) out_lo[idx] = lo;
+    }
 }
 
 template <class KT, int D>
@@ -153,19 +159,19 @@ static void rows_dispatch_g(const float* q, int64_t ldq, int R, int n_heads, Row
 }
 
 hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, RowMap rm, KVLayer kv, int n_splits,
-                            float* part, float* out_f32, uint16_t* out_bf16, int64_t ldo, uint32_t* err,
-                            hipStream_t s) {
+                            float* part, float* out_f32, uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo,
+                            uint32_t* err, hipStream_t s) {
     if (R <= 0) return hipSuccess;
     const int G = n_heads / kv.n_kv;
     if (G != 1 && G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
     if (kv.d == 128) {
         if (kv.type == KV_F16) rows_dispatch_g<F16, 128>(q, ldq, R, n_heads, rm, kv, n_splits, part, err, s);
         else rows_dispatch_g<F32, 128>(q, ldq, R, n_heads, rm, kv, n_splits, part, err, s);
-        attn_combine_kernel<128><<<dim3(R, n_heads), 128, 0, s>>>(part, n_heads, n_splits, out_f32, out_bf16, ldo);
+        attn_combine_kernel<128><<<dim3(R, n_heads), 128, 0, s>>>(part, n_heads, n_splits, out_f32, out_bf16, out_bf16_lo, ldo);
     } else if (kv.d == 64) {
         if (kv.type == KV_F16) rows_dispatch_g<F16, 64>(q, ldq, R, n_heads, rm, kv, n_splits, part, err, s);
         else rows_dispatch_g<F32, 64>(q, ldq, R, n_heads, rm, kv, n_splits, part, err, s);
-        attn_combine_kernel<64><<<dim3(R, n_heads), 64, 0, s>>>(part, n_heads, n_splits, out_f32, out_bf16, ldo);
+        attn_combine_kernel<64><<<dim3(R, n_heads), 64, 0, s>>>(part, n_heads, n_splits, out_f32, out_bf16, out_bf16_lo, ldo);
     } else {
         return hipErrorInvalidValue;
     }
@@ -184,7 +190,8 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
 template <int D>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __restrict__ q16, int64_t ldq, int T,
                                                            int pos0, int seq, int n_heads, KVLayer kv,
-                                                           uint16_t* __restrict__ out, int64_t ldo) {
+                                                           uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo,
+                                                           int64_t ldo) {
     constexpr int KB = 64;                 // keys per block
     constexpr int KS = D + 8;              // K row stride in LDS (f16)
     constexpr int VS = KB + 8;             // V^T row stride in LDS
@@ -317,19 +324,24 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
         if (t >= T) continue;
         const float inv = 1.0f / lsum;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
-            out[(int64_t)t * ldo + h * D + dt * 16 + lane % 16] = f32_to_bf16_bits(o[dt][rr] * inv);
+        for (int dt = 0; dt < D / 16; ++dt) {
+            uint16_t hi, lo;
+            split_bf16(o[dt][rr] * inv, hi, lo);
+            const int64_t idx = (int64_t)t * ldo + h * D + dt * 16 + lane % 16;
+            out[idx] = hi;
+            if (out_lo) out_lo[idx] = lo;
+        }
     }
 }
 
 hipError_t launch_attn_prefill(const uint16_t* q16, int64_t ldq, int T, int pos0, int seq, int n_heads, KVLayer kv,
-                               uint16_t* out_bf16, int64_t ldo, hipStream_t s) {
+                               uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     dim3 grid((T + 63) / 64, n_heads);
     if (kv.d == 128)
-        attn_prefill_kernel<128><<<grid, 256, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, ldo);
+        attn_prefill_kernel<128><<<grid, 256, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo);
     else if (kv.d == 64)
-        attn_prefill_kernel<64><<<grid, 256, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, ldo);
+        attn_prefill_kernel<64><<<grid, 256, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -12,7 +12,8 @@ namespace sttd {
 template <class GT>
 __global__ __launch_bounds__(256) void rmsnorm_rows_bf16_kernel(const float* __restrict__ x, int64_t ldx,
                                                                 const typename GT::T* __restrict__ g,
-                                                                uint16_t* __restrict__ out, int64_t ldo, int H,
+                                                                uint16_t* __restrict__ out,
+                                                                uint16_t* __restrict__ out_lo, int64_t ldo, int H,
                                                                 float eps) {
     __shared__ float red[4];
     const float* xr = x + (int64_t)blockIdx.x * ldx;
@@ -28,20 +29,30 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_bf16_kernel(const float* __r
         float4 v = *reinterpret_cast<const float4*>(xr + i);
         const float a0 = v.x * rs * GT::ld(g, i), a1 = v.y * rs * GT::ld(g, i + 1);
         const float a2 = v.z * rs * GT::ld(g, i + 2), a3 = v.w * rs * GT::ld(g, i + 3);
+        uint16_t h0, h1, h2, h3, l0, l1, l2, l3;
+        split_bf16(a0, h0, l0);
+        split_bf16(a1, h1, l1);
+        split_bf16(a2, h2, l2);
+        split_bf16(a3, h3, l3);
         uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16_bits(a0) | ((uint32_t)f32_to_bf16_bits(a1) << 16);
-        pk.y = (uint32_t)f32_to_bf16_bits(a2) | ((uint32_t)f32_to_bf16_bits(a3) << 16);
+        pk.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        pk.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
         *reinterpret_cast<uint2*>(o + i) = pk;
+        if (out_lo) {
+            pk.x = (uint32_t)l0 | ((uint32_t)l1 << 16);
+            pk.y = (uint32_t)l2 | ((uint32_t)l3 << 16);
+            *reinterpret_cast<uint2*>(out_lo + (int64_t)blockIdx.x * ldo + i) = pk;
+        }
     }
 }
 
 hipError_t launch_rmsnorm_rows_bf16(const float* x, int64_t ldx, const void* gain, WType gt, uint16_t* out,
-                                    int64_t ldo, int R, int H, float eps, hipStream_t s) {
+                                    uint16_t* out_lo, int64_t ldo, int R, int H, float eps, hipStream_t s) {
     if (R <= 0) return hipSuccess;
     if (gt == W_BF16)
-        rmsnorm_rows_bf16_kernel<BF16><<<R, 256, 0, s>>>(x, ldx, (const uint16_t*)gain, out, ldo, H, eps);
+        rmsnorm_rows_bf16_kernel<BF16><<<R, 256, 0, s>>>(x, ldx, (const uint16_t*)gain, out, out_lo, ldo, H, eps);
     else
-        rmsnorm_rows_bf16_kernel<F32><<<R, 256, 0, s>>>(x, ldx, (const float*)gain, out, ldo, H, eps);
+        rmsnorm_rows_bf16_kernel<F32><<<R, 256, 0, s>>>(x, ldx, (const float*)gain, out, out_lo, ldo, H, eps);
     return hipGetLastError();
 }
 

@@ -31,8 +31,9 @@ struct KVLayer {
 
 // ---- norms, rotary, gathers (kernels_misc.hip)
 // out[r, :] = x[r, :] / sqrt(mean(x[r]^2) + eps) * gain, rows r < R; out bf16.
+// With out_lo, the value is also split: out = bf16(v), out_lo = bf16(v - out).
 hipError_t launch_rmsnorm_rows_bf16(const float* x, int64_t ldx, const void* gain, WType gt, uint16_t* out,
-                                    int64_t ldo, int R, int H, float eps, hipStream_t s);
+                                    uint16_t* out_lo, int64_t ldo, int R, int H, float eps, hipStream_t s);
 // Per-head Q/K RMSNorm + NeoX RoPE (table) + K/V cache write; q written to q_out
 // as fp32 (q_f16 false) or f16 (q_f16 true) with row stride ldq.
 hipError_t launch_qk_norm_rope_kv(const float* qkv, int64_t ldqkv, int R, int n_heads, int n_kv, int d,
@@ -83,8 +84,13 @@ hipError_t launch_lm_head_argmax(const HeadArgs& a, WType wt, hipStream_t s);
 
 // ---- MFMA GEMM (kernels_gemm.hip): C = A W^T, A bf16 [M, K], W bf16 [N, K].
 enum GemmEpi { GEMM_STORE = 0, GEMM_RESID = 1, GEMM_SWIGLU = 2 };
+// A_lo (optional) holds bf16(a - bf16(a)) of every A element with the same
+// stride: the product then takes A + A_lo, an activation operand with about
+// 16 significant bits, at twice the MFMA work (used where HBM bounds the GEMM).
+// SWIGLU with Cb_lo writes the act output split the same way.
 struct GemmArgs {
     const uint16_t* A;
+    const uint16_t* A_lo;
     int64_t lda;
     int M, K;
     const uint16_t* w[3];
@@ -93,6 +99,7 @@ struct GemmArgs {
     float* C;            // STORE / RESID output (fp32, ldc)
     int64_t ldc;
     uint16_t* Cb;        // SWIGLU output (bf16, ldcb)
+    uint16_t* Cb_lo;     // optional low half of the SWIGLU output
     int64_t ldcb;
 };
 hipError_t launch_gemm(const GemmArgs& g, GemmEpi epi, hipStream_t s);
@@ -101,10 +108,10 @@ hipError_t launch_gemm(const GemmArgs& g, GemmEpi epi, hipStream_t s);
 // Split-K GQA attention of independent rows (decode, and prefill on f32 caches):
 // row r attends slab rows [0, pos_r] of its head group; partials then combine.
 hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, RowMap rm, KVLayer kv, int n_splits,
-                            float* part, float* out_f32, uint16_t* out_bf16, int64_t ldo, uint32_t* err,
-                            hipStream_t s);
+                            float* part, float* out_f32, uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo,
+                            uint32_t* err, hipStream_t s);
 // Causal flash attention (MFMA, f16 cache) of T rows of one slab at positions pos0..
 hipError_t launch_attn_prefill(const uint16_t* q16, int64_t ldq, int T, int pos0, int seq, int n_heads, KVLayer kv,
-                               uint16_t* out_bf16, int64_t ldo, hipStream_t s);
+                               uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo, hipStream_t s);
 
 }  // namespace sttd
