@@ -33,10 +33,9 @@ struct sttd_workspace {
     void* qbuf;         // [max_rows][nq d] fp32 (or f16)
     float* attn_o;      // [max_rows][nq d] fp32, or two bf16 planes (high, low)
     float* act;         // [max_rows][ffn] fp32, or two bf16 planes (high, low)
-    float* part;        // [part_cap][nq][d + 2]
-    unsigned long long* slots;  // [max_rows]
-    uint32_t* counters;         // [max_rows / 4 + 1]
-    uint32_t* err;              // [1]
+    float* part;        // [part_cap][nq][d + 4] attention split partials
+    unsigned long long* partials;  // [max_rows][kHeadPartials] head argmax partials
+    uint32_t* err;                 // [1]
 };
 
 namespace {
@@ -89,6 +88,7 @@ class ProfScope {
 constexpr int kGemvMaxRows = 4;    // rows beyond this take the MFMA GEMMs (bf16 weights)
 constexpr int kSplitMaxRows = 512; // up to here the GEMMs are HBM-bound: split activations (hi + lo)
 constexpr int kMaxSplits = 64;
+constexpr int kHeadPartials = 1024;  // workgroups of the persistent head GEMV
 
 sttd_status from_hip(hipError_t e) {
     if (e == hipSuccess) return STTD_OK;
@@ -144,8 +144,11 @@ KVLayer kv_layer(const sttd_kv_cache* kv, int layer) {
     return l;
 }
 
+// Splits of the rows-attention grid: about 256 cache rows per split at the
+// host bound (16-wave workgroups read them two rows per 16-lane group per
+// step), one split (no merge kernel) up to 256 positions.
 int choose_splits(int rows, int pos_bound, int part_cap) {
-    int s = (pos_bound + 63) / 64;
+    int s = (pos_bound + 255) / 256;
     if (s > kMaxSplits) s = kMaxSplits;
     if (s > part_cap / rows) s = part_cap / rows;
     return s < 1 ? 1 : s;
@@ -171,6 +174,10 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
     uint16_t* act_lo = split ? act + (size_t)ws->max_rows * I : nullptr;
 
     // --- attention half: norm + QKV projection
+    QkRope qr{};
+    qr.q_gain = w->q_norm; qr.k_gain = w->k_norm; qr.eps = eps; qr.rope = ws->rope; qr.max_pos = ws->max_pos;
+    qr.rm = rm; qr.kv = kl; qr.q_out = ws->qbuf; qr.q_f16 = flash; qr.ldq = qd; qr.err = ws->err;
+    qr.n_heads = nq; qr.n_kv = nkv; qr.d = d;
     if (mfma) {
         {
             ProfScope ps(STTD_KERN_RMSNORM, s);
@@ -192,22 +199,25 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
         ProfScope ps(STTD_KERN_QKV_GEMV, s);
         TRY(launch_gemv(a, wt, GEMV_STORE, s));
     }
-    // --- per-head Q/K norm, RoPE, cache write
-    {
+    // --- per-head Q/K norm + RoPE + cache write, then attention. Prefill rows of
+    // one sequence need every key written first (separate kernel); decode rows
+    // (one per slab) do it inside the attention kernel.
+    if (prefill) {
         ProfScope ps(STTD_KERN_QK_ROPE_KV, s);
-        TRY(launch_qk_norm_rope_kv(ws->qkv, qkv_cols, R, nq, nkv, d, w->q_norm, w->k_norm, wt, eps, ws->rope,
-                                   ws->max_pos, rm, kl, ws->qbuf, flash, qd, ws->err, s));
+        TRY(launch_qk_norm_rope_kv(ws->qkv, qkv_cols, R, wt, qr, s));
     }
-    // --- attention
+    int splits = 1;
     if (flash) {
         ProfScope ps(STTD_KERN_ATTN_PREFILL, s);
         TRY(launch_attn_prefill((const uint16_t*)ws->qbuf, qd, R, rm.pos0, rm.seq0, nq, kl, ao, ao_lo, qd, s));
     } else {
-        const int splits = choose_splits(R, pos_bound, ws->part_cap);
+        splits = choose_splits(R, pos_bound, ws->part_cap);
+        // GEMV path: a split result stays as partials and the O projection merges them on load
+        const bool defer = !mfma && splits > 1;
         ProfScope ps(STTD_KERN_ATTN_ROWS, s);
-        TRY(launch_attn_rows((const float*)ws->qbuf, qd, R, nq, rm, kl, splits, ws->part,
-                             mfma ? nullptr : ws->attn_o, mfma ? ao : nullptr, mfma ? ao_lo : nullptr, qd, ws->err,
-                             s));
+        TRY(launch_attn_rows(prefill ? (const float*)ws->qbuf : ws->qkv, prefill ? qd : qkv_cols, R, nq, rm, kl,
+                             splits, ws->part, mfma || defer ? nullptr : ws->attn_o, mfma ? ao : nullptr,
+                             mfma ? ao_lo : nullptr, qd, ws->err, prefill ? nullptr : &qr, wt, s));
     }
     // --- O projection + residual
     if (mfma) {
@@ -221,6 +231,9 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
         GemvArgs a{};
         a.w[0] = w->wo; a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = H;
         a.N = H; a.K = qd; a.x = ws->attn_o; a.ldx = qd; a.rows = R; a.y = x; a.ldy = H; a.resid = x; a.ldr = H;
+        if (splits > 1) {
+            a.xpart = ws->part; a.n_splits = splits; a.head_dim = d;
+        }
         ProfScope ps(STTD_KERN_O_GEMV, s);
         TRY(launch_gemv(a, wt, GEMV_RESID, s));
     }
@@ -367,9 +380,8 @@ sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int m
     const size_t o_q = take(R * nq * d * sizeof(float));
     const size_t o_ao = take(R * nq * d * sizeof(float));
     const size_t o_act = take(R * I * sizeof(float));
-    const size_t o_part = take((size_t)part_cap * nq * (d + 2) * sizeof(float));
-    const size_t o_slots = take(R * sizeof(unsigned long long));
-    const size_t o_cnt = take((R / 4 + 1) * sizeof(uint32_t));
+    const size_t o_part = take((size_t)part_cap * nq * (d + 4) * sizeof(float));
+    const size_t o_partials = take(R * kHeadPartials * sizeof(unsigned long long));
     const size_t o_err = take(sizeof(uint32_t));
     sttd_workspace* ws = new (std::nothrow) sttd_workspace();
     if (!ws) return STTD_ERR_OOM;
@@ -392,8 +404,7 @@ sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int m
     ws->attn_o = (float*)(b + o_ao);
     ws->act = (float*)(b + o_act);
     ws->part = (float*)(b + o_part);
-    ws->slots = (unsigned long long*)(b + o_slots);
-    ws->counters = (uint32_t*)(b + o_cnt);
+    ws->partials = (unsigned long long*)(b + o_partials);
     ws->err = (uint32_t*)(b + o_err);
     // RoPE table in fp64 on the host: pair i of position pos turns by pos * theta^(-2i/d)
     std::vector<float> table((size_t)max_pos * d);
@@ -487,7 +498,7 @@ sttd_status sttd_lm_head_argmax(const void* final_norm, const void* embed, sttd_
     HeadArgs a{};
     a.gain = final_norm; a.embed = embed; a.vocab = vocab; a.hidden = hidden; a.eps = rms_eps;
     a.x = x; a.ldx = x_row_stride; a.rows = B; a.ids = ids; a.logits = logits; a.next_x = next_x; a.pos = pos;
-    a.slots = ws->slots; a.counters = ws->counters; a.err = ws->err;
+    a.partials = ws->partials; a.max_partials = kHeadPartials; a.err = ws->err;
     ProfScope ps(STTD_KERN_LM_HEAD, (hipStream_t)stream);
     TRY(launch_lm_head_argmax(a, wtype == STTD_BF16 ? W_BF16 : W_F32, (hipStream_t)stream));
     return STTD_OK;

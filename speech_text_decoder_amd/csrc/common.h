@@ -72,9 +72,45 @@ __device__ __forceinline__ void load8(const float* p, float* o, F32) {
 }
 
 // ------------------------------------------------------------ reductions
+// Cross-lane moves stay in the VALU (no LDS round trip). Inside a 16-lane row,
+// DPP: row_mirror pairs lane i with 15 - i, row_half_mirror i with 7 - i
+// (within 8), quad_perm [2,3,0,1] i with i ^ 2 and [1,0,3,2] i with i ^ 1; each
+// is a perfect matching that flips lane bit 3, 2, 1 and 0 respectively (the
+// mirrors also flip the lower bits). Between rows, v_permlane16_swap and
+// v_permlane32_swap (gfx950): with both operands the same register, result
+// [0] holds the value of lane (l & ~16) (resp. ~32) and [1] that of lane
+// (l | 16) (resp. | 32) - checked on the device.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __builtin_amdgcn_update_dpp(0.f, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_ROW_MIRROR = 0x140, DPP_ROW_HALF_MIRROR = 0x141, DPP_XOR2 = 0x4E, DPP_XOR1 = 0xB1;
+
+__device__ __forceinline__ float xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// Sum over the 8 (resp. 16) lanes of an aligned group; every lane gets it.
+__device__ __forceinline__ float row8_sum(float v) {
+    v += dpp_move<DPP_ROW_HALF_MIRROR>(v);
+    v += dpp_move<DPP_XOR2>(v);
+    v += dpp_move<DPP_XOR1>(v);
+    return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_move<DPP_ROW_MIRROR>(v);
+    return row8_sum(v);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    v = row16_sum(v);
+    v += xor16(v);
+    v += xor32(v);
     return v;
 }
 __device__ __forceinline__ float wave_max(float v) {

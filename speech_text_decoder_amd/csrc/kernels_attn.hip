@@ -11,44 +11,208 @@
 
 namespace sttd {
 
-// ------------------------------------------------------------------ split-K rows
-// Grid (row, kv head, split). The split's share of cache rows [0, p] is
-// ceil((p + 1) / n_splits) rows, so the work follows the actual position even
-// though the grid is sized from a host bound. Within a workgroup, groups of
-// LPK = d/8 lanes read one cache row (16 bytes per lane for f16, coalesced)
-// and keep a running (max, sum, output) per query head of the group; the
-// groups then merge through LDS and the workgroup writes one partial
-// (m, l, o[d]) per query head. attn_combine merges the splits.
-template <class KT, int D, int G>
-__global__ __launch_bounds__(256) void attn_rows_kernel(const float* __restrict__ q, int64_t ldq, int n_heads,
-                                                        RowMap rm, KVLayer kv, int n_splits, float* __restrict__ part,
-                                                        uint32_t* err) {
-    typedef typename KT::T T;
-    constexpr int LPK = D / 8;            // lanes per cache row
-    constexpr int GROUPS = 256 / LPK;     // cache rows in flight per step
-    __shared__ float m_lds[GROUPS][G], l_lds[GROUPS][G];
-    __shared__ float o_lds[GROUPS][G][D + 1];
+// ------------------------------------------------------------------ rows attention (decode)
+// Grid (row, kv head, split), NW waves per workgroup. The split's share of
+// cache rows [0, p] is ceil((p + 1) / n_splits) rows, so the work follows the
+// actual position although the grid is sized from a host bound.
+//
+// FUSE (decode rows, one row per slab): the workgroup starts from the raw
+// Q|K|V projection of its row: waves RMSNorm + rotate the G query heads of
+// the group into LDS, and the workgroup whose split holds position p also
+// norms + rotates the new key, writes key and value to cache row p and keeps
+// them in LDS, so no other kernel or workgroup is waited on. Without FUSE the
+// query rows come normed and rotated and the cache already holds every key
+// (prefill rows on an f32 cache).
+//
+// Groups of LPK = d/8 lanes read one cache row (16 bytes per lane for f16,
+// coalesced), two rows per step, and keep a running (max, sum, output) per
+// query head; groups merge by shuffles inside a wave and through LDS across
+// waves. One split: the workgroup writes o = O / L. Several: it writes the
+// partial (M, L, O); attn_combine merges the splits into o, or, when no
+// output is given, the consumer (the O-projection GEMV) merges them as it
+// loads its activations.
+struct RowsArgs {
+    const float* q;      // FUSE: raw projection rows [R][(nq + 2 nkv) d]; else q rows [R][nq d]
+    int64_t ldq;
+    int n_heads;
+    RowMap rm;
+    KVLayer kv;
+    int n_splits;
+    float* part;
+    float* out_f32;
+    uint16_t* out_bf16;
+    uint16_t* out_lo;
+    int64_t ldo;
+    uint32_t* err;
+    const void* q_gain;  // FUSE only
+    const void* k_gain;
+    float eps;
+    const float* rope;
+    int max_pos;
+};
 
-    const int r = blockIdx.x, j = blockIdx.y, split = blockIdx.z;
-    const int tid = threadIdx.x;
-    const int grp = tid / LPK, sub = tid % LPK;
-    const int pos = row_pos(rm, r);
-    const int seq = row_seq(rm, r);
-    const bool ok = pos >= 0 && pos < kv.n_ctx && seq >= 0 && seq < kv.n_seq;
-    if (!ok && tid == 0 && split == 0 && j == 0) record_error(err, pos < 0 || pos >= kv.n_ctx ? 1u : 2u);
-    const int n_keys = ok ? pos + 1 : 0;
-    const int chunk = (n_keys + n_splits - 1) / n_splits;
-    const int c0 = split * chunk;
-    const int c1 = min(c0 + chunk, n_keys);
+// One head vector of D values: RMSNorm with `gain`, NeoX rotation at `pos`,
+// times `scale`, into dst (LDS); one wave. Lane i < D/2 owns the pair (i, i + D/2).
+template <class GT, int D>
+__device__ __forceinline__ void norm_rope_head(const float* __restrict__ src, const typename GT::T* gain, float eps,
+                                               const float* __restrict__ rope, int pos, float scale, float* dst) {
+    constexpr int HALF = D / 2;
+    const int lane = threadIdx.x % WAVE;
+    const bool act = lane < HALF;
+    const float u0 = act ? src[lane] : 0.f, u1 = act ? src[lane + HALF] : 0.f;
+    const float rs = 1.0f / sqrtf(wave_sum(u0 * u0 + u1 * u1) / (float)D + eps);
+    if (act) {
+        const float a = u0 * rs * GT::ld(gain, lane), b = u1 * rs * GT::ld(gain, lane + HALF);
+        const float2 cs = reinterpret_cast<const float2*>(rope)[(int64_t)pos * HALF + lane];
+        dst[lane] = (a * cs.x - b * cs.y) * scale;
+        dst[lane + HALF] = (a * cs.y + b * cs.x) * scale;
+    }
+}
 
-    const float scale = 1.4426950408889634f / sqrtf((float)D);
-    float qv[G][8];
+// Fold another (m, l, o) running state into this one (base-2 exponents).
+template <int G>
+__device__ __forceinline__ void merge_state(float (&m)[G], float (&l)[G], float (&o)[G][8], const float (&m2)[G],
+                                            const float (&l2)[G], const float (&o2)[G][8]) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        const float* qh = q + (int64_t)r * ldq + (j * G + g) * D + sub * 8;
+        const float M = fmaxf(m[g], m2[g]);
+        const float a = M == -INFINITY ? 0.f : exp2f(m[g] - M);
+        const float b = M == -INFINITY ? 0.f : exp2f(m2[g] - M);
+        l[g] = l[g] * a + l2[g] * b;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) qv[g][i] = qh[i] * scale;
+        for (int i = 0; i < 8; ++i) o[g][i] = o[g][i] * a + o2[g][i] * b;
+        m[g] = M;
     }
+}
+
+template <int G>
+__device__ __forceinline__ void step_state(float (&m)[G], float (&l)[G], float (&o)[G][8], const float (&s)[G],
+                                           const float (&vr)[8]) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float mn = fmaxf(m[g], s[g]);
+        const float alpha = exp2f(m[g] - mn);
+        const float p = exp2f(s[g] - mn);
+        l[g] = l[g] * alpha + p;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[g][i] = fmaf(o[g][i], alpha, p * vr[i]);
+        m[g] = mn;
+    }
+}
+
+// Sum over the LPK lanes that share one cache row.
+template <int LPK>
+__device__ __forceinline__ float group_sum(float v) {
+    return LPK == 16 ? row16_sum(v) : row8_sum(v);
+}
+
+template <class KT, class GT, int D, int G, int NW, bool FUSE>
+__global__ __launch_bounds__(NW * 64) void attn_rows_kernel(RowsArgs a) {
+    typedef typename KT::T T;
+    constexpr int LPK = D / 8;                 // lanes per cache row
+    constexpr int GPW = WAVE / LPK;            // groups per wave
+    constexpr int NG = NW * GPW;               // groups per workgroup
+    constexpr int HALF = D / 2;
+    constexpr int SLOTS = NW * (16 / LPK);     // states per workgroup after the in-wave merge
+    static_assert(LPK == 8 || LPK == 16, "head_dim 64 or 128");
+    __shared__ float q_lds[G][D];
+    __shared__ float kn_lds[D], vn_lds[D];
+    __shared__ float wm_lds[SLOTS][G], wl_lds[SLOTS][G];
+    __shared__ float wo_lds[SLOTS][G][D];
+
+    const int r = blockIdx.x, j = blockIdx.y, split = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
+    const int grp = tid / LPK, sub = tid % LPK;
+    const float scale = 1.4426950408889634f / sqrtf((float)D);
+
+    // 1. loads that do not depend on the position: this wave's head items of the
+    //    raw projection (items: G query heads, then the key, then the value;
+    //    wave w takes items w and w + NW)
+    constexpr int IPW = (G + 2 + NW - 1) / NW;  // items per wave
+    float u0[IPW], u1[IPW], g0[IPW], g1[IPW];
+#pragma unroll
+    for (int k = 0; k < IPW; ++k) {
+        const int it = wave + k * NW;
+        u0[k] = u1[k] = 0.f;
+        g0[k] = g1[k] = 1.f;
+        if (FUSE && it < G + 2 && lane < HALF) {
+            const float* src = a.q + (int64_t)r * a.ldq;
+            const int col = it < G ? (j * G + it) * D : (it == G ? (a.n_heads + j) * D
+                                                                : (a.n_heads + a.kv.n_kv + j) * D);
+            u0[k] = src[col + lane];
+            u1[k] = src[col + lane + HALF];
+            if (it <= G) {
+                const typename GT::T* gain = (const typename GT::T*)(it < G ? a.q_gain : a.k_gain);
+                g0[k] = GT::ld(gain, lane);
+                g1[k] = GT::ld(gain, lane + HALF);
+            }
+        }
+    }
+    // 2. the row's position and slab, then the first two cache rows of each group
+    const int pos = row_pos(a.rm, r);
+    const int seq = row_seq(a.rm, r);
+    const bool ok = pos >= 0 && pos < a.kv.n_ctx && pos < (FUSE ? a.max_pos : a.kv.n_ctx) && seq >= 0 &&
+                    seq < a.kv.n_seq;
+    if (!ok && tid == 0 && split == 0 && j == 0) record_error(a.err, pos < 0 || pos >= a.kv.n_ctx ? 1u : 2u);
+    const int n_keys = ok ? pos + 1 : 0;
+    const int chunk = (n_keys + a.n_splits - 1) / a.n_splits;
+    const int c0 = split * chunk;
+    const int c1 = min(c0 + chunk, n_keys);
+    const bool owner = FUSE && ok && c0 <= pos && pos < c1;  // this split holds the new key
+    const int64_t slab = ((int64_t)(ok ? seq : 0) * a.kv.n_kv + j) * a.kv.n_ctx * D;
+    const T* Kp = (const T*)a.kv.k + slab + sub * 8;
+    const T* Vp = (const T*)a.kv.v + slab + sub * 8;
+    const int cend = owner ? pos : c1;  // the new key (owner) is folded in from LDS below
+    int c = c0 + grp;
+    float kr[8], vr[8], kr2[8], vr2[8];
+    {
+        const int ca = c < cend ? c : 0, cb = c + NG < cend ? c + NG : 0;
+        load8(Kp + (int64_t)ca * D, kr, KT());
+        load8(Vp + (int64_t)ca * D, vr, KT());
+        load8(Kp + (int64_t)cb * D, kr2, KT());
+        load8(Vp + (int64_t)cb * D, vr2, KT());
+    }
+    // 3. finish the head items: RMSNorm + rotation (queries, key); the owner
+    //    writes key and value to cache row pos
+    if (FUSE) {
+#pragma unroll
+        for (int k = 0; k < IPW; ++k) {
+            const int it = wave + k * NW;
+            if (it >= G + 2 || !ok) continue;
+            if (it <= G) {
+                const float rs = 1.0f / sqrtf(wave_sum(u0[k] * u0[k] + u1[k] * u1[k]) / (float)D + a.eps);
+                if (lane < HALF) {
+                    const float x0 = u0[k] * rs * g0[k], x1 = u1[k] * rs * g1[k];
+                    const float2 cs = reinterpret_cast<const float2*>(a.rope)[(int64_t)pos * HALF + lane];
+                    const float r0 = x0 * cs.x - x1 * cs.y, r1 = x0 * cs.y + x1 * cs.x;
+                    if (it < G) {
+                        q_lds[it][lane] = r0 * scale;
+                        q_lds[it][lane + HALF] = r1 * scale;
+                    } else if (owner) {
+                        kn_lds[lane] = r0;
+                        kn_lds[lane + HALF] = r1;
+                        KT::st((T*)a.kv.k, slab + (int64_t)pos * D + lane, r0);
+                        KT::st((T*)a.kv.k, slab + (int64_t)pos * D + lane + HALF, r1);
+                    }
+                }
+            } else if (owner && lane < HALF) {
+                vn_lds[lane] = u0[k];
+                vn_lds[lane + HALF] = u1[k];
+                KT::st((T*)a.kv.v, slab + (int64_t)pos * D + lane, u0[k]);
+                KT::st((T*)a.kv.v, slab + (int64_t)pos * D + lane + HALF, u1[k]);
+            }
+        }
+    } else {
+        for (int t = tid; t < G * D; t += NW * 64)
+            q_lds[t / D][t % D] = ok ? a.q[(int64_t)r * a.ldq + (j * G + t / D) * D + t % D] * scale : 0.f;
+    }
+    __syncthreads();
+
+    float qv[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[g][i] = q_lds[g][sub * 8 + i];
     float m[G], l[G], o[G][8];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -57,79 +221,144 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const float* __restrict_
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[g][i] = 0.f;
     }
-    const int64_t slab = ((int64_t)(ok ? seq : 0) * kv.n_kv + j) * kv.n_ctx * D;
-    const T* Kp = (const T*)kv.k + slab + sub * 8;
-    const T* Vp = (const T*)kv.v + slab + sub * 8;
-    for (int c = c0 + grp; c < c1; c += GROUPS) {
-        float kr[8], vr[8];
-        load8(Kp + (int64_t)c * D, kr, KT());
-        load8(Vp + (int64_t)c * D, vr, KT());
+    // 4. cache rows [c0, cend): two per group per step, the next two in flight
+    for (; c < cend; c += 2 * NG) {
+        const bool two = c + NG < cend;
+        float s[G], s2[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            float s = 0.f;
+            float t1 = 0.f, t2 = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) s = fmaf(qv[g][i], kr[i], s);
-#pragma unroll
-            for (int off = LPK / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, WAVE);
-            const float mn = fmaxf(m[g], s);
-            const float alpha = exp2f(m[g] - mn);
-            const float p = exp2f(s - mn);
-            l[g] = l[g] * alpha + p;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[g][i] = fmaf(o[g][i], alpha, p * vr[i]);
-            m[g] = mn;
+            for (int i = 0; i < 8; ++i) {
+                t1 = fmaf(qv[g][i], kr[i], t1);
+                t2 = fmaf(qv[g][i], kr2[i], t2);
+            }
+            s[g] = group_sum<LPK>(t1);
+            s2[g] = two ? group_sum<LPK>(t2) : -INFINITY;
         }
+        float vcur[8], vcur2[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            vcur[i] = vr[i];
+            vcur2[i] = vr2[i];
+        }
+        const int cn = c + 2 * NG;
+        if (cn < cend) {
+            const int cb = cn + NG < cend ? cn + NG : cn;
+            load8(Kp + (int64_t)cn * D, kr, KT());
+            load8(Vp + (int64_t)cn * D, vr, KT());
+            load8(Kp + (int64_t)cb * D, kr2, KT());
+            load8(Vp + (int64_t)cb * D, vr2, KT());
+        }
+        step_state<G>(m, l, o, s, vcur);
+        if (two) step_state<G>(m, l, o, s2, vcur2);
     }
-    // merge the groups
-    if (sub == 0) {
+    // 5. the new key (held in LDS by the owner), folded in by group 0
+    if (owner && grp == 0) {
+        float kn[8], vn[8], s[G];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            kn[i] = kn_lds[sub * 8 + i];
+            vn[i] = vn_lds[sub * 8 + i];
+        }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            m_lds[grp][g] = m[g];
-            l_lds[grp][g] = l[g];
+            float t1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) t1 = fmaf(qv[g][i], kn[i], t1);
+            s[g] = group_sum<LPK>(t1);
+        }
+        step_state<G>(m, l, o, s, vn);
+    }
+    // 6. merge across rows of the wave (lane bits 4, 5) with permlane swaps; the
+    //    16-lane rows (for head_dim 64: both 8-lane groups of a row) then go to LDS
+    {
+        float m2[G], l2[G], o2[G][8];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            m2[g] = xor16(m[g]);
+            l2[g] = xor16(l[g]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o2[g][i] = xor16(o[g][i]);
+        }
+        merge_state<G>(m, l, o, m2, l2, o2);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            m2[g] = xor32(m[g]);
+            l2[g] = xor32(l[g]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o2[g][i] = xor32(o[g][i]);
+        }
+        merge_state<G>(m, l, o, m2, l2, o2);
+    }
+    if (lane < 16) {
+        const int slot = wave * (16 / LPK) + lane / LPK;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (sub == 0) {
+                wm_lds[slot][g] = m[g];
+                wl_lds[slot][g] = l[g];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wo_lds[slot][g][sub * 8 + i] = o[g][i];
         }
     }
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o_lds[grp][g][sub * 8 + i] = o[g][i];
     __syncthreads();
-    // thread t < G*D: head g = t / D, element e = t % D
-    for (int t = tid; t < G * D; t += 256) {
+    // 7. merge the slots; write o (one split) or the split's partial record
+    for (int t = tid; t < G * D; t += NW * 64) {
         const int g = t / D, e = t % D;
         float M = -INFINITY;
-        for (int k = 0; k < GROUPS; ++k) M = fmaxf(M, m_lds[k][g]);
+#pragma unroll
+        for (int w = 0; w < SLOTS; ++w) M = fmaxf(M, wm_lds[w][g]);
         float L = 0.f, O = 0.f;
         if (M != -INFINITY) {
-            for (int k = 0; k < GROUPS; ++k) {
-                const float w = exp2f(m_lds[k][g] - M);
-                L += w * l_lds[k][g];
-                O += w * o_lds[k][g][e];
+#pragma unroll
+            for (int w = 0; w < SLOTS; ++w) {
+                const float f = exp2f(wm_lds[w][g] - M);
+                L += f * wl_lds[w][g];
+                O += f * wo_lds[w][g][e];
             }
         }
-        float* pp = part + (((int64_t)r * n_heads + j * G + g) * n_splits + split) * (D + 2);
-        if (e == 0) {
-            pp[0] = M;
-            pp[1] = L;
+        if (a.n_splits == 1) {
+            const float v = L > 0.f ? O / L : 0.f;
+            const int64_t idx = (int64_t)r * a.ldo + (j * G + g) * D + e;
+            if (a.out_f32) {
+                a.out_f32[idx] = v;
+            } else {
+                uint16_t hi, lo;
+                split_bf16(v, hi, lo);
+                a.out_bf16[idx] = hi;
+                if (a.out_lo) a.out_lo[idx] = lo;
+            }
+        } else {
+            float* pp = a.part + (((int64_t)r * a.n_heads + j * G + g) * a.n_splits + split) * (D + 4);
+            if (e == 0) {
+                pp[0] = M;
+                pp[1] = L;
+            }
+            pp[4 + e] = O;
         }
-        pp[2 + e] = O;
     }
 }
 
 // Merge the splits of each (row, query head): o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// Partial records are [m, l, -, -, o[D]] (D + 4 floats, 16-byte aligned).
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict__ part, int n_heads, int n_splits,
                                                          float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16,
                                                          uint16_t* __restrict__ out_lo, int64_t ldo) {
     const int r = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
-    const float* pp = part + ((int64_t)r * n_heads + h) * n_splits * (D + 2);
+    const float* pp = part + ((int64_t)r * n_heads + h) * n_splits * (D + 4);
     float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, pp[s * (D + 2)]);
+#pragma unroll 16
+    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, pp[s * (D + 4)]);
     float L = 0.f, O = 0.f;
     if (M != -INFINITY) {
+#pragma unroll 16
         for (int s = 0; s < n_splits; ++s) {
-            const float w = exp2f(pp[s * (D + 2)] - M);
-            L += w * pp[s * (D + 2) + 1];
-            O += w * pp[s * (D + 2) + 2 + e];
+            const float w = exp2f(pp[s * (D + 4)] - M);
+            L += w * pp[s * (D + 4) + 1];
+            O += w * pp[s * (D + 4) + 4 + e];
         }
     }
     const float v = L > 0.f ? O / L : 0.f;
@@ -144,38 +373,52 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
     }
 }
 
-template <class KT, int D>
-static void rows_dispatch_g(const float* q, int64_t ldq, int R, int n_heads, RowMap rm, KVLayer kv, int n_splits,
-                            float* part, uint32_t* err, hipStream_t s) {
-    const int G = n_heads / kv.n_kv;
-    dim3 grid(R, kv.n_kv, n_splits);
+template <class KT, class GT, int D, bool FUSE>
+static hipError_t rows_dispatch(const RowsArgs& a, int R, hipStream_t s) {
+    const int G = a.n_heads / a.kv.n_kv;
+    const dim3 grid(R, a.kv.n_kv, a.n_splits);
+#define ROWS_LAUNCH(G_)                                                                             \
+    do {                                                                                            \
+        constexpr int NW_ = G_ <= 2 ? 4 : 8;                                                      \
+        attn_rows_kernel<KT, GT, D, G_, NW_, FUSE><<<grid, NW_ * 64, 0, s>>>(a);                  \
+    } while (0)
     switch (G) {
-        case 1: attn_rows_kernel<KT, D, 1><<<grid, 256, 0, s>>>(q, ldq, n_heads, rm, kv, n_splits, part, err); break;
-        case 2: attn_rows_kernel<KT, D, 2><<<grid, 256, 0, s>>>(q, ldq, n_heads, rm, kv, n_splits, part, err); break;
-        case 4: attn_rows_kernel<KT, D, 4><<<grid, 256, 0, s>>>(q, ldq, n_heads, rm, kv, n_splits, part, err); break;
-        case 8: attn_rows_kernel<KT, D, 8><<<grid, 256, 0, s>>>(q, ldq, n_heads, rm, kv, n_splits, part, err); break;
-        default: break;
+        case 1: ROWS_LAUNCH(1); break;
+        case 2: ROWS_LAUNCH(2); break;
+        case 4: ROWS_LAUNCH(4); break;
+        case 8: ROWS_LAUNCH(8); break;
+        default: return hipErrorInvalidValue;
     }
+#undef ROWS_LAUNCH
+    if (a.n_splits > 1 && (a.out_f32 || a.out_bf16))
+        attn_combine_kernel<D><<<dim3(R, a.n_heads), D, 0, s>>>(a.part, a.n_heads, a.n_splits, a.out_f32, a.out_bf16,
+                                                                a.out_lo, a.ldo);
+    return hipGetLastError();
+}
+
+template <class GT, bool FUSE>
+static hipError_t rows_dispatch_kv(const RowsArgs& a, int R, hipStream_t s) {
+    if (a.kv.d == 128)
+        return a.kv.type == KV_F16 ? rows_dispatch<F16, GT, 128, FUSE>(a, R, s) : rows_dispatch<F32, GT, 128, FUSE>(a, R, s);
+    if (a.kv.d == 64)
+        return a.kv.type == KV_F16 ? rows_dispatch<F16, GT, 64, FUSE>(a, R, s) : rows_dispatch<F32, GT, 64, FUSE>(a, R, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, RowMap rm, KVLayer kv, int n_splits,
                             float* part, float* out_f32, uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo,
-                            uint32_t* err, hipStream_t s) {
+                            uint32_t* err, const QkRope* fuse, WType gt, hipStream_t s) {
     if (R <= 0) return hipSuccess;
-    const int G = n_heads / kv.n_kv;
-    if (G != 1 && G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
-    if (kv.d == 128) {
-        if (kv.type == KV_F16) rows_dispatch_g<F16, 128>(q, ldq, R, n_heads, rm, kv, n_splits, part, err, s);
-        else rows_dispatch_g<F32, 128>(q, ldq, R, n_heads, rm, kv, n_splits, part, err, s);
-        attn_combine_kernel<128><<<dim3(R, n_heads), 128, 0, s>>>(part, n_heads, n_splits, out_f32, out_bf16, out_bf16_lo, ldo);
-    } else if (kv.d == 64) {
-        if (kv.type == KV_F16) rows_dispatch_g<F16, 64>(q, ldq, R, n_heads, rm, kv, n_splits, part, err, s);
-        else rows_dispatch_g<F32, 64>(q, ldq, R, n_heads, rm, kv, n_splits, part, err, s);
-        attn_combine_kernel<64><<<dim3(R, n_heads), 64, 0, s>>>(part, n_heads, n_splits, out_f32, out_bf16, out_bf16_lo, ldo);
-    } else {
-        return hipErrorInvalidValue;
+    if (n_splits < 1 || n_splits > 64) return hipErrorInvalidValue;
+    RowsArgs a{};
+    a.q = q; a.ldq = ldq; a.n_heads = n_heads; a.rm = rm; a.kv = kv; a.n_splits = n_splits; a.part = part;
+    a.out_f32 = out_f32; a.out_bf16 = out_bf16; a.out_lo = out_bf16_lo; a.ldo = ldo; a.err = err;
+    if (fuse) {
+        a.q_gain = fuse->q_gain; a.k_gain = fuse->k_gain; a.eps = fuse->eps; a.rope = fuse->rope;
+        a.max_pos = fuse->max_pos;
+        return gt == W_BF16 ? rows_dispatch_kv<BF16, true>(a, R, s) : rows_dispatch_kv<F32, true>(a, R, s);
     }
-    return hipGetLastError();
+    return rows_dispatch_kv<BF16, false>(a, R, s);
 }
 
 // ------------------------------------------------------------------ causal flash prefill (MFMA, f16 cache)

@@ -2,298 +2,524 @@
 // fp32-weight path): y = x W^T over a few activation rows, with the block's
 // RMSNorm fused in front and residual / SwiGLU / argmax fused behind.
 //
-// Layout: W is [N, K] row-major (bf16 or fp32). A wave owns RW output rows
-// (SwiGLU: RW gate rows and the RW matching up rows); each lane streams
-// 8 consecutive K elements per 512-wide chunk with 16-byte loads, so a wave
-// reads 1 KB (bf16) of a row per instruction, fully coalesced. Activations
-// are fp32 and stay fp32: products are exact, accumulation is fp32. A
-// workgroup of 4 waves serves BT activation rows; more rows tile blockIdx.y.
+// Layout: W is [N, K] row-major (bf16 or fp32). A workgroup of 4 waves owns
+// NR weight rows; the K axis is dealt to the waves in 512-element chunks
+// (wave w takes chunks w, w+4, ...), and in each chunk lane l reads the 8
+// consecutive elements at 8l with one 16-byte load per row (bf16), so a wave
+// reads 1 KB of a row per instruction, fully coalesced. Every weight load of
+// the workgroup is issued before anything waits on memory: addresses are
+// clamped instead of branched around, and the RMSNorm statistics come from
+// the same activation chunks the dot products use, summed in the one LDS
+// reduction that also merges the waves' partial dot products (a butterfly
+// leaves one (row, activation-row) sum per lane group). Activations are fp32
+// and stay fp32: products are exact, accumulation is fp32. BT activation rows
+// per workgroup; more tile blockIdx.y.
 #include "common.h"
 #include "launch.h"
 
 namespace sttd {
 
-template <class WT, int BT>
-__device__ __forceinline__ void row_scales(const float* __restrict__ x, int64_t ldx, int nb, int K, float eps,
-                                           float* rs /*[BT]*/) {
-    __shared__ float red[4][BT];
-    const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE;
-    float ss[BT];
-#pragma unroll
-    for (int b = 0; b < BT; ++b) {
-        ss[b] = 0.f;
-        if (b < nb) {
-            const float* xr = x + b * ldx;
-            for (int i = threadIdx.x * 4; i < K; i += 1024) {
-                float4 v = *reinterpret_cast<const float4*>(xr + i);
-                ss[b] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-            }
-        }
-        ss[b] = wave_sum(ss[b]);
+constexpr int CHUNK = 512;  // K elements per wave per step (64 lanes x 8)
+
+// 8 consecutive weights in their storage form.
+template <class WT>
+struct Raw8;
+template <>
+struct Raw8<BF16> {
+    u32x4 v;
+    __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const u32x4*>(p); }
+    __device__ __forceinline__ void widen(float* o) const {
+        o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xFFFF0000u);
+        o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xFFFF0000u);
+        o[4] = __uint_as_float(v.z << 16); o[5] = __uint_as_float(v.z & 0xFFFF0000u);
+        o[6] = __uint_as_float(v.w << 16); o[7] = __uint_as_float(v.w & 0xFFFF0000u);
     }
-    if (lane == 0) {
-#pragma unroll
-        for (int b = 0; b < BT; ++b) red[wave][b] = ss[b];
+};
+template <>
+struct Raw8<F32> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const f32x4*>(p);
+        b = *reinterpret_cast<const f32x4*>(p + 4);
     }
-    __syncthreads();
-#pragma unroll
-    for (int b = 0; b < BT; ++b) rs[b] = 1.0f / sqrtf((red[0][b] + red[1][b] + red[2][b] + red[3][b]) / (float)K + eps);
+    __device__ __forceinline__ void widen(float* o) const {
+        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+        o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    }
+};
+
+// Butterfly reduction of V partial sums per lane (V a power of two, V <= 64).
+// The first log2(V) steps exchange halves with a partner lane (partners by
+// lane bit 3, 2, 1, 0 through DPP, then bit 4, 5 through permlane swaps): the lane
+// whose deciding bit is set keeps the upper half. Remaining steps add plainly.
+// On return every lane holds the full sum of value index multi_index<V>(lane).
+template <int CTRL>
+__device__ __forceinline__ float lane_partner(float v, int off) {
+    if (CTRL != 0) return dpp_move<CTRL>(v);
+    return off == 16 ? xor16(v) : xor32(v);
 }
 
-// Dot products of NR weight rows with BT activation rows, one wave; results
-// are complete (wave-reduced) in every lane.
-template <class WT, int NR, int BT, bool NORM>
-__device__ __forceinline__ void wave_dots(const typename WT::T* const* wr, const bool* valid,
-                                          const float* __restrict__ x, int64_t ldx, int nb, int K,
-                                          const typename WT::T* __restrict__ gain, float (&acc)[NR][BT]) {
-    const int lane = threadIdx.x % WAVE;
+constexpr int kStepBit[6] = {3, 2, 1, 0, 4, 5};
+
+template <int V>
+__device__ __forceinline__ int multi_index(int lane) {
+    int idx = 0, width = V;
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
+    for (int st = 0; st < 6; ++st) {
+        if (width > 1) {
+            idx = idx * 2 + ((lane >> kStepBit[st]) & 1);
+            width /= 2;
+        }
+    }
+    return idx;
+}
+
+// true for one lane per value index (the lanes whose plain-sum bits are zero)
+template <int V>
+__device__ __forceinline__ bool multi_writer(int lane) {
+    int width = V, mask = 0;
 #pragma unroll
-        for (int b = 0; b < BT; ++b) acc[r][b] = 0.f;
-#pragma unroll 2
-    for (int k = lane * 8; k < K; k += 512) {
-        float wv[NR][8];
+    for (int st = 0; st < 6; ++st) {
+        if (width > 1) width /= 2;
+        else mask |= 1 << kStepBit[st];
+    }
+    return (lane & mask) == 0;
+}
+
+template <int V, int ST, int CTRL, int OFF>
+__device__ __forceinline__ void butterfly_step(float (&v)[V], int& width, int lane) {
+    if (width > 1) {
+        const int half = width / 2;
+        const bool upper = (lane >> kStepBit[ST]) & 1;
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            if (valid[r]) load8(wr[r] + k, wv[r], WT());
-            else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) wv[r][i] = 0.f;
+        for (int i = 0; i < V / 2; ++i) {
+            if (i < half) {
+                const float send = upper ? v[i] : v[i + half];
+                const float keep = upper ? v[i + half] : v[i];
+                v[i] = keep + lane_partner<CTRL>(send, OFF);
             }
         }
+        width = half;
+    } else {
+        v[0] += lane_partner<CTRL>(v[0], OFF);
+    }
+}
+
+template <int V>
+__device__ __forceinline__ float wave_reduce_multi(float (&v)[V]) {
+    const int lane = threadIdx.x % WAVE;
+    int width = V;
+    butterfly_step<V, 0, DPP_ROW_MIRROR, 0>(v, width, lane);
+    butterfly_step<V, 1, DPP_ROW_HALF_MIRROR, 0>(v, width, lane);
+    butterfly_step<V, 2, DPP_XOR2, 0>(v, width, lane);
+    butterfly_step<V, 3, DPP_XOR1, 0>(v, width, lane);
+    butterfly_step<V, 4, 0, 16>(v, width, lane);
+    butterfly_step<V, 5, 0, 32>(v, width, lane);
+    return v[0];
+}
+
+// This wave's activation chunks: xv[c][b][i] = x[b][k_c + i] (* gain when NORM),
+// zero where k_c + i >= K or b >= nb; ss[b] += sum of x^2 over those elements.
+template <class WT, int KCH, int BT, bool NORM>
+__device__ __forceinline__ void load_activations(const float* __restrict__ x, int64_t ldx, int nb, int K,
+                                                 const typename WT::T* __restrict__ gain, const int (&kk)[KCH],
+                                                 float (&xv)[KCH][BT][8], float (&ss)[BT]) {
+#pragma unroll
+    for (int b = 0; b < BT; ++b) ss[b] = 0.f;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+        const bool in = kk[c] < K;
+        const int k = in ? kk[c] : 0;
         float gv[8];
         if (NORM) load8(gain + k, gv, WT());
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
-            if (b < nb) {
-                float xv[8];
-                load8(x + b * ldx + k, xv, F32());
-                if (NORM) {
+            float v[8];
+            load8(x + (int64_t)(b < nb ? b : 0) * ldx + k, v, F32());
+            const bool use = in && b < nb;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) xv[i] *= gv[i];
-                }
-#pragma unroll
-                for (int r = 0; r < NR; ++r)
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[r][b] = fmaf(wv[r][i], xv[i], acc[r][b]);
+            for (int i = 0; i < 8; ++i) {
+                const float xi = use ? v[i] : 0.f;
+                ss[b] = fmaf(xi, xi, ss[b]);
+                xv[c][b][i] = NORM ? xi * gv[i] : xi;
             }
         }
     }
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-        for (int b = 0; b < BT; ++b) acc[r][b] = wave_sum(acc[r][b]);
 }
 
-template <class WT, int EPI, int BT, int RW, bool NORM>
+// Activation chunks merged from attention split partials (see GemvArgs::xpart):
+// one online pass over the splits per 8-element chunk (8 divides head_dim).
+template <int KCH, int BT>
+__device__ __forceinline__ void load_activations_merged(const GemvArgs& a, int b0, int nb, const int (&kk)[KCH],
+                                                        float (&xv)[KCH][BT][8]) {
+    const int n_heads = a.K / a.head_dim;
+    const int rec = a.head_dim + 4;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+        const bool in = kk[c] < a.K;
+        const int k = in ? kk[c] : 0;
+        const int h = k / a.head_dim, e0 = k % a.head_dim;
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+            const bool use = in && b < nb;
+            const float* pr = a.xpart + ((int64_t)((b0 + (b < nb ? b : 0)) * n_heads + h) * a.n_splits) * rec;
+            float M = -INFINITY, L = 0.f, O[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) O[i] = 0.f;
+#pragma unroll 4
+            for (int sp = 0; sp < a.n_splits; ++sp) {
+                const float* p = pr + (int64_t)sp * rec;
+                const float ms = p[0], ls = p[1];
+                float os[8];
+                load8(p + 4 + e0, os, F32());
+                const float Mn = fmaxf(M, ms);
+                const float fa = Mn == -INFINITY ? 0.f : exp2f(M - Mn);
+                const float fb = Mn == -INFINITY ? 0.f : exp2f(ms - Mn);
+                L = L * fa + ls * fb;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) O[i] = O[i] * fa + os[i] * fb;
+                M = Mn;
+            }
+            const float inv = L > 0.f ? 1.0f / L : 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xv[c][b][i] = use ? O[i] * inv : 0.f;
+        }
+    }
+}
+
+// Dot products of the loaded weight chunks with the activation chunks.
+template <class WT, int KCH, int NR, int BT>
+__device__ __forceinline__ void chunk_dots(const Raw8<WT> (&w)[KCH][NR], const float (&xv)[KCH][BT][8],
+                                           float (&acc)[NR * BT]) {
+#pragma unroll
+    for (int i = 0; i < NR * BT; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            float wf[8];
+            w[c][r].widen(wf);
+#pragma unroll
+            for (int b = 0; b < BT; ++b)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[r * BT + b] = fmaf(wf[i], xv[c][b][i], acc[r * BT + b]);
+        }
+    }
+}
+
+// Merge the waves: on return dot holds the full sum of value index t = r*BT + b
+// for threads t < NR*BT, and rs[b] the row scale (1 when !NORM), in every thread.
+template <int V, int BT, bool NORM>
+__device__ __forceinline__ void block_merge(float (&acc)[V], float (&ss)[BT], float (*red)[V + BT], int K, float eps,
+                                            float& dot, float (&rs)[BT]) {
+    const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE;
+    const float s = wave_reduce_multi<V>(acc);
+    if (multi_writer<V>(lane)) red[wave][multi_index<V>(lane)] = s;
+    if (NORM) {
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+            const float t = wave_sum(ss[b]);
+            if (lane == 0) red[wave][V + b] = t;
+        }
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    dot = t < V ? red[0][t] + red[1][t] + red[2][t] + red[3][t] : 0.f;
+#pragma unroll
+    for (int b = 0; b < BT; ++b)
+        rs[b] = NORM ? 1.0f / sqrtf((red[0][V + b] + red[1][V + b] + red[2][V + b] + red[3][V + b]) / (float)K + eps)
+                     : 1.f;
+}
+
+template <class WT, int EPI, int BT, int NR, int KCH, bool NORM, bool XPART>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     typedef typename WT::T T;
-    constexpr int NR = EPI == GEMV_SWIGLU ? 2 * RW : RW;
-    const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE;
+    constexpr int V = NR * BT;
+    __shared__ float red[4][V + BT];
+    __shared__ float vals[V];
+    const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE, t = threadIdx.x;
     const int b0 = blockIdx.y * BT;
     const int nb = min(BT, a.rows - b0);
     const float* x = a.x + (int64_t)b0 * a.ldx;
 
-    float rs[BT];
-    if (NORM) row_scales<WT, BT>(x, a.ldx, nb, a.K, a.eps, rs);
-    else {
-#pragma unroll
-        for (int b = 0; b < BT; ++b) rs[b] = 1.f;
-    }
-
-    const int n0 = (blockIdx.x * 4 + wave) * RW;  // first output column of this wave
-    if (n0 >= a.N) return;
+    // weight rows of this workgroup (clamped to valid rows)
     const T* wr[NR];
-    bool valid[NR];
+    int n0;
     if (EPI == GEMV_SWIGLU) {
+        constexpr int NP = NR / 2;
+        n0 = blockIdx.x * NP;
         const T* W = (const T*)a.w[0];
 #pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            valid[r] = valid[RW + r] = (n0 + r) < a.N;
-            wr[r] = W + (int64_t)(n0 + r) * a.K;
-            wr[RW + r] = W + (int64_t)(n0 + r + a.N) * a.K;
+        for (int r = 0; r < NP; ++r) {
+            const int n = min(n0 + r, a.N - 1);
+            wr[r] = W + (int64_t)n * a.K;
+            wr[NP + r] = W + (int64_t)(n + a.N) * a.K;
         }
     } else {
+        n0 = blockIdx.x * NR;
         const bool s2 = n0 >= a.seg_end[1], s1 = n0 >= a.seg_end[0];
         const int start = s2 ? a.seg_end[1] : (s1 ? a.seg_end[0] : 0);
+        const int end = s2 ? a.seg_end[2] : (s1 ? a.seg_end[1] : a.seg_end[0]);
         const T* W = (const T*)(s2 ? a.w[2] : (s1 ? a.w[1] : a.w[0]));
 #pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            valid[r] = (n0 + r) < a.N;
-            wr[r] = W + (int64_t)(n0 + r - start) * a.K;
-        }
+        for (int r = 0; r < NR; ++r) wr[r] = W + (int64_t)(min(n0 + r, end - 1) - start) * a.K;
     }
-
-    float acc[NR][BT];
-    wave_dots<WT, NR, BT, NORM>(wr, valid, x, a.ldx, nb, a.K, (const T*)a.gain, acc);
-
-    // epilogue: lane (r * BT + b) writes output (b, n0 + r)
+    // 1. every weight load of the workgroup, in flight at once
+    int kk[KCH];
+    Raw8<WT> w[KCH][NR];
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
+    for (int c = 0; c < KCH; ++c) {
+        kk[c] = (c * 4 + wave) * CHUNK + lane * 8;
+        const int k = kk[c] < a.K ? kk[c] : 0;
 #pragma unroll
-        for (int b = 0; b < BT; ++b) {
-            if (lane != r * BT + b || b >= nb || !valid[r]) continue;
-            const int64_t row = b0 + b;
-            const int n = n0 + r;
-            float v = acc[r][b] * rs[b];
-            if (EPI == GEMV_SWIGLU) {
-                const float u = acc[RW + r][b] * rs[b];
-                v = v / (1.0f + expf(-v)) * u;
-            } else if (EPI == GEMV_RESID) {
-                v += a.resid[row * a.ldr + n];
+        for (int r = 0; r < NR; ++r) w[c][r].load(wr[r] + k);
+    }
+    // 2. activations (and the RMSNorm statistics) of the same chunks
+    float xv[KCH][BT][8], ss[BT];
+    if (XPART) {
+        load_activations_merged<KCH, BT>(a, b0, nb, kk, xv);
+#pragma unroll
+        for (int b = 0; b < BT; ++b) ss[b] = 0.f;
+    } else {
+        load_activations<WT, KCH, BT, NORM>(x, a.ldx, nb, a.K, (const T*)a.gain, kk, xv, ss);
+    }
+    // 3. dot products, merged over the waves
+    float acc[V];
+    chunk_dots<WT, KCH, NR, BT>(w, xv, acc);
+    float dot, rs[BT];
+    block_merge<V, BT, NORM>(acc, ss, red, a.K, a.eps, dot, rs);
+
+    if (EPI == GEMV_SWIGLU) {
+        if (t < V) vals[t] = dot;
+        __syncthreads();
+        constexpr int NP = NR / 2;
+        if (t < NP * BT) {
+            const int r = t / BT, b = t % BT;
+            if (b < nb && n0 + r < a.N) {
+                const float gt = vals[r * BT + b] * rs[b];
+                const float up = vals[(NP + r) * BT + b] * rs[b];
+                a.y[(int64_t)(b0 + b) * a.ldy + n0 + r] = gt / (1.0f + expf(-gt)) * up;
             }
-            a.y[row * a.ldy + n] = v;
+        }
+        return;
+    }
+    if (t < V) {
+        const int r = t / BT, b = t % BT;
+        if (b < nb && n0 + r < a.N) {
+            float v = dot * rs[b];
+            const int64_t row = b0 + b;
+            if (EPI == GEMV_RESID) v += a.resid[row * a.ldr + n0 + r];
+            a.y[row * a.ldy + n0 + r] = v;
         }
     }
 }
 
-template <class WT, int EPI, int RW, bool NORM>
+template <class WT, int EPI, int NR, int KCH, bool NORM, bool XPART>
 static void launch_bt(const GemvArgs& a, hipStream_t s) {
-    const int waves = (a.N + RW - 1) / RW;
-    dim3 grid((waves + 3) / 4, 1);
+    const int per_wg = EPI == GEMV_SWIGLU ? NR / 2 : NR;
+    dim3 grid((a.N + per_wg - 1) / per_wg, 1);
     if (a.rows == 1) {
-        gemv_kernel<WT, EPI, 1, RW, NORM><<<grid, 256, 0, s>>>(a);
+        gemv_kernel<WT, EPI, 1, NR, KCH, NORM, XPART><<<grid, 256, 0, s>>>(a);
     } else if (a.rows == 2) {
-        gemv_kernel<WT, EPI, 2, RW, NORM><<<grid, 256, 0, s>>>(a);
+        gemv_kernel<WT, EPI, 2, NR, KCH, NORM, XPART><<<grid, 256, 0, s>>>(a);
     } else {
         grid.y = (a.rows + 3) / 4;
-        gemv_kernel<WT, EPI, 4, RW, NORM><<<grid, 256, 0, s>>>(a);
+        gemv_kernel<WT, EPI, 4, NR, KCH, NORM, XPART><<<grid, 256, 0, s>>>(a);
     }
+}
+
+template <class WT, int EPI, int NR, bool NORM, bool XPART = false>
+static hipError_t launch_k(const GemvArgs& a, hipStream_t s) {
+    const int kch = (a.K + 4 * CHUNK - 1) / (4 * CHUNK);
+    switch (kch) {
+        case 1: launch_bt<WT, EPI, NR, 1, NORM, XPART>(a, s); break;
+        case 2: launch_bt<WT, EPI, NR, 2, NORM, XPART>(a, s); break;
+        case 3: launch_bt<WT, EPI, NR, 3, NORM, XPART>(a, s); break;
+        case 4: launch_bt<WT, EPI, NR, 4, NORM, XPART>(a, s); break;
+        default: return hipErrorInvalidValue;  // K > 8192
+    }
+    return hipGetLastError();
 }
 
 template <class WT>
-static void launch_wt(const GemvArgs& a, GemvEpi epi, hipStream_t s) {
+static hipError_t launch_wt(const GemvArgs& a, GemvEpi epi, hipStream_t s) {
+    // Rows per workgroup, measured on the decode shapes: more, shorter workgroups
+    // overlap one another's load latency and reduction tails better than fewer,
+    // wider ones (2-4 rows beat 8-16 by 10-40%).
     const bool norm = a.gain != nullptr;
-    if (epi == GEMV_SWIGLU) {
-        if (norm) launch_bt<WT, GEMV_SWIGLU, 1, true>(a, s);
-        else launch_bt<WT, GEMV_SWIGLU, 1, false>(a, s);
-    } else if (epi == GEMV_RESID) {
-        if (norm) launch_bt<WT, GEMV_RESID, 2, true>(a, s);
-        else launch_bt<WT, GEMV_RESID, 2, false>(a, s);
-    } else {
-        if (norm) launch_bt<WT, GEMV_STORE, 2, true>(a, s);
-        else launch_bt<WT, GEMV_STORE, 2, false>(a, s);
+    if (epi == GEMV_SWIGLU)
+        return norm ? launch_k<WT, GEMV_SWIGLU, 4, true>(a, s) : launch_k<WT, GEMV_SWIGLU, 4, false>(a, s);
+    if (epi == GEMV_RESID) {
+        if (a.xpart) return launch_k<WT, GEMV_RESID, 2, false, true>(a, s);
+        return norm ? launch_k<WT, GEMV_RESID, 2, true>(a, s) : launch_k<WT, GEMV_RESID, 2, false>(a, s);
     }
+    return norm ? launch_k<WT, GEMV_STORE, 4, true>(a, s) : launch_k<WT, GEMV_STORE, 4, false>(a, s);
 }
 
 hipError_t launch_gemv(const GemvArgs& a, WType wt, GemvEpi epi, hipStream_t s) {
     if (a.rows <= 0 || a.N <= 0) return hipSuccess;
-    if (wt == W_BF16) launch_wt<BF16>(a, epi, s);
-    else launch_wt<F32>(a, epi, s);
-    return hipGetLastError();
+    return wt == W_BF16 ? launch_wt<BF16>(a, epi, s) : launch_wt<F32>(a, epi, s);
 }
 
 // ------------------------------------------------------------------ lm_head + argmax
 // Final RMSNorm and the tied head (build_step_graph on the Qwen3-ASR decoder
-// page: logits = E * (RMSNorm(x) * g), then argmax on device). Each wave scores
-// RW vocabulary rows; the workgroup's best (logit, index) per activation row is
-// folded into a 64-bit slot with one atomic max, the key being
-// (order-preserving bits of the logit) << 32 | ~index, so the largest logit
-// wins and, among equal logits, the lowest index (the strict greater-than scan
-// of run() on the model page). The last workgroup to finish (atomic counter)
-// reads the slots, writes the ids, gathers the next input rows E[id], bumps the
-// positions and re-zeroes slots and counter for the next call.
-template <class WT, int BT, int RW>
+// page: logits = E * (RMSNorm(x) * g), then argmax on device). A persistent
+// grid walks the vocabulary in blocks of NR rows, fetching the next block's
+// weights while it finishes the current one. Each workgroup keeps, per
+// activation row, its best (logit, index) as the 64-bit key
+// (order-preserving bits of the logit) << 32 | ~index, so the larger logit
+// wins and, among equal logits, the lower index (the strict greater-than scan
+// of run() on the model page), and writes it to a partials array;
+// lm_head_finalize reduces them, writes the ids, gathers the next input rows
+// E[id] and bumps the positions. No atomics, nothing to re-arm.
+template <class WT, int BT, int NR, int KCH>
 __global__ __launch_bounds__(256) void lm_head_kernel(HeadArgs a) {
     typedef typename WT::T T;
-    __shared__ unsigned long long best_lds[4][BT];
-    __shared__ int last_lds;
-    const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE;
+    constexpr int V = NR * BT;
+    __shared__ float red[4][V + BT];
+    __shared__ unsigned long long keys[V];
+    const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE, t = threadIdx.x;
     const int b0 = blockIdx.y * BT;
     const int nb = min(BT, a.rows - b0);
     const float* x = a.x + (int64_t)b0 * a.ldx;
-    float rs[BT];
-    row_scales<WT, BT>(x, a.ldx, nb, a.hidden, a.eps, rs);
-
-    const int n0 = (blockIdx.x * 4 + wave) * RW;
     const T* E = (const T*)a.embed;
-    const T* wr[RW];
-    bool valid[RW];
-#pragma unroll
-    for (int r = 0; r < RW; ++r) {
-        valid[r] = (n0 + r) < a.vocab;
-        wr[r] = E + (int64_t)(valid[r] ? n0 + r : 0) * a.hidden;
-    }
-    float acc[RW][BT];
-    wave_dots<WT, RW, BT, true>(wr, valid, x, a.ldx, nb, a.hidden, (const T*)a.gain, acc);
+    const int n_blocks = (a.vocab + NR - 1) / NR;
 
-    unsigned long long best[BT];
+    int kk[KCH];
 #pragma unroll
-    for (int b = 0; b < BT; ++b) {
-        best[b] = 0ull;
+    for (int c = 0; c < KCH; ++c) kk[c] = (c * 4 + wave) * CHUNK + lane * 8;
+    auto fetch = [&](int blk, Raw8<WT> (&w)[KCH][NR]) {
 #pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            if (!valid[r]) continue;
-            const float v = acc[r][b] * rs[b];
-            const unsigned long long key =
-                ((unsigned long long)float_order_key(v) << 32) | (unsigned long long)(~(uint32_t)(n0 + r));
-            best[b] = key > best[b] ? key : best[b];
-            if (a.logits && b < nb && lane == r) a.logits[(int64_t)(b0 + b) * a.vocab + n0 + r] = v;
+        for (int c = 0; c < KCH; ++c) {
+            const int k = kk[c] < a.hidden ? kk[c] : 0;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) w[c][r].load(E + (int64_t)min(blk * NR + r, a.vocab - 1) * a.hidden + k);
         }
-    }
-    if (lane == 0) {
+    };
+    Raw8<WT> wc[KCH][NR], wn[KCH][NR];
+    int blk = blockIdx.x;
+    if (blk < n_blocks) fetch(blk, wc);
+    float xv[KCH][BT][8], ss[BT];
+    load_activations<WT, KCH, BT, true>(x, a.ldx, nb, a.hidden, (const T*)a.gain, kk, xv, ss);
+    float rs[BT];
+    {
+        // row scales once per workgroup
 #pragma unroll
-        for (int b = 0; b < BT; ++b) best_lds[wave][b] = best[b];
+        for (int b = 0; b < BT; ++b) {
+            const float s = wave_sum(ss[b]);
+            if (lane == 0) red[wave][b] = s;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < BT; ++b)
+            rs[b] = 1.0f / sqrtf((red[0][b] + red[1][b] + red[2][b] + red[3][b]) / (float)a.hidden + a.eps);
+        __syncthreads();
     }
-    __syncthreads();
-    if (threadIdx.x < BT && threadIdx.x < nb) {
-        const int b = threadIdx.x;
-        unsigned long long m = best_lds[0][b];
-        for (int w = 1; w < 4; ++w) m = best_lds[w][b] > m ? best_lds[w][b] : m;
-        atomicMax(&a.slots[b0 + b], m);
+    unsigned long long best = 0ull;  // thread t < BT: best key of activation row t
+    for (; blk < n_blocks; blk += gridDim.x) {
+        const int nxt = blk + gridDim.x;
+        if (nxt < n_blocks) fetch(nxt, wn);
+        float acc[V];
+        chunk_dots<WT, KCH, NR, BT>(wc, xv, acc);
+        float dot, dummy[BT];
+        float no_ss[BT];
+#pragma unroll
+        for (int b = 0; b < BT; ++b) no_ss[b] = 0.f;
+        block_merge<V, BT, false>(acc, no_ss, red, a.hidden, a.eps, dot, dummy);
+        if (t < V) {
+            const int r = t / BT, b = t % BT;
+            unsigned long long key = 0ull;
+            const int n = blk * NR + r;
+            if (b < nb && n < a.vocab) {
+                const float v = dot * rs[b];
+                key = ((unsigned long long)float_order_key(v) << 32) | (unsigned long long)(~(uint32_t)n);
+                if (a.logits) a.logits[(int64_t)(b0 + b) * a.vocab + n] = v;
+            }
+            keys[t] = key;
+        }
+        __syncthreads();
+        if (t < BT) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) best = keys[r * BT + t] > best ? keys[r * BT + t] : best;
+        }
+#pragma unroll
+        for (int c = 0; c < KCH; ++c)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) wc[c][r] = wn[c][r];
     }
-    __threadfence();
+    if (t < nb) a.partials[(int64_t)(b0 + t) * gridDim.x + blockIdx.x] = best;
+}
+
+// One workgroup per activation row: reduce the partial keys, emit the id.
+template <class WT>
+__global__ __launch_bounds__(256) void lm_head_finalize_kernel(HeadArgs a, int n_partials) {
+    typedef typename WT::T T;
+    __shared__ unsigned long long red[4];
+    __shared__ int id_lds;
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE;
+    unsigned long long best = 0ull;
+    for (int i = threadIdx.x; i < n_partials; i += 256) {
+        const unsigned long long k = a.partials[(int64_t)b * n_partials + i];
+        best = k > best ? k : best;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const unsigned long long o = __shfl_xor(best, off, WAVE);
+        best = o > best ? o : best;
+    }
+    if (lane == 0) red[wave] = best;
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t prev = atomicAdd(&a.counters[blockIdx.y], 1u);
-        last_lds = prev == gridDim.x - 1;
+        unsigned long long m = red[0];
+        for (int w = 1; w < 4; ++w) m = red[w] > m ? red[w] : m;
+        const int id = (int)(~(uint32_t)(m & 0xFFFFFFFFull));
+        id_lds = id;
+        a.ids[b] = id;
+        if (a.pos) a.pos[b] += 1;
     }
-    __syncthreads();
-    if (!last_lds) return;
-    __threadfence();
-    __shared__ int ids_lds[BT];
-    if (threadIdx.x < nb) {
-        const int b = threadIdx.x;
-        const unsigned long long key =
-            __hip_atomic_load(&a.slots[b0 + b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int id = (int)(~(uint32_t)(key & 0xFFFFFFFFull));
-        ids_lds[b] = id;
-        a.ids[b0 + b] = id;
-        if (a.pos) a.pos[b0 + b] += 1;
-        a.slots[b0 + b] = 0ull;
-    }
-    if (threadIdx.x == 0) a.counters[blockIdx.y] = 0u;
     __syncthreads();
     if (a.next_x) {
-        for (int b = 0; b < nb; ++b) {
-            const int id = ids_lds[b];
-            const bool ok = id >= 0 && id < a.vocab;
-            if (!ok && threadIdx.x == 0) record_error(a.err, 4u);
-            float* xr = a.next_x + (int64_t)(b0 + b) * a.hidden;
-            for (int i = threadIdx.x; i < a.hidden; i += 256) xr[i] = ok ? WT::ld(E, (int64_t)id * a.hidden + i) : 0.f;
-        }
+        const int id = id_lds;
+        const bool ok = id >= 0 && id < a.vocab;
+        if (!ok && threadIdx.x == 0) record_error(a.err, 4u);
+        const T* E = (const T*)a.embed;
+        float* xr = a.next_x + (int64_t)b * a.hidden;
+        for (int i = threadIdx.x; i < a.hidden; i += 256) xr[i] = ok ? WT::ld(E, (int64_t)id * a.hidden + i) : 0.f;
     }
+}
+
+template <class WT, int KCH>
+static void launch_head_k(const HeadArgs& a, dim3 grid, hipStream_t s) {
+    constexpr int NR = 8;
+    if (a.rows == 1) lm_head_kernel<WT, 1, NR, KCH><<<grid, 256, 0, s>>>(a);
+    else if (a.rows == 2) lm_head_kernel<WT, 2, NR, KCH><<<grid, 256, 0, s>>>(a);
+    else {
+        grid.y = (a.rows + 3) / 4;
+        lm_head_kernel<WT, 4, NR, KCH><<<grid, 256, 0, s>>>(a);
+    }
+}
+
+template <class WT>
+static hipError_t launch_head_wt(const HeadArgs& a, hipStream_t s) {
+    constexpr int NR = 8;
+    const int n_blocks = (a.vocab + NR - 1) / NR;
+    const int grid_x = n_blocks < a.max_partials ? n_blocks : a.max_partials;
+    const dim3 grid(grid_x, 1);
+    switch ((a.hidden + 4 * CHUNK - 1) / (4 * CHUNK)) {
+        case 1: launch_head_k<WT, 1>(a, grid, s); break;
+        case 2: launch_head_k<WT, 2>(a, grid, s); break;
+        case 3: launch_head_k<WT, 3>(a, grid, s); break;
+        case 4: launch_head_k<WT, 4>(a, grid, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    lm_head_finalize_kernel<WT><<<a.rows, 256, 0, s>>>(a, grid_x);
+    return hipGetLastError();
 }
 
 hipError_t launch_lm_head_argmax(const HeadArgs& a, WType wt, hipStream_t s) {
     if (a.rows <= 0) return hipSuccess;
-    constexpr int RW = 2;
-    const int waves = (a.vocab + RW - 1) / RW;
-    dim3 grid((waves + 3) / 4, 1);
-#define HEAD_LAUNCH(WT_)                                                    \
-    do {                                                                    \
-        if (a.rows == 1) lm_head_kernel<WT_, 1, RW><<<grid, 256, 0, s>>>(a); \
-        else if (a.rows == 2) lm_head_kernel<WT_, 2, RW><<<grid, 256, 0, s>>>(a); \
-        else {                                                              \
-            grid.y = (a.rows + 3) / 4;                                      \
-            lm_head_kernel<WT_, 4, RW><<<grid, 256, 0, s>>>(a);             \
-        }                                                                   \
-    } while (0)
-    if (wt == W_BF16) HEAD_LAUNCH(BF16);
-    else HEAD_LAUNCH(F32);
-#undef HEAD_LAUNCH
-    return hipGetLastError();
+    return wt == W_BF16 ? launch_head_wt<BF16>(a, s) : launch_head_wt<F32>(a, s);
 }
 
 }  // namespace sttd

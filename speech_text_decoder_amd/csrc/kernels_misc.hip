@@ -1,6 +1,7 @@
 // kernels_misc.hip - RMSNorm rows, per-head Q/K RMSNorm + NeoX RoPE + KV write,
 // token-embedding gather, fills.
 #include "common.h"
+#include "headops.h"
 #include "launch.h"
 
 namespace sttd {
@@ -57,104 +58,28 @@ hipError_t launch_rmsnorm_rows_bf16(const float* x, int64_t ldx, const void* gai
 }
 
 // ------------------------------------------------------------------ Q/K norm + RoPE + KV write
-// One wave per (row, head item); items are the n_heads query heads, then the
-// n_kv key heads, then the n_kv value heads. Lane i < d/2 owns the NeoX pair
-// (i, i + d/2). Query and key heads: RMSNorm over head_dim with the shared
-// gain, then the pair turns by the table angle pos * theta^(-2i/d). Keys and
-// values go to cache row `pos` of the row's slab; values are copied as is.
-// (Qwen3-ASR decoder page, file header; the cache index equals the position:
-// build_step_graph's kv_idx and run() on the model page.)
+// One wave per (row, head item); see qk_head_item.
 template <class GT, class KT>
-__global__ __launch_bounds__(256) void qk_norm_rope_kv_kernel(
-    const float* __restrict__ qkv, int64_t ldqkv, int R, int n_heads, int n_kv, int d,
-    const typename GT::T* __restrict__ qg, const typename GT::T* __restrict__ kg, float eps,
-    const float* __restrict__ rope, int max_pos, RowMap rm, KVLayer kv, void* __restrict__ q_out, bool q_f16,
-    int64_t ldq, uint32_t* err) {
-    const int lane = threadIdx.x % WAVE;
-    const int items = n_heads + 2 * n_kv;
+__global__ __launch_bounds__(256) void qk_norm_rope_kv_kernel(const float* __restrict__ qkv, int64_t ldqkv, int R,
+                                                              QkRope p) {
+    const int items = p.n_heads + 2 * p.n_kv;
     const int item = blockIdx.x * 4 + threadIdx.x / WAVE;
     if (item >= R * items) return;
     const int r = item / items, hi = item % items;
-    const int half = d / 2;
-    const int pos = row_pos(rm, r);
-    const int seq = row_seq(rm, r);
-    if (pos < 0 || pos >= kv.n_ctx || pos >= max_pos) {
-        if (lane == 0) record_error(err, 1u);
-        return;
-    }
-    if (seq < 0 || seq >= kv.n_seq) {
-        if (lane == 0) record_error(err, 2u);
-        return;
-    }
-    const bool act = lane < half;
-    const float* src = qkv + (int64_t)r * ldqkv;
-    int col;
-    if (hi < n_heads) col = hi * d;
-    else if (hi < n_heads + n_kv) col = n_heads * d + (hi - n_heads) * d;
-    else col = n_heads * d + n_kv * d + (hi - n_heads - n_kv) * d;
-    float u0 = act ? src[col + lane] : 0.f;
-    float u1 = act ? src[col + lane + half] : 0.f;
-    if (hi >= n_heads + n_kv) {  // value head: straight copy into the cache
-        const int j = hi - n_heads - n_kv;
-        const int64_t off = ((int64_t)(seq * kv.n_kv + j) * kv.n_ctx + pos) * d;
-        if (act) {
-            KT::st((typename KT::T*)kv.v, off + lane, u0);
-            KT::st((typename KT::T*)kv.v, off + lane + half, u1);
-        }
-        return;
-    }
-    const bool is_q = hi < n_heads;
-    const typename GT::T* g = is_q ? qg : kg;
-    const float ss = wave_sum(u0 * u0 + u1 * u1);
-    const float rs = 1.0f / sqrtf(ss / (float)d + eps);
-    float a = 0.f, b = 0.f, c = 1.f, sn = 0.f;
-    if (act) {
-        a = u0 * rs * GT::ld(g, lane);
-        b = u1 * rs * GT::ld(g, lane + half);
-        const float2 cs = reinterpret_cast<const float2*>(rope)[(int64_t)pos * half + lane];
-        c = cs.x;
-        sn = cs.y;
-    }
-    const float r0 = a * c - b * sn;
-    const float r1 = a * sn + b * c;
-    if (!act) return;
-    if (is_q) {
-        const int64_t off = (int64_t)r * ldq + hi * d;
-        if (q_f16) {
-            F16::st((uint16_t*)q_out, off + lane, r0);
-            F16::st((uint16_t*)q_out, off + lane + half, r1);
-        } else {
-            ((float*)q_out)[off + lane] = r0;
-            ((float*)q_out)[off + lane + half] = r1;
-        }
-    } else {
-        const int j = hi - n_heads;
-        const int64_t off = ((int64_t)(seq * kv.n_kv + j) * kv.n_ctx + pos) * d;
-        KT::st((typename KT::T*)kv.k, off + lane, r0);
-        KT::st((typename KT::T*)kv.k, off + lane + half, r1);
-    }
+    qk_head_item<GT, KT>(qkv + (int64_t)r * ldqkv, r, hi, p);
 }
 
-hipError_t launch_qk_norm_rope_kv(const float* qkv, int64_t ldqkv, int R, int n_heads, int n_kv, int d,
-                                  const void* q_gain, const void* k_gain, WType gt, float eps, const float* rope,
-                                  int max_pos, RowMap rm, KVLayer kv, void* q_out, bool q_f16, int64_t ldq,
-                                  uint32_t* err, hipStream_t s) {
+hipError_t launch_qk_norm_rope_kv(const float* qkv, int64_t ldqkv, int R, WType gt, const QkRope& q, hipStream_t s) {
     if (R <= 0) return hipSuccess;
-    const int items = R * (n_heads + 2 * n_kv);
+    const int items = R * (q.n_heads + 2 * q.n_kv);
     const int grid = (items + 3) / 4;
-#define QK_LAUNCH(GT_, KT_)                                                                                     \
-    qk_norm_rope_kv_kernel<GT_, KT_><<<grid, 256, 0, s>>>(qkv, ldqkv, R, n_heads, n_kv, d,                     \
-                                                          (const typename GT_::T*)q_gain,                     \
-                                                          (const typename GT_::T*)k_gain, eps, rope, max_pos, \
-                                                          rm, kv, q_out, q_f16, ldq, err)
     if (gt == W_BF16) {
-        if (kv.type == KV_F16) QK_LAUNCH(BF16, F16);
-        else QK_LAUNCH(BF16, F32);
+        if (q.kv.type == KV_F16) qk_norm_rope_kv_kernel<BF16, F16><<<grid, 256, 0, s>>>(qkv, ldqkv, R, q);
+        else qk_norm_rope_kv_kernel<BF16, F32><<<grid, 256, 0, s>>>(qkv, ldqkv, R, q);
     } else {
-        if (kv.type == KV_F16) QK_LAUNCH(F32, F16);
-        else QK_LAUNCH(F32, F32);
+        if (q.kv.type == KV_F16) qk_norm_rope_kv_kernel<F32, F16><<<grid, 256, 0, s>>>(qkv, ldqkv, R, q);
+        else qk_norm_rope_kv_kernel<F32, F32><<<grid, 256, 0, s>>>(qkv, ldqkv, R, q);
     }
-#undef QK_LAUNCH
     return hipGetLastError();
 }
 

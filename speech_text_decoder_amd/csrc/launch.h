@@ -29,6 +29,23 @@ struct KVLayer {
     KVType type;
 };
 
+// Everything one (row, head) item of the per-head Q/K RMSNorm + RoPE + KV
+// write needs (qk_head_item in headops.h).
+struct QkRope {
+    const void* q_gain;
+    const void* k_gain;
+    float eps;
+    const float* rope;   // [max_pos][d/2] (cos, sin)
+    int max_pos;
+    RowMap rm;
+    KVLayer kv;
+    void* q_out;         // [rows][n_heads * d], fp32 or f16 (q_f16)
+    bool q_f16;
+    int64_t ldq;
+    uint32_t* err;
+    int n_heads, n_kv, d;
+};
+
 // ---- norms, rotary, gathers (kernels_misc.hip)
 // out[r, :] = x[r, :] / sqrt(mean(x[r]^2) + eps) * gain, rows r < R; out bf16.
 // With out_lo, the value is also split: out = bf16(v), out_lo = bf16(v - out).
@@ -36,10 +53,7 @@ hipError_t launch_rmsnorm_rows_bf16(const float* x, int64_t ldx, const void* gai
                                     uint16_t* out_lo, int64_t ldo, int R, int H, float eps, hipStream_t s);
 // Per-head Q/K RMSNorm + NeoX RoPE (table) + K/V cache write; q written to q_out
 // as fp32 (q_f16 false) or f16 (q_f16 true) with row stride ldq.
-hipError_t launch_qk_norm_rope_kv(const float* qkv, int64_t ldqkv, int R, int n_heads, int n_kv, int d,
-                                  const void* q_gain, const void* k_gain, WType gt, float eps, const float* rope,
-                                  int max_pos, RowMap rm, KVLayer kv, void* q_out, bool q_f16, int64_t ldq,
-                                  uint32_t* err, hipStream_t s);
+hipError_t launch_qk_norm_rope_kv(const float* qkv, int64_t ldqkv, int R, WType gt, const QkRope& q, hipStream_t s);
 hipError_t launch_embed_gather(const void* embed, WType wt, int vocab, int hidden, int B, const int32_t* ids,
                                float* x, uint32_t* err, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
@@ -60,6 +74,13 @@ struct GemvArgs {
     int64_t ldy;
     const float* resid;  // RESID: y = resid + x W^T (may equal y)
     int64_t ldr;
+    // Optional: the activation rows are attention split partials to merge on
+    // load: records [m, l, -, -, o[head_dim]] at ((row * (K / head_dim) + h) *
+    // n_splits + s) * (head_dim + 4); x[row][h * head_dim + e] = sum_s 2^(m_s - M)
+    // o_s[e] / sum_s 2^(m_s - M) l_s.
+    const float* xpart;
+    int n_splits;
+    int head_dim;
 };
 hipError_t launch_gemv(const GemvArgs& a, WType wt, GemvEpi epi, hipStream_t s);
 
@@ -76,8 +97,8 @@ struct HeadArgs {
     float* logits;       // optional [rows, vocab]
     float* next_x;       // optional [rows, hidden]
     int32_t* pos;        // optional, += 1
-    unsigned long long* slots;  // [rows], zero between calls
-    uint32_t* counters;         // [ceil(rows / 4)], zero between calls
+    unsigned long long* partials;  // [rows][max_partials] per-workgroup best keys
+    int max_partials;              // workgroups of the head GEMV (its grid width)
     uint32_t* err;
 };
 hipError_t launch_lm_head_argmax(const HeadArgs& a, WType wt, hipStream_t s);
@@ -107,9 +128,13 @@ hipError_t launch_gemm(const GemmArgs& g, GemmEpi epi, hipStream_t s);
 // ---- attention (kernels_attn.hip)
 // Split-K GQA attention of independent rows (decode, and prefill on f32 caches):
 // row r attends slab rows [0, pos_r] of its head group; partials then combine.
+// With `fuse`, q holds the raw Q|K|V projection rows (one row per slab):
+// the kernel norms and rotates the queries itself and writes the new key and
+// value at each row's position (Q/K norm + RoPE + KV write fused); without
+// it q holds normed, rotated query rows and the cache holds every key.
 hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, RowMap rm, KVLayer kv, int n_splits,
                             float* part, float* out_f32, uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo,
-                            uint32_t* err, hipStream_t s);
+                            uint32_t* err, const QkRope* fuse, WType gt, hipStream_t s);
 // Causal flash attention (MFMA, f16 cache) of T rows of one slab at positions pos0..
 hipError_t launch_attn_prefill(const uint16_t* q16, int64_t ldq, int T, int pos0, int seq, int n_heads, KVLayer kv,
                                uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo, hipStream_t s);
