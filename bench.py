@@ -67,6 +67,10 @@ def kernel_cost(name, sh, rows, mean_keys=0.0):
         return rows * (qkv * 4 + qd * 4 + 2 * kvd * kvb), 0.0
     if name == "lm_head":
         return sh.vocab * H * wb + rows * H * 4, 2.0 * rows * sh.vocab * H
+    if name == "attn_prefill":   # causal: row t attends to t+1 keys; rows = prefill rows
+        return rows * (2 * qd * 4 + 2 * kvd * kvb), 4.0 * qd * rows * (rows + 1) / 2
+    if name == "rmsnorm":
+        return rows * H * (4 + 4) + H * wb, 4.0 * rows * H
     return 0, 0.0
 
 
@@ -91,20 +95,58 @@ def cpu_threads():
     return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
 
 
-def profile_table(binding, sh, rows_of, keys_of, launches_ms=None):
-    """Read the per-kernel event timings; attach algorithmic bytes and rates."""
-    import ctypes
-    L = binding.lib()
-    out = {}
+CLOCK_SLOTS = 1024
+ALL_KERNELS = (1 << len(KERNEL_NAMES)) - 1
+
+
+def clock_accumulate(binding, totals):
     for k, name in enumerate(KERNEL_NAMES):
-        n = ctypes.c_int64()
-        ms = ctypes.c_double()
-        L.sttd_profile_read(k, ctypes.byref(n), ctypes.byref(ms))
-        if n.value == 0:
-            continue
-        avg_us = ms.value * 1e3 / n.value
+        n, us = binding.clock_read(k)
+        if n:
+            t = totals.setdefault(name, [0, 0.0])
+            t[0] += n
+            t[1] += us
+
+
+def clock_profile(binding, torch, stream, eager=None, capture=None, reps=8):
+    """Per-kernel device-clock spans (first workgroup start to last workgroup end).
+
+    eager(): launches run once, eagerly; capture(): launches captured into one HIP
+    graph, which is then replayed `reps` times with the slots re-armed in between.
+    Returns {name: [launches, total_us]}."""
+    totals = {}
+    if eager is not None:
+        binding.clock_enable(ALL_KERNELS, CLOCK_SLOTS)
+        with torch.cuda.stream(stream):
+            eager()
+        torch.cuda.synchronize()
+        binding.clock_disable()
+        clock_accumulate(binding, totals)
+    if capture is not None:
+        binding.clock_enable(ALL_KERNELS, CLOCK_SLOTS)
+        with torch.cuda.stream(stream):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                capture()
+        torch.cuda.synchronize()
+        binding.clock_disable()
+        for _ in range(reps):
+            binding.clock_reset()
+            with torch.cuda.stream(stream):
+                g.replay()
+            torch.cuda.synchronize()
+            clock_accumulate(binding, totals)
+        del g
+    return totals
+
+
+def kernel_table(totals, sh, rows_of, keys_of):
+    """Attach algorithmic bytes/flops per launch and the achieved rates to the clock spans."""
+    out = {}
+    for name, (n, us) in totals.items():
+        avg_us = us / n
         b, f = kernel_cost(name, sh, rows_of(name), keys_of(name))
-        out[name] = {"launches": n.value, "avg_us": round(avg_us, 3), "bytes": int(b),
+        out[name] = {"launches": n, "avg_us": round(avg_us, 3), "bytes": int(b), "flops": f,
                      "gbs": round(b / (avg_us * 1e-6) / 1e9, 1) if b else None,
                      "tflops": round(f / (avg_us * 1e-6) / 1e12, 2) if f else None}
     return out
@@ -119,7 +161,8 @@ def roofline_entry(table, name, bound):
                 "frac": round(e["gbs"] / HBM_PEAK_GBS, 4), "traffic": None, "avg_us": e["avg_us"],
                 "bytes_per_launch": e["bytes"]}
     return {"kernel": name, "bound": "mfma", "achieved": e["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(e["tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": None, "avg_us": e["avg_us"]}
+            "frac": round(e["tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": None, "avg_us": e["avg_us"],
+            "flops_per_launch": e.get("flops")}
 
 
 # ---------------------------------------------------------------- greedy stack (prefill + greedy decode)
@@ -208,20 +251,17 @@ def bench_greedy_stack(args, wl):
                    "n_ctx": wl.n_ctx, "parallelism": "none (1 GPU)"},
     }
     if not args.no_kernel_profile:
-        # per-kernel event timing on one eager job (same kernels, same shapes)
-        binding.lib().sttd_profile_enable((1 << len(KERNEL_NAMES)) - 1)
-        with torch.cuda.stream(stream):
-            prefill_part(stream)
-            for _ in range(min(n_steps, 32)):
-                sess.step(xs, pos, pos_bound=wl.n_ctx)
-                sess.head(xs, ids, next_x=xs, pos=pos)
+        # device-clock spans: the prefill part eagerly, the decode step+head as a replayed graph
+        reps = 16
+        pre = clock_profile(binding, torch, stream, eager=lambda: prefill_part(stream))
+        dec = clock_profile(binding, torch, stream, reps=reps, capture=lambda: (
+            sess.step(xs, pos, pos_bound=wl.n_ctx), sess.head(xs, ids, next_x=xs, pos=pos)))
         torch.cuda.synchronize()
-        binding.lib().sttd_profile_enable(0)
         rows = lambda n: T if n.endswith("gemm") or n in ("rmsnorm", "attn_prefill") else 1
-        keys = lambda n: mean_keys
-        table = profile_table(binding, sh, rows, keys)
-        res["kernels"] = table
-        res["roofline"] = roofline_entry(table, "gateup_gemv", "hbm")
+        res["kernels"] = {"prefill": kernel_table(pre, sh, rows, lambda n: T),
+                          "decode": kernel_table(dec, sh, lambda n: 1, lambda n: T + 1 + reps / 2.0)}
+        res["kernel_timing"] = "device clock (s_memrealtime, 100 MHz): first-workgroup start to last-workgroup end"
+        res["roofline"] = roofline_entry(res["kernels"]["decode"], "gateup_gemv", "hbm")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_greedy(wl, layers, E, g, x_host, new_tokens)
     sess.close()
@@ -335,22 +375,27 @@ def bench_block(args, wl):
                    "parallelism": "none (1 GPU)"},
     }
     if not args.no_kernel_profile:
-        binding.lib().sttd_profile_enable((1 << len(KERNEL_NAMES)) - 1)
-        with torch.cuda.stream(stream):
+        n_prof = min(n_steps, 16)
+
+        def pre_eager():
             x.copy_(x0)
             rows.copy_(r0)
             sess.prefill(x)
-            for k in range(min(n_steps, 16)):
+
+        def dec_capture():
+            for k in range(n_prof):
                 sess.step(rows[k:k + 1], pos_all[k], pos_bound=T + k + 1)
-        torch.cuda.synchronize()
-        binding.lib().sttd_profile_enable(0)
+
+        pre = clock_profile(binding, torch, stream, eager=pre_eager)
+        dec = clock_profile(binding, torch, stream, capture=dec_capture, reps=4)
         rw = lambda n: T if n.endswith("gemm") or n in ("rmsnorm", "attn_prefill") else 1
-        table = profile_table(binding, sh, rw, lambda n: mean_keys)
-        res["kernels"] = table
+        res["kernels"] = {"prefill": kernel_table(pre, sh, rw, lambda n: T),
+                          "decode": kernel_table(dec, sh, lambda n: 1, lambda n: T + (n_prof + 1) / 2.0)}
+        res["kernel_timing"] = "device clock (s_memrealtime, 100 MHz): first-workgroup start to last-workgroup end"
         if T >= 1024 and sh.wdtype == "bf16":
-            res["roofline"] = roofline_entry(table, "gateup_gemm", "mfma")
+            res["roofline"] = roofline_entry(res["kernels"]["prefill"], "gateup_gemm", "mfma")
         else:
-            res["roofline"] = roofline_entry(table, "gateup_gemv", "hbm")
+            res["roofline"] = roofline_entry(res["kernels"]["decode"], "gateup_gemv", "hbm")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_block(wl, layers[0], x_host, rows_host)
     sess.close()
@@ -446,17 +491,15 @@ def bench_batched(args, wl):
                    "kv_dtype": sh.kvdtype, "parallelism": "none (1 GPU)"},
     }
     if not args.no_kernel_profile:
-        binding.lib().sttd_profile_enable((1 << len(KERNEL_NAMES)) - 1)
         with torch.cuda.stream(stream):
             x.copy_(x0)
             pos.copy_(pos0)
-            for _ in range(4):
-                sess.step(x, pos, pos_bound=bound)
-                sess.head(x, ids, next_x=x, pos=pos)
-        torch.cuda.synchronize()
-        binding.lib().sttd_profile_enable(0)
-        table = profile_table(binding, sh, lambda n: Bn, lambda n: mean_keys)
-        res["kernels"] = table
+        reps = 8
+        dec = clock_profile(binding, torch, stream, reps=reps, capture=lambda: (
+            sess.step(x, pos, pos_bound=bound), sess.head(x, ids, next_x=x, pos=pos)))
+        table = kernel_table(dec, sh, lambda n: Bn, lambda n: float(lens.mean()) + (reps + 1) / 2.0)
+        res["kernels"] = {"decode": table}
+        res["kernel_timing"] = "device clock (s_memrealtime, 100 MHz): first-workgroup start to last-workgroup end"
         res["roofline"] = roofline_entry(table, "gateup_gemm" if "gateup_gemm" in table else "gateup_gemv", "hbm")
     sess.close()
     return res

@@ -203,6 +203,27 @@ typedef enum {
 sttd_status sttd_profile_enable(uint32_t mask);
 sttd_status sttd_profile_read(int kernel, int64_t *launches /* host */, double *total_ms /* host */);
 
+/* Device-clock timing, usable inside HIP graphs: while enabled, each launch
+ * of a family in `mask` takes the next of max_launches device slots (256 KiB
+ * each); thread 0 of every workgroup records its start and end on the 100 MHz
+ * device clock (s_memrealtime), and a slot's span runs from the first start to
+ * the last end (workgroups beyond the first 12288 of a launch go unrecorded).
+ * A captured graph keeps its slots: sttd_clock_reset re-arms the slots handed
+ * out so far (call it between replays, outside any capture), and
+ * sttd_clock_read sums the spans of one family (microseconds) over the slots
+ * stamped since. Enabling with more slots than before reallocates them, which
+ * invalidates graphs captured with the old ones. enable/reset/read synchronise
+ * the device. */
+sttd_status sttd_clock_enable(uint32_t mask, int max_launches);
+sttd_status sttd_clock_disable(void);
+sttd_status sttd_clock_reset(void);
+sttd_status sttd_clock_read(int kernel, int64_t *launches /* host */, double *total_us /* host */);
+/* The raw slots in launch order (a timeline): kinds[i] is the family of slot i,
+ * start_end[2i], start_end[2i+1] its first start and last end in 100 MHz ticks
+ * (~0 and 0 when the launch has not run since the last reset). Copies at most
+ * `max` slots; *n receives the number copied. Host buffers. */
+sttd_status sttd_clock_spans(int max, int *kinds, uint64_t *start_end, int *n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,8 @@ DEVERR_POSITION, DEVERR_SLAB, DEVERR_TOKEN = 1, 2, 4
 EXPORTS = [
     "sttd_status_string", "sttd_kv_cache_alloc", "sttd_kv_cache_free", "sttd_kv_cache_clear", "sttd_kv_cache_view",
     "sttd_workspace_alloc", "sttd_workspace_free", "sttd_workspace_error", "sttd_embed_gather",
-    "sttd_block_prefill", "sttd_block_step", "sttd_lm_head_argmax",
+    "sttd_block_prefill", "sttd_block_step", "sttd_lm_head_argmax", "sttd_profile_enable", "sttd_profile_read",
+    "sttd_clock_enable", "sttd_clock_disable", "sttd_clock_reset", "sttd_clock_read", "sttd_clock_spans",
 ]
 
 
@@ -69,6 +70,13 @@ def lib():
                                    vp],
             "sttd_block_step": [P(BlockParams), P(BlockWeights), vp, vp, i32, i32, vp, vp, i32, vp, vp],
             "sttd_lm_head_argmax": [vp, vp, i32, i32, i32, f32, vp, i32, vp, i64, vp, vp, vp, vp, vp],
+            "sttd_profile_enable": [ctypes.c_uint32],
+            "sttd_profile_read": [i32, P(i64), P(ctypes.c_double)],
+            "sttd_clock_enable": [ctypes.c_uint32, i32],
+            "sttd_clock_disable": [],
+            "sttd_clock_reset": [],
+            "sttd_clock_read": [i32, P(i64), P(ctypes.c_double)],
+            "sttd_clock_spans": [i32, P(i32), P(ctypes.c_uint64), P(i32)],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -148,6 +156,43 @@ def block_prefill(params, weights, ws, kv, layer, seq, pos0, T, x, flags=0, stre
 def block_step(params, weights, ws, kv, layer, B, seq, pos, pos_bound, x, stream=0):
     _check(lib().sttd_block_step(ctypes.byref(params), ctypes.byref(weights), ws, kv, layer, B, seq, pos, pos_bound,
                                  x, stream), "sttd_block_step")
+
+
+def profile_enable(mask):
+    _check(lib().sttd_profile_enable(mask), "sttd_profile_enable")
+
+
+def profile_read(kernel):
+    n, ms = ctypes.c_int64(), ctypes.c_double()
+    _check(lib().sttd_profile_read(kernel, ctypes.byref(n), ctypes.byref(ms)), "sttd_profile_read")
+    return n.value, ms.value
+
+
+def clock_enable(mask, max_launches):
+    _check(lib().sttd_clock_enable(mask, max_launches), "sttd_clock_enable")
+
+
+def clock_disable():
+    _check(lib().sttd_clock_disable(), "sttd_clock_disable")
+
+
+def clock_reset():
+    _check(lib().sttd_clock_reset(), "sttd_clock_reset")
+
+
+def clock_read(kernel):
+    n, us = ctypes.c_int64(), ctypes.c_double()
+    _check(lib().sttd_clock_read(kernel, ctypes.byref(n), ctypes.byref(us)), "sttd_clock_read")
+    return n.value, us.value
+
+
+def clock_spans(max_slots):
+    """[(kind, start_tick, end_tick)] of the slots handed out, in launch order."""
+    kinds = (ctypes.c_int * max_slots)()
+    se = (ctypes.c_uint64 * (2 * max_slots))()
+    n = ctypes.c_int()
+    _check(lib().sttd_clock_spans(max_slots, kinds, se, ctypes.byref(n)), "sttd_clock_spans")
+    return [(kinds[i], se[2 * i], se[2 * i + 1]) for i in range(n.value)]
 
 
 def lm_head_argmax(final_norm, embed, wtype, vocab, hidden, rms_eps, ws, B, x, x_row_stride, ids, logits=0,

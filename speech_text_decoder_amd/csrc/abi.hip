@@ -13,6 +13,7 @@
 
 using namespace sttd;
 
+
 struct sttd_kv_cache {
     int n_layers, n_seq, n_ctx, n_kv, d;
     sttd_dtype type;
@@ -60,10 +61,46 @@ struct Profiler {
 };
 Profiler g_prof;
 
-// Brackets the launches of one kernel family with an event pair when timing is on.
+// Device-clock timing: one slot of kClockEntries (start, end) pairs per timed launch.
+struct ClockProf {
+    std::mutex mu;
+    uint32_t mask = 0;
+    uint64_t* slots = nullptr;  // device [cap][kClockEntries][2]
+    uint64_t* red = nullptr;    // device [cap][2]: reduced spans
+    int cap = 0, used = 0;
+    std::vector<int> kinds;     // kernel family of each used slot
+    uint64_t* current = nullptr;
+};
+ClockProf g_clk;
+
+constexpr size_t kClockSlotBytes = (size_t)kClockEntries * 2 * sizeof(uint64_t);
+
+hipError_t clock_fill(int n) {
+    return n ? hipMemset(g_clk.slots, 0, kClockSlotBytes * (size_t)n) : hipSuccess;
+}
+
+// Reduced (start, end) of the used slots into h (host, 2 * used).
+hipError_t clock_collect(std::vector<uint64_t>& h) {
+    h.assign(2 * (size_t)g_clk.used, 0);
+    if (!g_clk.used) return hipSuccess;
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = launch_clock_reduce(g_clk.slots, g_clk.used, g_clk.red, nullptr);
+    if (e == hipSuccess) e = hipMemcpy(h.data(), g_clk.red, h.size() * sizeof(uint64_t), hipMemcpyDeviceToHost);
+    return e;
+}
+
+// Times the launches of one kernel family: event pairs (eager launches) and/or
+// a device-clock slot (eager or captured launches), as enabled.
 class ProfScope {
   public:
     ProfScope(int kind, hipStream_t s) : kind_(kind), s_(s) {
+        if (g_clk.mask & (1u << kind)) {
+            std::lock_guard<std::mutex> lk(g_clk.mu);
+            if (g_clk.used < g_clk.cap) {
+                g_clk.current = g_clk.slots + (size_t)kClockEntries * 2 * (size_t)g_clk.used++;
+                g_clk.kinds.push_back(kind);
+            }
+        }
         if (!(g_prof.mask & (1u << kind))) return;
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
@@ -73,6 +110,7 @@ class ProfScope {
         if (b_ && e_ && hipEventRecord(b_, s) != hipSuccess) b_ = nullptr;
     }
     ~ProfScope() {
+        g_clk.current = nullptr;
         if (!b_ || !e_) return;
         if (hipEventRecord(e_, s_) != hipSuccess) return;
         std::lock_guard<std::mutex> lk(g_prof.mu);
@@ -279,6 +317,8 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
 }
 
 }  // namespace
+
+uint64_t* sttd::clock_slot() { return g_clk.current; }
 
 extern "C" {
 
@@ -507,6 +547,75 @@ sttd_status sttd_lm_head_argmax(const void* final_norm, const void* embed, sttd_
 sttd_status sttd_profile_enable(uint32_t mask) {
     std::lock_guard<std::mutex> lk(g_prof.mu);
     g_prof.mask = mask & ((1u << STTD_KERN_COUNT) - 1);
+    return STTD_OK;
+}
+
+sttd_status sttd_clock_enable(uint32_t mask, int max_launches) {
+    if (max_launches < 0) return STTD_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lk(g_clk.mu);
+    if (max_launches > g_clk.cap) {
+        if (g_clk.slots) (void)hipFree(g_clk.slots);
+        if (g_clk.red) (void)hipFree(g_clk.red);
+        g_clk.slots = g_clk.red = nullptr;
+        g_clk.cap = 0;
+        if (hipMalloc(&g_clk.slots, kClockSlotBytes * (size_t)max_launches) != hipSuccess ||
+            hipMalloc(&g_clk.red, 2 * sizeof(uint64_t) * (size_t)max_launches) != hipSuccess) {
+            (void)hipGetLastError();
+            if (g_clk.slots) (void)hipFree(g_clk.slots);
+            g_clk.slots = nullptr;
+            return STTD_ERR_OOM;
+        }
+        g_clk.cap = max_launches;
+    }
+    g_clk.used = 0;
+    g_clk.kinds.clear();
+    TRY(clock_fill(g_clk.cap));
+    g_clk.mask = mask & ((1u << STTD_KERN_COUNT) - 1);
+    return STTD_OK;
+}
+
+sttd_status sttd_clock_disable(void) {
+    std::lock_guard<std::mutex> lk(g_clk.mu);
+    g_clk.mask = 0;
+    return STTD_OK;
+}
+
+sttd_status sttd_clock_reset(void) {
+    std::lock_guard<std::mutex> lk(g_clk.mu);
+    TRY(hipDeviceSynchronize());
+    TRY(clock_fill(g_clk.used));
+    return STTD_OK;
+}
+
+sttd_status sttd_clock_read(int kernel, int64_t* launches, double* total_us) {
+    if (kernel < 0 || kernel >= STTD_KERN_COUNT || !launches || !total_us) return STTD_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lk(g_clk.mu);
+    std::vector<uint64_t> h;
+    TRY(clock_collect(h));
+    int64_t n = 0;
+    double us = 0.0;
+    for (int i = 0; i < g_clk.used; ++i) {
+        if (g_clk.kinds[i] != kernel || h[2 * i] == ~0ull || h[2 * i + 1] < h[2 * i]) continue;
+        ++n;
+        us += (double)(h[2 * i + 1] - h[2 * i]) * 0.01;  // 100 MHz clock
+    }
+    *launches = n;
+    *total_us = us;
+    return STTD_OK;
+}
+
+sttd_status sttd_clock_spans(int max, int* kinds, uint64_t* start_end, int* n) {
+    if (max < 0 || !n || (max > 0 && (!kinds || !start_end))) return STTD_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lk(g_clk.mu);
+    std::vector<uint64_t> h;
+    TRY(clock_collect(h));
+    const int m = max < g_clk.used ? max : g_clk.used;
+    for (int i = 0; i < m; ++i) {
+        kinds[i] = g_clk.kinds[i];
+        start_end[2 * i] = h[2 * i];
+        start_end[2 * i + 1] = h[2 * i + 1];
+    }
+    *n = m;
     return STTD_OK;
 }
 

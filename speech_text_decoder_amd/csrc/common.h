@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -139,6 +141,33 @@ __device__ __forceinline__ uint32_t float_order_key(float f) {
     if (f != f) return 0u;
     uint32_t u = __float_as_uint(f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ------------------------------------------------------------ device clock stamps
+// Kernel timing that also works inside HIP graphs. A timed launch gets a slot
+// of kClockEntries (start, end) pairs; thread 0 of each workgroup stores its
+// start and end ticks of the 100 MHz device clock (s_memrealtime) in the pair
+// of its linear workgroup id, with plain stores: same-address atomics from
+// thousands of workgroups would serialise and slow the kernel being timed.
+// Bank 0 holds ids below kClockBank1; bank 1 (a second kernel launched under
+// the same slot, e.g. a finishing pass) holds the rest. Ids beyond a bank's
+// size are not recorded.
+__device__ __forceinline__ uint64_t* clock_entry(uint64_t* slot, int bank) {
+    const uint32_t id = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const uint32_t cap = bank ? (uint32_t)(sttd::kClockEntries - sttd::kClockBank1) : (uint32_t)sttd::kClockBank1;
+    return id < cap ? slot + 2 * (size_t)((bank ? sttd::kClockBank1 : 0) + id) : nullptr;
+}
+__device__ __forceinline__ void clock_begin(uint64_t* slot, int bank = 0) {
+    if (slot && threadIdx.x == 0) {
+        uint64_t* e = clock_entry(slot, bank);
+        if (e) e[0] = wall_clock64();
+    }
+}
+__device__ __forceinline__ void clock_end(uint64_t* slot, int bank = 0) {
+    if (slot && threadIdx.x == 0) {
+        uint64_t* e = clock_entry(slot, bank);
+        if (e) e[1] = wall_clock64();
+    }
 }
 
 // ------------------------------------------------------------ device error word

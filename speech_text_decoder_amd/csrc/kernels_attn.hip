@@ -49,6 +49,7 @@ struct RowsArgs {
     float eps;
     const float* rope;
     int max_pos;
+    uint64_t* clk;
 };
 
 // One head vector of D values: RMSNorm with `gain`, NeoX rotation at `pos`,
@@ -120,6 +121,7 @@ __global__ __launch_bounds__(NW * 64) void attn_rows_kernel(RowsArgs a) {
     __shared__ float wm_lds[SLOTS][G], wl_lds[SLOTS][G];
     __shared__ float wo_lds[SLOTS][G][D];
 
+    clock_begin(a.clk);
     const int r = blockIdx.x, j = blockIdx.y, split = blockIdx.z;
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
     const int grp = tid / LPK, sub = tid % LPK;
@@ -339,6 +341,7 @@ __global__ __launch_bounds__(NW * 64) void attn_rows_kernel(RowsArgs a) {
             pp[4 + e] = O;
         }
     }
+    clock_end(a.clk);
 }
 
 // Merge the splits of each (row, query head): o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
@@ -346,7 +349,8 @@ __global__ __launch_bounds__(NW * 64) void attn_rows_kernel(RowsArgs a) {
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict__ part, int n_heads, int n_splits,
                                                          float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16,
-                                                         uint16_t* __restrict__ out_lo, int64_t ldo) {
+                                                         uint16_t* __restrict__ out_lo, int64_t ldo, uint64_t* clk) {
+    clock_begin(clk, 1);
     const int r = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
     const float* pp = part + ((int64_t)r * n_heads + h) * n_splits * (D + 4);
     float M = -INFINITY;
@@ -371,6 +375,7 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
         out_bf16[idx] = hi;
         if (out_lo) out_lo[idx] = lo;
     }
+    clock_end(clk, 1);
 }
 
 template <class KT, class GT, int D, bool FUSE>
@@ -392,7 +397,7 @@ static hipError_t rows_dispatch(const RowsArgs& a, int R, hipStream_t s) {
 #undef ROWS_LAUNCH
     if (a.n_splits > 1 && (a.out_f32 || a.out_bf16))
         attn_combine_kernel<D><<<dim3(R, a.n_heads), D, 0, s>>>(a.part, a.n_heads, a.n_splits, a.out_f32, a.out_bf16,
-                                                                a.out_lo, a.ldo);
+                                                                a.out_lo, a.ldo, a.clk);
     return hipGetLastError();
 }
 
@@ -413,6 +418,7 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
     RowsArgs a{};
     a.q = q; a.ldq = ldq; a.n_heads = n_heads; a.rm = rm; a.kv = kv; a.n_splits = n_splits; a.part = part;
     a.out_f32 = out_f32; a.out_bf16 = out_bf16; a.out_lo = out_bf16_lo; a.ldo = ldo; a.err = err;
+    a.clk = clock_slot();
     if (fuse) {
         a.q_gain = fuse->q_gain; a.k_gain = fuse->k_gain; a.eps = fuse->eps; a.rope = fuse->rope;
         a.max_pos = fuse->max_pos;
@@ -434,7 +440,8 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __restrict__ q16, int64_t ldq, int T,
                                                            int pos0, int seq, int n_heads, KVLayer kv,
                                                            uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo,
-                                                           int64_t ldo) {
+                                                           int64_t ldo, uint64_t* clk) {
+    clock_begin(clk);
     constexpr int KB = 64;                 // keys per block
     constexpr int KS = D + 8;              // K row stride in LDS (f16)
     constexpr int VS = KB + 8;             // V^T row stride in LDS
@@ -575,6 +582,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
             if (out_lo) out_lo[idx] = lo;
         }
     }
+    clock_end(clk);
 }
 
 hipError_t launch_attn_prefill(const uint16_t* q16, int64_t ldq, int T, int pos0, int seq, int n_heads, KVLayer kv,
@@ -582,9 +590,9 @@ hipError_t launch_attn_prefill(const uint16_t* q16, int64_t ldq, int T, int pos0
     if (T <= 0) return hipSuccess;
     dim3 grid((T + 63) / 64, n_heads);
     if (kv.d == 128)
-        attn_prefill_kernel<128><<<grid, 256, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo);
+        attn_prefill_kernel<128><<<grid, 256, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, clock_slot());
     else if (kv.d == 64)
-        attn_prefill_kernel<64><<<grid, 256, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo);
+        attn_prefill_kernel<64><<<grid, 256, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, clock_slot());
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

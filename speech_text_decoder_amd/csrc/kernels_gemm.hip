@@ -51,6 +51,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) uint16_t Als[SPLIT ? BM * LDS_STRIDE : 8];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDS_STRIDE];
 
+    clock_begin(g.clk);
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
     const int wm = wave / 2, wn = wave % 2;
     const int m0 = blockIdx.y * BM;
@@ -182,6 +183,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
             }
         }
     }
+    clock_end(g.clk);
 }
 
 template <bool SPLIT>
@@ -193,8 +195,10 @@ static void launch_gemm_t(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     else gemm_bf16_kernel<BM, BN, GEMM_STORE, SPLIT><<<grid, 256, 0, s>>>(g);
 }
 
-hipError_t launch_gemm(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
-    if (g.M <= 0) return hipSuccess;
+hipError_t launch_gemm(const GemmArgs& args, GemmEpi epi, hipStream_t s) {
+    if (args.M <= 0) return hipSuccess;
+    GemmArgs g = args;
+    g.clk = clock_slot();
     if (g.A_lo) launch_gemm_t<true>(g, epi, s);
     else launch_gemm_t<false>(g, epi, s);
     return hipGetLastError();

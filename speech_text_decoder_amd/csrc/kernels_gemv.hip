@@ -237,6 +237,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     constexpr int V = NR * BT;
     __shared__ float red[4][V + BT];
     __shared__ float vals[V];
+    clock_begin(a.clk);
     const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE, t = threadIdx.x;
     const int b0 = blockIdx.y * BT;
     const int nb = min(BT, a.rows - b0);
@@ -301,6 +302,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
                 a.y[(int64_t)(b0 + b) * a.ldy + n0 + r] = gt / (1.0f + expf(-gt)) * up;
             }
         }
+        clock_end(a.clk);
         return;
     }
     if (t < V) {
@@ -312,6 +314,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
             a.y[row * a.ldy + n0 + r] = v;
         }
     }
+    clock_end(a.clk);
 }
 
 template <class WT, int EPI, int NR, int KCH, bool NORM, bool XPART>
@@ -356,8 +359,10 @@ static hipError_t launch_wt(const GemvArgs& a, GemvEpi epi, hipStream_t s) {
     return norm ? launch_k<WT, GEMV_STORE, 4, true>(a, s) : launch_k<WT, GEMV_STORE, 4, false>(a, s);
 }
 
-hipError_t launch_gemv(const GemvArgs& a, WType wt, GemvEpi epi, hipStream_t s) {
-    if (a.rows <= 0 || a.N <= 0) return hipSuccess;
+hipError_t launch_gemv(const GemvArgs& args, WType wt, GemvEpi epi, hipStream_t s) {
+    if (args.rows <= 0 || args.N <= 0) return hipSuccess;
+    GemvArgs a = args;
+    a.clk = clock_slot();
     return wt == W_BF16 ? launch_wt<BF16>(a, epi, s) : launch_wt<F32>(a, epi, s);
 }
 
@@ -378,6 +383,7 @@ __global__ __launch_bounds__(256) void lm_head_kernel(HeadArgs a) {
     constexpr int V = NR * BT;
     __shared__ float red[4][V + BT];
     __shared__ unsigned long long keys[V];
+    clock_begin(a.clk);
     const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE, t = threadIdx.x;
     const int b0 = blockIdx.y * BT;
     const int nb = min(BT, a.rows - b0);
@@ -448,6 +454,7 @@ __global__ __launch_bounds__(256) void lm_head_kernel(HeadArgs a) {
             for (int r = 0; r < NR; ++r) wc[c][r] = wn[c][r];
     }
     if (t < nb) a.partials[(int64_t)(b0 + t) * gridDim.x + blockIdx.x] = best;
+    clock_end(a.clk);
 }
 
 // One workgroup per activation row: reduce the partial keys, emit the id.
@@ -456,6 +463,7 @@ __global__ __launch_bounds__(256) void lm_head_finalize_kernel(HeadArgs a, int n
     typedef typename WT::T T;
     __shared__ unsigned long long red[4];
     __shared__ int id_lds;
+    clock_begin(a.clk, 1);
     const int b = blockIdx.x;
     const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE;
     unsigned long long best = 0ull;
@@ -487,6 +495,7 @@ __global__ __launch_bounds__(256) void lm_head_finalize_kernel(HeadArgs a, int n
         float* xr = a.next_x + (int64_t)b * a.hidden;
         for (int i = threadIdx.x; i < a.hidden; i += 256) xr[i] = ok ? WT::ld(E, (int64_t)id * a.hidden + i) : 0.f;
     }
+    clock_end(a.clk, 1);
 }
 
 template <class WT, int KCH>
@@ -517,8 +526,10 @@ static hipError_t launch_head_wt(const HeadArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_lm_head_argmax(const HeadArgs& a, WType wt, hipStream_t s) {
-    if (a.rows <= 0) return hipSuccess;
+hipError_t launch_lm_head_argmax(const HeadArgs& args, WType wt, hipStream_t s) {
+    if (args.rows <= 0) return hipSuccess;
+    HeadArgs a = args;
+    a.clk = clock_slot();
     return wt == W_BF16 ? launch_head_wt<BF16>(a, s) : launch_head_wt<F32>(a, s);
 }
 

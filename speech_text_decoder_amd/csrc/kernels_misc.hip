@@ -15,8 +15,9 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_bf16_kernel(const float* __r
                                                                 const typename GT::T* __restrict__ g,
                                                                 uint16_t* __restrict__ out,
                                                                 uint16_t* __restrict__ out_lo, int64_t ldo, int H,
-                                                                float eps) {
+                                                                float eps, uint64_t* clk) {
     __shared__ float red[4];
+    clock_begin(clk);
     const float* xr = x + (int64_t)blockIdx.x * ldx;
     uint16_t* o = out + (int64_t)blockIdx.x * ldo;
     float ss = 0.f;
@@ -45,15 +46,16 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_bf16_kernel(const float* __r
             *reinterpret_cast<uint2*>(out_lo + (int64_t)blockIdx.x * ldo + i) = pk;
         }
     }
+    clock_end(clk);
 }
 
 hipError_t launch_rmsnorm_rows_bf16(const float* x, int64_t ldx, const void* gain, WType gt, uint16_t* out,
                                     uint16_t* out_lo, int64_t ldo, int R, int H, float eps, hipStream_t s) {
     if (R <= 0) return hipSuccess;
     if (gt == W_BF16)
-        rmsnorm_rows_bf16_kernel<BF16><<<R, 256, 0, s>>>(x, ldx, (const uint16_t*)gain, out, out_lo, ldo, H, eps);
+        rmsnorm_rows_bf16_kernel<BF16><<<R, 256, 0, s>>>(x, ldx, (const uint16_t*)gain, out, out_lo, ldo, H, eps, clock_slot());
     else
-        rmsnorm_rows_bf16_kernel<F32><<<R, 256, 0, s>>>(x, ldx, (const float*)gain, out, out_lo, ldo, H, eps);
+        rmsnorm_rows_bf16_kernel<F32><<<R, 256, 0, s>>>(x, ldx, (const float*)gain, out, out_lo, ldo, H, eps, clock_slot());
     return hipGetLastError();
 }
 
@@ -62,15 +64,17 @@ hipError_t launch_rmsnorm_rows_bf16(const float* x, int64_t ldx, const void* gai
 template <class GT, class KT>
 __global__ __launch_bounds__(256) void qk_norm_rope_kv_kernel(const float* __restrict__ qkv, int64_t ldqkv, int R,
                                                               QkRope p) {
+    clock_begin(p.clk);
     const int items = p.n_heads + 2 * p.n_kv;
     const int item = blockIdx.x * 4 + threadIdx.x / WAVE;
-    if (item >= R * items) return;
-    const int r = item / items, hi = item % items;
-    qk_head_item<GT, KT>(qkv + (int64_t)r * ldqkv, r, hi, p);
+    if (item < R * items) qk_head_item<GT, KT>(qkv + (int64_t)(item / items) * ldqkv, item / items, item % items, p);
+    clock_end(p.clk);
 }
 
-hipError_t launch_qk_norm_rope_kv(const float* qkv, int64_t ldqkv, int R, WType gt, const QkRope& q, hipStream_t s) {
+hipError_t launch_qk_norm_rope_kv(const float* qkv, int64_t ldqkv, int R, WType gt, const QkRope& qr, hipStream_t s) {
     if (R <= 0) return hipSuccess;
+    QkRope q = qr;
+    q.clk = clock_slot();
     const int items = R * (q.n_heads + 2 * q.n_kv);
     const int grid = (items + 3) / 4;
     if (gt == W_BF16) {
@@ -123,6 +127,45 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
     if (grid > 8192) grid = 8192;
     if (grid == 0) grid = 1;
     fill_zero_kernel<<<(unsigned)grid, 256, 0, s>>>((uint4*)p, n16, (uint8_t*)p + n16 * 16, bytes - n16 * 16);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ clock slot reduction
+// One workgroup per slot: first start (min over recorded starts) and last end.
+__global__ __launch_bounds__(256) void clock_reduce_kernel(const uint64_t* __restrict__ slots,
+                                                           uint64_t* __restrict__ out) {
+    __shared__ uint64_t lo_s[4], hi_s[4];
+    const uint64_t* e = slots + (size_t)blockIdx.x * kClockEntries * 2;
+    uint64_t lo = ~0ull, hi = 0ull;
+    for (int i = threadIdx.x; i < kClockEntries; i += 256) {
+        const uint64_t a = e[2 * i], b = e[2 * i + 1];
+        if (a && a < lo) lo = a;
+        if (b > hi) hi = b;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint64_t a = __shfl_xor(lo, off, WAVE), b = __shfl_xor(hi, off, WAVE);
+        lo = a < lo ? a : lo;
+        hi = b > hi ? b : hi;
+    }
+    if (threadIdx.x % WAVE == 0) {
+        lo_s[threadIdx.x / WAVE] = lo;
+        hi_s[threadIdx.x / WAVE] = hi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 4; ++w) {
+            lo = lo_s[w] < lo ? lo_s[w] : lo;
+            hi = hi_s[w] > hi ? hi_s[w] : hi;
+        }
+        out[2 * blockIdx.x] = lo;
+        out[2 * blockIdx.x + 1] = hi;
+    }
+}
+
+hipError_t launch_clock_reduce(const uint64_t* slots, int n, uint64_t* out, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    clock_reduce_kernel<<<n, 256, 0, s>>>(slots, out);
     return hipGetLastError();
 }
 

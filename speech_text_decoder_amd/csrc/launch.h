@@ -6,6 +6,17 @@
 
 namespace sttd {
 
+// Device-clock slot: kClockEntries (start, end) pairs, one per workgroup id;
+// ids from kClockBank1 up belong to a second kernel launched under the slot.
+constexpr int kClockEntries = 16384;
+constexpr int kClockBank1 = 12288;
+
+// Clock slot of the launch being issued when device-clock timing is on, else
+// nullptr (kClockEntries (start, end) pairs, see common.h).
+uint64_t* clock_slot();
+// out[2i], out[2i+1] = first start and last end recorded in slot i (~0, 0 if none).
+hipError_t launch_clock_reduce(const uint64_t* slots, int n, uint64_t* out, hipStream_t s);
+
 enum WType { W_F32 = 0, W_BF16 = 1 };
 enum KVType { KV_F32 = 0, KV_F16 = 2 };
 
@@ -44,6 +55,7 @@ struct QkRope {
     int64_t ldq;
     uint32_t* err;
     int n_heads, n_kv, d;
+    uint64_t* clk;
 };
 
 // ---- norms, rotary, gathers (kernels_misc.hip)
@@ -81,6 +93,7 @@ struct GemvArgs {
     const float* xpart;
     int n_splits;
     int head_dim;
+    uint64_t* clk;
 };
 hipError_t launch_gemv(const GemvArgs& a, WType wt, GemvEpi epi, hipStream_t s);
 
@@ -100,6 +113,7 @@ struct HeadArgs {
     unsigned long long* partials;  // [rows][max_partials] per-workgroup best keys
     int max_partials;              // workgroups of the head GEMV (its grid width)
     uint32_t* err;
+    uint64_t* clk;
 };
 hipError_t launch_lm_head_argmax(const HeadArgs& a, WType wt, hipStream_t s);
 
@@ -122,6 +136,7 @@ struct GemmArgs {
     uint16_t* Cb;        // SWIGLU output (bf16, ldcb)
     uint16_t* Cb_lo;     // optional low half of the SWIGLU output
     int64_t ldcb;
+    uint64_t* clk;
 };
 hipError_t launch_gemm(const GemmArgs& g, GemmEpi epi, hipStream_t s);
 
