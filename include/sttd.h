@@ -64,7 +64,9 @@ typedef enum {
 typedef enum { STTD_F32 = 0, STTD_BF16 = 1, STTD_F16 = 2 } sttd_dtype;
 
 /* Block shape (to_block_params on the decoder page). head_dim must be 64 or
- * 128; n_heads a multiple of n_kv_heads; hidden and ffn multiples of 128. */
+ * 128; n_heads / n_kv_heads one of 1, 2, 4, 8; hidden and ffn multiples of
+ * 64; hidden, ffn and n_heads * head_dim at most 8192 (else
+ * STTD_ERR_UNSUPPORTED). */
 typedef struct {
     int32_t hidden, n_heads, n_kv_heads, head_dim, ffn;
     float rms_eps;    /* RMSNorm epsilon, inside the square root */

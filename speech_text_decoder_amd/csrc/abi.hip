@@ -151,6 +151,8 @@ bool params_ok(const sttd_block_params* p) {
 sttd_status params_supported(const sttd_block_params* p) {
     if (p->head_dim != 64 && p->head_dim != 128) return STTD_ERR_UNSUPPORTED;
     if (p->hidden % 64 || p->ffn % 64) return STTD_ERR_UNSUPPORTED;
+    // the decode GEMVs keep a whole input row in registers: K <= 8192
+    if (p->hidden > 8192 || p->ffn > 8192 || p->n_heads * p->head_dim > 8192) return STTD_ERR_UNSUPPORTED;
     const int g = p->n_heads / p->n_kv_heads;
     if (g != 1 && g != 2 && g != 4 && g != 8) return STTD_ERR_UNSUPPORTED;
     if (p->wtype != STTD_BF16 && p->wtype != STTD_F32) return STTD_ERR_UNSUPPORTED;
@@ -533,7 +535,7 @@ sttd_status sttd_lm_head_argmax(const void* final_norm, const void* embed, sttd_
                                 int32_t* ids, float* logits, float* next_x, int32_t* pos, void* stream) {
     if (!final_norm || !embed || !ws || !x || !ids || vocab <= 0 || hidden <= 0 || B <= 0) return STTD_ERR_INVALID_ARG;
     if (wtype != STTD_BF16 && wtype != STTD_F32) return STTD_ERR_UNSUPPORTED;
-    if (hidden % 64) return STTD_ERR_UNSUPPORTED;
+    if (hidden % 64 || hidden > 8192) return STTD_ERR_UNSUPPORTED;
     if (B > ws->max_rows || vocab > ws->vocab || x_row_stride < hidden) return STTD_ERR_INVALID_ARG;
     HeadArgs a{};
     a.gain = final_norm; a.embed = embed; a.vocab = vocab; a.hidden = hidden; a.eps = rms_eps;

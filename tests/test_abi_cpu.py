@@ -58,3 +58,7 @@ def test_null_and_bad_arguments_rejected_on_host():
     assert L.sttd_workspace_alloc(ctypes.byref(bad), 4, 16, 0, ctypes.byref(out)) == B.ERR_UNSUPPORTED
     bad = B.block_params(256, 4, 2, 64, 500, 1e-6, 1e6, B.BF16)       # ffn not a multiple of 64
     assert L.sttd_workspace_alloc(ctypes.byref(bad), 4, 16, 0, ctypes.byref(out)) == B.ERR_UNSUPPORTED
+    bad = B.block_params(256, 4, 2, 64, 8256, 1e-6, 1e6, B.BF16)      # ffn above the 8192 GEMV row limit
+    assert L.sttd_workspace_alloc(ctypes.byref(bad), 4, 16, 0, ctypes.byref(out)) == B.ERR_UNSUPPORTED
+    bad = B.block_params(256, 72, 9, 128, 512, 1e-6, 1e6, B.BF16)     # n_heads * head_dim = 9216
+    assert L.sttd_workspace_alloc(ctypes.byref(bad), 4, 16, 0, ctypes.byref(out)) == B.ERR_UNSUPPORTED
