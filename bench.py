@@ -29,6 +29,28 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
 
+# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by a plain
+# 256 MiB copy (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0); valid only for the kernel
+# sources they were taken on (sha256 of the listed files).
+TRAFFIC = {
+    "gateup_gemv": {"rows": 1, "bytes": 50582654, "files": ["kernels_gemv.hip", "common.h"],
+                    "sha256": "29e880c56c35c60ef6a882c3fe3647d4e33771fcd48472124f58acfcb9cde512",
+                    "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"},
+}
+
+
+def traffic_bytes(name, rows):
+    """Counter-measured HBM bytes per launch, or None if absent, taken at another row
+    count, or the kernel changed since."""
+    import hashlib
+    t = TRAFFIC.get(name)
+    if not t or t["rows"] != rows:
+        return None
+    csrc = os.path.join(ROOT, "speech_text_decoder_amd", "csrc")
+    h = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in t["files"])).hexdigest()
+    return t["bytes"] if h == t["sha256"] else None
+
+
 KERNEL_NAMES = ["rmsnorm", "qkv_gemv", "qkv_gemm", "qk_rope_kv", "attn_rows", "attn_prefill", "o_gemv", "o_gemm",
                 "gateup_gemv", "gateup_gemm", "down_gemv", "down_gemm", "lm_head"]
 
@@ -36,13 +58,15 @@ KERNEL_NAMES = ["rmsnorm", "qkv_gemv", "qkv_gemm", "qk_rope_kv", "attn_rows", "a
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3_1p7b_stack28_greedy256")
     ap.add_argument("--replicas", type=int, default=8,
                     help="independent weight/KV replicas stacked for single-block workloads (MALL honesty)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-profile", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 3 times (scales HBM byte counters)")
     return ap.parse_args()
 
 
@@ -152,13 +176,13 @@ def kernel_table(totals, sh, rows_of, keys_of):
     return out
 
 
-def roofline_entry(table, name, bound):
+def roofline_entry(table, name, bound, rows=1):
     e = table.get(name)
     if not e:
         return None
     if bound == "hbm":
         return {"kernel": name, "bound": "hbm", "achieved": e["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(e["gbs"] / HBM_PEAK_GBS, 4), "traffic": None, "avg_us": e["avg_us"],
+                "frac": round(e["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(name, rows), "avg_us": e["avg_us"],
                 "bytes_per_launch": e["bytes"]}
     return {"kernel": name, "bound": "mfma", "achieved": e["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(e["tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": None, "avg_us": e["avg_us"],
@@ -500,7 +524,8 @@ def bench_batched(args, wl):
         table = kernel_table(dec, sh, lambda n: Bn, lambda n: float(lens.mean()) + (reps + 1) / 2.0)
         res["kernels"] = {"decode": table}
         res["kernel_timing"] = "device clock (s_memrealtime, 100 MHz): first-workgroup start to last-workgroup end"
-        res["roofline"] = roofline_entry(table, "gateup_gemm" if "gateup_gemm" in table else "gateup_gemv", "hbm")
+        res["roofline"] = roofline_entry(table, "gateup_gemm" if "gateup_gemm" in table else "gateup_gemv", "hbm",
+                                         rows=Bn)
     sess.close()
     return res
 
@@ -519,6 +544,15 @@ def main():
     binding.lib()  # fails loudly when the HIP library is missing
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n // 4, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": 3}}), flush=True)
+        return
     wl = WORKLOADS[args.workload]
     if wl.greedy and wl.prefill_rows > 0:
         res = bench_greedy_stack(args, wl)
