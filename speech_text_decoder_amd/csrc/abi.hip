@@ -37,6 +37,7 @@ struct sttd_workspace {
     float* part;        // [part_cap][nq][d + 4] attention split partials
     unsigned long long* partials;  // [max_rows][kHeadPartials] head argmax partials
     uint32_t* err;                 // [1]
+    int32_t* iota;                 // [max_rows]: 0, 1, ... (slab b of row b when no slab ids are given)
 };
 
 namespace {
@@ -425,6 +426,7 @@ sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int m
     const size_t o_part = take((size_t)part_cap * nq * (d + 4) * sizeof(float));
     const size_t o_partials = take(R * kHeadPartials * sizeof(unsigned long long));
     const size_t o_err = take(sizeof(uint32_t));
+    const size_t o_iota = take(R * sizeof(int32_t));
     sttd_workspace* ws = new (std::nothrow) sttd_workspace();
     if (!ws) return STTD_ERR_OOM;
     ws->p = *p;
@@ -448,6 +450,7 @@ sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int m
     ws->part = (float*)(b + o_part);
     ws->partials = (unsigned long long*)(b + o_partials);
     ws->err = (uint32_t*)(b + o_err);
+    ws->iota = (int32_t*)(b + o_iota);
     // RoPE table in fp64 on the host: pair i of position pos turns by pos * theta^(-2i/d)
     std::vector<float> table((size_t)max_pos * d);
     const int half = d / 2;
@@ -459,8 +462,11 @@ sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int m
             table[((size_t)pos * half + i) * 2 + 1] = (float)sin(a);
         }
     }
+    std::vector<int32_t> iota(R);
+    for (size_t i = 0; i < R; ++i) iota[i] = (int32_t)i;
     if (hipMemset(ws->base, 0, off) != hipSuccess ||
-        hipMemcpy(ws->rope, table.data(), table.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess) {
+        hipMemcpy(ws->rope, table.data(), table.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(ws->iota, iota.data(), R * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess) {
         (void)hipFree(ws->base);
         delete ws;
         return STTD_ERR_BACKEND;
@@ -526,7 +532,7 @@ sttd_status sttd_block_step(const sttd_block_params* p, const sttd_block_weights
     if (!pos || pos_bound <= 0) return STTD_ERR_INVALID_ARG;
     if (pos_bound > kv->n_ctx || pos_bound > ws->max_pos) return STTD_ERR_CONTEXT_FULL;
     if (!seq && B > kv->n_seq) return STTD_ERR_INVALID_ARG;
-    RowMap rm{pos, seq, 0, -1};
+    RowMap rm{pos, seq ? seq : ws->iota, 0, -1};
     return run_block(p, w, ws, kv, layer, B, rm, pos_bound, false, false, x, (hipStream_t)stream);
 }
 

@@ -37,16 +37,19 @@ struct F32 {
     typedef float T;
     static __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
     static __device__ __forceinline__ void st(float* p, int64_t i, float v) { p[i] = v; }
+    static __device__ __forceinline__ float cvt(float v) { return v; }
 };
 struct BF16 {
     typedef uint16_t T;
     static __device__ __forceinline__ float ld(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
     static __device__ __forceinline__ void st(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+    static __device__ __forceinline__ float cvt(uint16_t v) { return bf16_bits_to_f32(v); }
 };
 struct F16 {
     typedef uint16_t T;
     static __device__ __forceinline__ float ld(const uint16_t* p, int64_t i) { return f16_bits_to_f32(p[i]); }
     static __device__ __forceinline__ void st(uint16_t* p, int64_t i, float v) { p[i] = f32_to_f16_bits(v); }
+    static __device__ __forceinline__ float cvt(uint16_t v) { return f16_bits_to_f32(v); }
 };
 
 // 8 consecutive elements widened to fp32 (16-byte or 2x16-byte aligned loads).

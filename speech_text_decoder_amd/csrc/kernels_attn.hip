@@ -127,35 +127,42 @@ __global__ __launch_bounds__(NW * 64) void attn_rows_kernel(RowsArgs a) {
     const int grp = tid / LPK, sub = tid % LPK;
     const float scale = 1.4426950408889634f / sqrtf((float)D);
 
-    // 1. loads that do not depend on the position: this wave's head items of the
-    //    raw projection (items: G query heads, then the key, then the value;
-    //    wave w takes items w and w + NW)
+    // 1. the row's position and slab, this wave's raw head items of the
+    //    projection (items: G query heads, then the key, then the value; wave w
+    //    takes items w, w + NW, ...) and their gains: independent loads, all
+    //    issued before the first wait (addresses clamped, not branched around)
+    //    (decode rows always come with device position and slab arrays)
+    const int pos_v = FUSE ? a.rm.pos[r] : row_pos(a.rm, r);
+    const int seq_v = FUSE ? a.rm.seq[r] : row_seq(a.rm, r);
     constexpr int IPW = (G + 2 + NW - 1) / NW;  // items per wave
-    float u0[IPW], u1[IPW], g0[IPW], g1[IPW];
+    const int lc = lane < HALF ? lane : 0;
+    float u0[IPW], u1[IPW];
+    typename GT::T g0r[IPW], g1r[IPW];
+    if (FUSE) {
+        const float* src = a.q + (int64_t)r * a.ldq;
 #pragma unroll
-    for (int k = 0; k < IPW; ++k) {
-        const int it = wave + k * NW;
-        u0[k] = u1[k] = 0.f;
-        g0[k] = g1[k] = 1.f;
-        if (FUSE && it < G + 2 && lane < HALF) {
-            const float* src = a.q + (int64_t)r * a.ldq;
-            const int col = it < G ? (j * G + it) * D : (it == G ? (a.n_heads + j) * D
-                                                                : (a.n_heads + a.kv.n_kv + j) * D);
-            u0[k] = src[col + lane];
-            u1[k] = src[col + lane + HALF];
-            if (it <= G) {
-                const typename GT::T* gain = (const typename GT::T*)(it < G ? a.q_gain : a.k_gain);
-                g0[k] = GT::ld(gain, lane);
-                g1[k] = GT::ld(gain, lane + HALF);
-            }
+        for (int k = 0; k < IPW; ++k) {
+            const int it = wave + k * NW;
+            const int itc = it < G + 2 ? it : 0;
+            const int col = itc < G ? (j * G + itc) * D
+                                    : (itc == G ? (a.n_heads + j) * D : (a.n_heads + a.kv.n_kv + j) * D);
+            u0[k] = src[col + lc];
+            u1[k] = src[col + lc + HALF];
+            const typename GT::T* gain = (const typename GT::T*)(itc < G ? a.q_gain : a.k_gain);
+            g0r[k] = gain[lc];
+            g1r[k] = gain[lc + HALF];
         }
     }
-    // 2. the row's position and slab, then the first two cache rows of each group
-    const int pos = row_pos(a.rm, r);
-    const int seq = row_seq(a.rm, r);
+    // keep the scheduler from pulling the first use of a loaded value (and its
+    // wait) above the loads issued after it
+    __builtin_amdgcn_sched_barrier(0);
+    // 2. position-dependent loads: the rotation row, then the first cache rows of each group
+    const int pos = pos_v, seq = seq_v;
     const bool ok = pos >= 0 && pos < a.kv.n_ctx && pos < (FUSE ? a.max_pos : a.kv.n_ctx) && seq >= 0 &&
                     seq < a.kv.n_seq;
     if (!ok && tid == 0 && split == 0 && j == 0) record_error(a.err, pos < 0 || pos >= a.kv.n_ctx ? 1u : 2u);
+    float2 cs = make_float2(1.f, 0.f);
+    if (FUSE) cs = reinterpret_cast<const float2*>(a.rope)[(int64_t)(ok ? pos : 0) * HALF + lc];
     const int n_keys = ok ? pos + 1 : 0;
     const int chunk = (n_keys + a.n_splits - 1) / a.n_splits;
     const int c0 = split * chunk;
@@ -165,15 +172,18 @@ __global__ __launch_bounds__(NW * 64) void attn_rows_kernel(RowsArgs a) {
     const T* Kp = (const T*)a.kv.k + slab + sub * 8;
     const T* Vp = (const T*)a.kv.v + slab + sub * 8;
     const int cend = owner ? pos : c1;  // the new key (owner) is folded in from LDS below
+    // RIF rows per group in flight: row c + q * NG for q < RIF (clamped to row 0 past the end)
+    constexpr int RIF = G <= 2 ? 4 : (G == 4 ? 2 : 1);
+    constexpr int STEP = RIF * NG;
     int c = c0 + grp;
-    float kr[8], vr[8], kr2[8], vr2[8];
-    {
-        const int ca = c < cend ? c : 0, cb = c + NG < cend ? c + NG : 0;
-        load8(Kp + (int64_t)ca * D, kr, KT());
-        load8(Vp + (int64_t)ca * D, vr, KT());
-        load8(Kp + (int64_t)cb * D, kr2, KT());
-        load8(Vp + (int64_t)cb * D, vr2, KT());
+    float kr[RIF][8], vr[RIF][8];
+#pragma unroll
+    for (int q = 0; q < RIF; ++q) {
+        const int cq = c + q * NG < cend ? c + q * NG : 0;
+        load8(Kp + (int64_t)cq * D, kr[q], KT());
+        load8(Vp + (int64_t)cq * D, vr[q], KT());
     }
+    __builtin_amdgcn_sched_barrier(0);
     // 3. finish the head items: RMSNorm + rotation (queries, key); the owner
     //    writes key and value to cache row pos
     if (FUSE) {
@@ -181,11 +191,11 @@ __global__ __launch_bounds__(NW * 64) void attn_rows_kernel(RowsArgs a) {
         for (int k = 0; k < IPW; ++k) {
             const int it = wave + k * NW;
             if (it >= G + 2 || !ok) continue;
+            const float v0 = lane < HALF ? u0[k] : 0.f, v1 = lane < HALF ? u1[k] : 0.f;
             if (it <= G) {
-                const float rs = 1.0f / sqrtf(wave_sum(u0[k] * u0[k] + u1[k] * u1[k]) / (float)D + a.eps);
+                const float rs = 1.0f / sqrtf(wave_sum(v0 * v0 + v1 * v1) / (float)D + a.eps);
                 if (lane < HALF) {
-                    const float x0 = u0[k] * rs * g0[k], x1 = u1[k] * rs * g1[k];
-                    const float2 cs = reinterpret_cast<const float2*>(a.rope)[(int64_t)pos * HALF + lane];
+                    const float x0 = v0 * rs * GT::cvt(g0r[k]), x1 = v1 * rs * GT::cvt(g1r[k]);
                     const float r0 = x0 * cs.x - x1 * cs.y, r1 = x0 * cs.y + x1 * cs.x;
                     if (it < G) {
                         q_lds[it][lane] = r0 * scale;
@@ -198,10 +208,10 @@ __global__ __launch_bounds__(NW * 64) void attn_rows_kernel(RowsArgs a) {
                     }
                 }
             } else if (owner && lane < HALF) {
-                vn_lds[lane] = u0[k];
-                vn_lds[lane + HALF] = u1[k];
-                KT::st((T*)a.kv.v, slab + (int64_t)pos * D + lane, u0[k]);
-                KT::st((T*)a.kv.v, slab + (int64_t)pos * D + lane + HALF, u1[k]);
+                vn_lds[lane] = v0;
+                vn_lds[lane + HALF] = v1;
+                KT::st((T*)a.kv.v, slab + (int64_t)pos * D + lane, v0);
+                KT::st((T*)a.kv.v, slab + (int64_t)pos * D + lane + HALF, v1);
             }
         }
     } else {
@@ -223,37 +233,36 @@ __global__ __launch_bounds__(NW * 64) void attn_rows_kernel(RowsArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[g][i] = 0.f;
     }
-    // 4. cache rows [c0, cend): two per group per step, the next two in flight
-    for (; c < cend; c += 2 * NG) {
-        const bool two = c + NG < cend;
-        float s[G], s2[G];
+    // 4. cache rows [c0, cend): RIF per group per step, the next RIF in flight
+    for (; c < cend; c += STEP) {
+        float sc[RIF][G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float t1 = 0.f, t2 = 0.f;
+        for (int q = 0; q < RIF; ++q) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                t1 = fmaf(qv[g][i], kr[i], t1);
-                t2 = fmaf(qv[g][i], kr2[i], t2);
+            for (int g = 0; g < G; ++g) {
+                float t = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) t = fmaf(qv[g][i], kr[q][i], t);
+                sc[q][g] = group_sum<LPK>(t);
             }
-            s[g] = group_sum<LPK>(t1);
-            s2[g] = two ? group_sum<LPK>(t2) : -INFINITY;
         }
-        float vcur[8], vcur2[8];
+        float vcur[RIF][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            vcur[i] = vr[i];
-            vcur2[i] = vr2[i];
-        }
-        const int cn = c + 2 * NG;
+        for (int q = 0; q < RIF; ++q)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vcur[q][i] = vr[q][i];
+        const int cn = c + STEP;
         if (cn < cend) {
-            const int cb = cn + NG < cend ? cn + NG : cn;
-            load8(Kp + (int64_t)cn * D, kr, KT());
-            load8(Vp + (int64_t)cn * D, vr, KT());
-            load8(Kp + (int64_t)cb * D, kr2, KT());
-            load8(Vp + (int64_t)cb * D, vr2, KT());
+#pragma unroll
+            for (int q = 0; q < RIF; ++q) {
+                const int cq = cn + q * NG < cend ? cn + q * NG : cn;
+                load8(Kp + (int64_t)cq * D, kr[q], KT());
+                load8(Vp + (int64_t)cq * D, vr[q], KT());
+            }
         }
-        step_state<G>(m, l, o, s, vcur);
-        if (two) step_state<G>(m, l, o, s2, vcur2);
+#pragma unroll
+        for (int q = 0; q < RIF; ++q)
+            if (c + q * NG < cend) step_state<G>(m, l, o, sc[q], vcur[q]);
     }
     // 5. the new key (held in LDS by the owner), folded in by group 0
     if (owner && grp == 0) {
@@ -384,7 +393,7 @@ static hipError_t rows_dispatch(const RowsArgs& a, int R, hipStream_t s) {
     const dim3 grid(R, a.kv.n_kv, a.n_splits);
 #define ROWS_LAUNCH(G_)                                                                             \
     do {                                                                                            \
-        constexpr int NW_ = G_ <= 2 ? 4 : 8;                                                      \
+        constexpr int NW_ = 8;                                                                      \
         attn_rows_kernel<KT, GT, D, G_, NW_, FUSE><<<grid, NW_ * 64, 0, s>>>(a);                  \
     } while (0)
     switch (G) {
@@ -414,7 +423,7 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
                             float* part, float* out_f32, uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo,
                             uint32_t* err, const QkRope* fuse, WType gt, hipStream_t s) {
     if (R <= 0) return hipSuccess;
-    if (n_splits < 1 || n_splits > 64) return hipErrorInvalidValue;
+    if (n_splits < 1 || n_splits > 64 || (fuse && (!rm.pos || !rm.seq))) return hipErrorInvalidValue;
     RowsArgs a{};
     a.q = q; a.ldq = ldq; a.n_heads = n_heads; a.rm = rm; a.kv = kv; a.n_splits = n_splits; a.part = part;
     a.out_f32 = out_f32; a.out_bf16 = out_bf16; a.out_lo = out_bf16_lo; a.ldo = ldo; a.err = err;

@@ -353,7 +353,9 @@ static hipError_t launch_wt(const GemvArgs& a, GemvEpi epi, hipStream_t s) {
     if (epi == GEMV_SWIGLU)
         return norm ? launch_k<WT, GEMV_SWIGLU, 4, true>(a, s) : launch_k<WT, GEMV_SWIGLU, 4, false>(a, s);
     if (epi == GEMV_RESID) {
-        if (a.xpart) return launch_k<WT, GEMV_RESID, 2, false, true>(a, s);
+        // merging the attention splits on load costs n_splits times the activation
+        // reads of a plain row, so fewer, wider workgroups pay it fewer times
+        if (a.xpart) return launch_k<WT, GEMV_RESID, 8, false, true>(a, s);
         return norm ? launch_k<WT, GEMV_RESID, 2, true>(a, s) : launch_k<WT, GEMV_RESID, 2, false>(a, s);
     }
     return norm ? launch_k<WT, GEMV_STORE, 4, true>(a, s) : launch_k<WT, GEMV_STORE, 4, false>(a, s);
