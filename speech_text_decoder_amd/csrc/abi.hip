@@ -188,8 +188,13 @@ KVLayer kv_layer(const sttd_kv_cache* kv, int layer) {
 // Splits of the rows-attention grid: about 256 cache rows per split at the
 // host bound (16-wave workgroups read them two rows per 16-lane group per
 // step), one split (no merge kernel) up to 256 positions.
-int choose_splits(int rows, int pos_bound, int part_cap) {
+// Splits of each row's cache span over workgroups: about 256 positions each,
+// but for batches of rows no more than keeps about two waves of workgroups
+// (512) busy, so each workgroup streams a longer run of rows.
+int choose_splits(int rows, int n_kv, int pos_bound, int part_cap) {
     int s = (pos_bound + 255) / 256;
+    const int fill = (512 + rows * n_kv - 1) / (rows * n_kv);
+    if (rows > 1 && s > fill) s = fill;
     if (s > kMaxSplits) s = kMaxSplits;
     if (s > part_cap / rows) s = part_cap / rows;
     return s < 1 ? 1 : s;
@@ -252,7 +257,7 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
         ProfScope ps(STTD_KERN_ATTN_PREFILL, s);
         TRY(launch_attn_prefill((const uint16_t*)ws->qbuf, qd, R, rm.pos0, rm.seq0, nq, kl, ao, ao_lo, qd, s));
     } else {
-        splits = choose_splits(R, pos_bound, ws->part_cap);
+        splits = choose_splits(R, nkv, pos_bound, ws->part_cap);
         // GEMV path: a split result stays as partials and the O projection merges them on load
         const bool defer = !mfma && splits > 1;
         ProfScope ps(STTD_KERN_ATTN_ROWS, s);
@@ -547,6 +552,7 @@ sttd_status sttd_lm_head_argmax(const void* final_norm, const void* embed, sttd_
     a.gain = final_norm; a.embed = embed; a.vocab = vocab; a.hidden = hidden; a.eps = rms_eps;
     a.x = x; a.ldx = x_row_stride; a.rows = B; a.ids = ids; a.logits = logits; a.next_x = next_x; a.pos = pos;
     a.partials = ws->partials; a.max_partials = kHeadPartials; a.err = ws->err;
+    a.zbuf = hidden <= ws->p.hidden ? ws->xn : nullptr;  // 2 * B * hidden bf16 fit in the normed-row planes
     ProfScope ps(STTD_KERN_LM_HEAD, (hipStream_t)stream);
     TRY(launch_lm_head_argmax(a, wtype == STTD_BF16 ? W_BF16 : W_F32, (hipStream_t)stream));
     return STTD_OK;

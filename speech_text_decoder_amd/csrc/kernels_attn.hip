@@ -391,10 +391,13 @@ template <class KT, class GT, int D, bool FUSE>
 static hipError_t rows_dispatch(const RowsArgs& a, int R, hipStream_t s) {
     const int G = a.n_heads / a.kv.n_kv;
     const dim3 grid(R, a.kv.n_kv, a.n_splits);
+    // one row: 8 waves per workgroup; batches of rows: 4, so two workgroups share a CU
 #define ROWS_LAUNCH(G_)                                                                             \
     do {                                                                                            \
-        constexpr int NW_ = 8;                                                                      \
-        attn_rows_kernel<KT, GT, D, G_, NW_, FUSE><<<grid, NW_ * 64, 0, s>>>(a);                  \
+        if (G_ <= 2 && R > 1)                                                                       \
+            attn_rows_kernel<KT, GT, D, G_, 4, FUSE><<<grid, 4 * 64, 0, s>>>(a);                    \
+        else                                                                                        \
+            attn_rows_kernel<KT, GT, D, G_, 8, FUSE><<<grid, 8 * 64, 0, s>>>(a);                    \
     } while (0)
     switch (G) {
         case 1: ROWS_LAUNCH(1); break;

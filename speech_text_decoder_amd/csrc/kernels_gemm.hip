@@ -73,7 +73,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
             grow = r < BN / 2 ? c : g.N + c;
             W = g.w[0];
         } else {
-            const int n = tile_n * BN + r;
+            const int n0 = tile_n * BN + r;
+            brow_ok[i] = n0 < g.N;
+            const int n = brow_ok[i] ? n0 : 0;
             const bool s2 = n >= g.seg_end[1], s1 = n >= g.seg_end[0];
             grow = n - (s2 ? g.seg_end[1] : (s1 ? g.seg_end[0] : 0));
             W = s2 ? g.w[2] : (s1 ? g.w[1] : g.w[0]);
@@ -176,6 +178,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
                     const int n = tile_n * BN + wn * (BN / 2) + j * 16 + lane % 16;
+                    if (n >= g.N) continue;
                     float* dst = g.C + (int64_t)m * g.ldc + n;
                     if (EPI == GEMM_RESID) *dst += acc[i][j][rr];
                     else *dst = acc[i][j][rr];
@@ -186,10 +189,331 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
     clock_end(g.clk);
 }
 
+
+// ------------------------------------------------------------------ large-M tiles
+// For prefills of many rows (the GEMMs are MFMA-bound there): 256 x 256 output
+// tiles, 4 waves in 2 x 2 each owning 128 x 128 (8 x 8 fragments of
+// v_mfma_f32_16x16x32_bf16, accumulators in the AGPR half of the register
+// file), K in steps of 64 through two LDS buffers so one barrier per step
+// separates staging from use. Per wave and 32-deep step the fragments cost
+// 16 KB of LDS reads for 64 MFMAs, half of what LDS delivers in that time.
+//
+// Tiles are handed out XCD-aware: workgroup i runs on XCD i % 8, so the tile
+// index is remapped to give each XCD a contiguous run of tiles with the row
+// tile varying fastest; the workgroups of one XCD then share weight tiles in
+// their L2.
+//
+// SWIGLU: LDS weight rows [128 wn, 128 wn + 64) hold gate rows and
+// [128 wn + 64, 128 wn + 128) the matching up rows of act columns
+// 128 tile_n + 64 wn .. + 64, so wave column wn finds gate (fragments 0..3)
+// and up (fragments 4..7) of the same columns in its own accumulators.
+constexpr int BIG_BM = 256, BIG_BN = 256, BIG_BK = 64, BIG_STR = BIG_BK + 8;
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+    constexpr int FM = 8, FN = 8;
+    constexpr int VECS = BIG_BM * BIG_BK / 8 / 256;  // 16-byte vectors per thread per operand and step
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BIG_BM * BIG_STR];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BIG_BN * BIG_STR];
+
+    clock_begin(g.clk);
+    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
+    const int wm = wave / 2, wn = wave % 2;
+    // XCD-aware tile order when the tile count splits evenly over the 8 XCDs
+    const int n_tiles = tiles_m * tiles_n;
+    const int id = blockIdx.x;
+    const int t = n_tiles % 8 ? id : (id % 8) * (n_tiles / 8) + id / 8;
+    const int tile_m = t % tiles_m, tile_n = t / tiles_m;
+    const int m0 = tile_m * BIG_BM;
+
+    const uint16_t* aptr[VECS];
+    const uint16_t* bptr[VECS];
+    bool bok[VECS];
+#pragma unroll
+    for (int i = 0; i < VECS; ++i) {
+        const int v = tid + i * 256;
+        const int r = v / (BIG_BK / 8), ck = (v % (BIG_BK / 8)) * 8;
+        const int am = m0 + r < g.M ? m0 + r : 0;
+        aptr[i] = g.A + (int64_t)am * g.lda + ck;
+        int grow;
+        const uint16_t* W;
+        bok[i] = true;
+        if (EPI == GEMM_SWIGLU) {
+            const int wsel = r / 128, within = r % 128;
+            const int c = tile_n * 128 + wsel * 64 + (within % 64);
+            grow = within < 64 ? c : g.N + c;
+            W = g.w[0];
+        } else {
+            const int n0 = tile_n * BIG_BN + r;
+            bok[i] = n0 < g.N;
+            const int n = bok[i] ? n0 : 0;
+            const bool s2 = n >= g.seg_end[1], s1 = n >= g.seg_end[0];
+            grow = n - (s2 ? g.seg_end[1] : (s1 ? g.seg_end[0] : 0));
+            W = s2 ? g.w[2] : (s1 ? g.w[1] : g.w[0]);
+        }
+        bptr[i] = W + (int64_t)grow * g.K + ck;
+    }
+    u32x4 areg[VECS], breg[VECS];
+    auto fetch = [&](int64_t k0) {
+#pragma unroll
+        for (int i = 0; i < VECS; ++i) areg[i] = *reinterpret_cast<const u32x4*>(aptr[i] + k0);
+#pragma unroll
+        for (int i = 0; i < VECS; ++i)
+            breg[i] = bok[i] ? *reinterpret_cast<const u32x4*>(bptr[i] + k0) : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < VECS; ++i) {
+            const int v = tid + i * 256;
+            const int o = (v / (BIG_BK / 8)) * BIG_STR + (v % (BIG_BK / 8)) * 8;
+            *reinterpret_cast<u32x4*>(&As[buf][o]) = areg[i];
+            *reinterpret_cast<u32x4*>(&Bs[buf][o]) = breg[i];
+        }
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = g.K / BIG_BK;
+    fetch(0);
+    stash(0);
+    if (nk > 1) fetch(BIG_BK);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        const uint16_t* Ab = As[buf];
+        const uint16_t* Bb = Bs[buf];
+#pragma unroll
+        for (int ks = 0; ks < BIG_BK / 32; ++ks) {
+            const int kc = ks * 32 + (lane / 16) * 8;
+            bf16x8 af[FM], bfr[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const bf16x8*>(&Ab[(wm * 128 + i * 16 + lane % 16) * BIG_STR + kc]);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8*>(&Bb[(wn * 128 + j * 16 + lane % 16) * BIG_STR + kc]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < nk) {
+            stash(buf ^ 1);  // the other buffer was last read before the previous barrier
+            if (kt + 2 < nk) fetch((int64_t)(kt + 2) * BIG_BK);
+        }
+        __syncthreads();
+    }
+
+    // epilogue
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int m = m0 + wm * 128 + i * 16 + (lane / 16) * 4 + rr;
+            if (m >= g.M) continue;
+            if (EPI == GEMM_SWIGLU) {
+#pragma unroll
+                for (int j = 0; j < FN / 2; ++j) {
+                    const int c = tile_n * 128 + wn * 64 + j * 16 + lane % 16;
+                    const float gt = acc[i][j][rr], up = acc[i][j + FN / 2][rr];
+                    const float a = gt / (1.0f + expf(-gt)) * up;
+                    uint16_t hi, lo;
+                    split_bf16(a, hi, lo);
+                    g.Cb[(int64_t)m * g.ldcb + c] = hi;
+                    if (g.Cb_lo) g.Cb_lo[(int64_t)m * g.ldcb + c] = lo;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int n = tile_n * BIG_BN + wn * 128 + j * 16 + lane % 16;
+                    if (n >= g.N) continue;
+                    float* dst = g.C + (int64_t)m * g.ldc + n;
+                    if (EPI == GEMM_RESID) *dst += acc[i][j][rr];
+                    else *dst = acc[i][j][rr];
+                }
+            }
+        }
+    }
+    clock_end(g.clk);
+}
+
+// Whether the large tiles apply: many rows, no split activations, shapes that tile.
+static bool big_tiles_fit(const GemmArgs& g, GemmEpi epi) {
+    if (g.A_lo || g.M < 1024 || g.K % BIG_BK) return false;
+    const int tiles_m = (g.M + BIG_BM - 1) / BIG_BM;
+    const int tiles_n = epi == GEMM_SWIGLU ? g.N / 128 : (g.N + BIG_BN - 1) / BIG_BN;
+    return tiles_m > 0 && tiles_n > 0 && !(epi == GEMM_SWIGLU && g.N % 128);
+}
+
+static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
+    const int tiles_m = (g.M + BIG_BM - 1) / BIG_BM;
+    const int tiles_n = epi == GEMM_SWIGLU ? g.N / 128 : (g.N + BIG_BN - 1) / BIG_BN;
+    const dim3 grid(tiles_m * tiles_n);
+    if (epi == GEMM_SWIGLU) gemm_big_kernel<GEMM_SWIGLU><<<grid, 256, 0, s>>>(g, tiles_m, tiles_n);
+    else if (epi == GEMM_RESID) gemm_big_kernel<GEMM_RESID><<<grid, 256, 0, s>>>(g, tiles_m, tiles_n);
+    else gemm_big_kernel<GEMM_STORE><<<grid, 256, 0, s>>>(g, tiles_m, tiles_n);
+}
+
+
+// ------------------------------------------------------------------ few rows (decode batches)
+// C[R, N] (+)= A[R, K] W[N, K]^T for R <= 16 RF rows: weight-stationary MFMA.
+// Each workgroup owns CF column fragments of 16 (SWIGLU: the gate and the up
+// fragment of 16 act columns) and a share of K, split over its 4 waves and
+// over gridDim.y workgroups (RESID only; those add into C with atomics). Weight
+// rows stream from global memory straight into B fragments (lane l: column
+// l % 16, K elements (l / 16) * 8 .. + 8), so every weight byte is read once;
+// the few activation rows (bf16 high and low parts) are the A fragments,
+// re-read from L2 by every workgroup. Loads run PD K-steps ahead.
+template <int EPI, int RF, int CF>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
+    constexpr int PD = 4;  // K-steps of 32 per load batch
+    __shared__ float red[4][RF * 16][CF * 16 + 1];
+    clock_begin(g.clk);
+    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
+    const int ct = blockIdx.x;
+    // weight row of each column fragment for this lane
+    const uint16_t* wrow[CF];
+    bool wok[CF];
+#pragma unroll
+    for (int f = 0; f < CF; ++f) {
+        if (EPI == GEMM_SWIGLU) {
+            const int c = ct * 16 + lane % 16;  // act column
+            wok[f] = c < g.N;
+            const int cc = wok[f] ? c : 0;
+            wrow[f] = g.w[0] + (int64_t)(f == 0 ? cc : g.N + cc) * g.K;
+        } else {
+            const int n0 = (ct * CF + f) * 16 + lane % 16;
+            wok[f] = n0 < g.N;
+            const int n = wok[f] ? n0 : 0;
+            const bool s2 = n >= g.seg_end[1], s1 = n >= g.seg_end[0];
+            const int grow = n - (s2 ? g.seg_end[1] : (s1 ? g.seg_end[0] : 0));
+            wrow[f] = (s2 ? g.w[2] : (s1 ? g.w[1] : g.w[0])) + (int64_t)grow * g.K;
+        }
+    }
+    const uint16_t* arow[RF];
+    const uint16_t* alrow[RF];
+#pragma unroll
+    for (int r = 0; r < RF; ++r) {
+        const int m = min(r * 16 + lane % 16, g.M - 1);
+        arow[r] = g.A + (int64_t)m * g.lda;
+        alrow[r] = (g.A_lo ? g.A_lo : g.A) + (int64_t)m * g.lda;
+    }
+    const bool lo = g.A_lo != nullptr;
+    // this wave's K-steps: [s0, s1) of K / 32
+    const int n_steps = g.K / 32;
+    const int parts = gridDim.y * 4;
+    const int per = (n_steps + parts - 1) / parts;
+    const int s0 = min((int)(blockIdx.y * 4 + wave) * per, n_steps);
+    const int s1 = min(s0 + per, n_steps);
+    const int koff = (lane / 16) * 8;
+
+    f32x4 acc[RF][CF];
+#pragma unroll
+    for (int r = 0; r < RF; ++r)
+#pragma unroll
+        for (int f = 0; f < CF; ++f) acc[r][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 wb[PD][CF], ab[PD][RF], alb[PD][RF];
+    auto load = [&](int s) {  // batch of PD steps from step s (clamped reads past s1 are not used)
+#pragma unroll
+        for (int p = 0; p < PD; ++p) {
+            const int k = min(s + p, n_steps - 1) * 32 + koff;
+#pragma unroll
+            for (int f = 0; f < CF; ++f) wb[p][f] = *reinterpret_cast<const u32x4*>(wrow[f] + k);
+#pragma unroll
+            for (int r = 0; r < RF; ++r) {
+                ab[p][r] = *reinterpret_cast<const u32x4*>(arow[r] + k);
+                if (lo) alb[p][r] = *reinterpret_cast<const u32x4*>(alrow[r] + k);
+            }
+        }
+    };
+    for (int s = s0; s < s1; s += PD) {
+        load(s);
+#pragma unroll
+        for (int p = 0; p < PD; ++p) {
+            if (s + p >= s1) break;
+#pragma unroll
+            for (int r = 0; r < RF; ++r)
+#pragma unroll
+                for (int f = 0; f < CF; ++f) {
+                    const bf16x8 bw = __builtin_bit_cast(bf16x8, wb[p][f]);
+                    acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ab[p][r]), bw,
+                                                                        acc[r][f], 0, 0, 0);
+                    if (lo)
+                        acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, alb[p][r]),
+                                                                            bw, acc[r][f], 0, 0, 0);
+                }
+        }
+    }
+    // merge the 4 waves' K shares
+#pragma unroll
+    for (int r = 0; r < RF; ++r)
+#pragma unroll
+        for (int f = 0; f < CF; ++f)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave][r * 16 + (lane / 16) * 4 + i][f * 16 + lane % 16] = acc[r][f][i];
+    __syncthreads();
+    constexpr int OUTS = RF * 16 * CF * 16;
+    for (int o = tid; o < OUTS; o += 256) {
+        const int row = o / (CF * 16), col = o % (CF * 16);
+        if (row >= g.M) continue;
+        const float v = red[0][row][col] + red[1][row][col] + red[2][row][col] + red[3][row][col];
+        if (EPI == GEMM_SWIGLU) {
+            if (col >= 16) continue;  // the up half is read with its gate
+            const int c = ct * 16 + col;
+            if (c >= g.N) continue;
+            const float up = red[0][row][col + 16] + red[1][row][col + 16] + red[2][row][col + 16] +
+                             red[3][row][col + 16];
+            const float a = v / (1.0f + expf(-v)) * up;
+            uint16_t hi, lo16;
+            split_bf16(a, hi, lo16);
+            g.Cb[(int64_t)row * g.ldcb + c] = hi;
+            if (g.Cb_lo) g.Cb_lo[(int64_t)row * g.ldcb + c] = lo16;
+        } else {
+            const int n = ct * CF * 16 + col;
+            if (n >= g.N) continue;
+            float* dst = g.C + (int64_t)row * g.ldc + n;
+            if (EPI == GEMM_STORE) *dst = v;
+            else if (gridDim.y == 1) *dst += v;
+            else atomicAdd(dst, v);
+        }
+    }
+    clock_end(g.clk);
+}
+
+// Rows a skinny launch takes (16 per row fragment, up to 4 fragments).
+constexpr int kSkinnyMaxRows = 64;
+
+template <int EPI, int CF>
+static void launch_skinny_rf(const GemmArgs& g, dim3 grid, hipStream_t s) {
+    if (g.M <= 16) gemm_skinny_kernel<EPI, 1, CF><<<grid, 256, 0, s>>>(g);
+    else if (g.M <= 32) gemm_skinny_kernel<EPI, 2, CF><<<grid, 256, 0, s>>>(g);
+    else gemm_skinny_kernel<EPI, 4, CF><<<grid, 256, 0, s>>>(g);
+}
+
+static void launch_gemm_skinny(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
+    if (epi == GEMM_SWIGLU) {
+        launch_skinny_rf<GEMM_SWIGLU, 2>(g, dim3((g.N + 15) / 16, 1), s);
+        return;
+    }
+    const int tiles = (g.N + 15) / 16;
+    // RESID may split K over workgroups (atomic adds) until about 256 workgroups run
+    int ks = 1;
+    if (epi == GEMM_RESID)
+        while (tiles * ks * 2 <= 256 && g.K / 32 >= ks * 2 * 4 * 4) ks *= 2;
+    if (epi == GEMM_RESID) launch_skinny_rf<GEMM_RESID, 1>(g, dim3(tiles, ks), s);
+    else launch_skinny_rf<GEMM_STORE, 1>(g, dim3(tiles, 1), s);
+}
+
 template <bool SPLIT>
 static void launch_gemm_t(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     constexpr int BM = 64, BN = 128;
-    dim3 grid(epi == GEMM_SWIGLU ? g.N / (BN / 2) : g.N / BN, (g.M + BM - 1) / BM);
+    dim3 grid(epi == GEMM_SWIGLU ? g.N / (BN / 2) : (g.N + BN - 1) / BN, (g.M + BM - 1) / BM);
     if (epi == GEMM_SWIGLU) gemm_bf16_kernel<BM, BN, GEMM_SWIGLU, SPLIT><<<grid, 256, 0, s>>>(g);
     else if (epi == GEMM_RESID) gemm_bf16_kernel<BM, BN, GEMM_RESID, SPLIT><<<grid, 256, 0, s>>>(g);
     else gemm_bf16_kernel<BM, BN, GEMM_STORE, SPLIT><<<grid, 256, 0, s>>>(g);
@@ -199,7 +523,9 @@ hipError_t launch_gemm(const GemmArgs& args, GemmEpi epi, hipStream_t s) {
     if (args.M <= 0) return hipSuccess;
     GemmArgs g = args;
     g.clk = clock_slot();
-    if (g.A_lo) launch_gemm_t<true>(g, epi, s);
+    if (g.M <= kSkinnyMaxRows && g.K % 32 == 0) launch_gemm_skinny(g, epi, s);
+    else if (big_tiles_fit(g, epi)) launch_gemm_big(g, epi, s);
+    else if (g.A_lo) launch_gemm_t<true>(g, epi, s);
     else launch_gemm_t<false>(g, epi, s);
     return hipGetLastError();
 }

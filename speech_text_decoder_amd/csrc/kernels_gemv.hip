@@ -528,10 +528,122 @@ static hipError_t launch_head_wt(const HeadArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+
+// Batches of rows (bf16 embedding): the normed rows z = RMSNorm(x) * g are
+// first rounded to bf16 high and low parts, then a weight-stationary MFMA
+// pass streams the embedding once for up to 16 rows: each workgroup walks
+// vocabulary tiles of 32 rows; each wave holds the A fragments (rows x its
+// quarter of K, high and low) in registers for the whole walk and feeds the
+// tile's embedding rows straight from global memory as B fragments. The
+// waves' partial logits meet in LDS; each thread keeps the best key of its
+// activation row over its two columns of every tile, and the 16 threads of a
+// row merge their keys at the end into the workgroup's partial.
+template <int KSW>
+__global__ __launch_bounds__(256) void head_mfma_kernel(HeadArgs a, const uint16_t* __restrict__ zh,
+                                                        const uint16_t* __restrict__ zl, int b0, int nb) {
+    constexpr int PD = KSW < 8 ? KSW : 8;  // K-steps of embedding loads in flight per wave
+    __shared__ float red[4][16][33];
+    clock_begin(a.clk);
+    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
+    const int n_steps = a.hidden / 32;
+    const int per = (n_steps + 3) / 4;
+    const int s0 = min(wave * per, n_steps), s1 = min(s0 + per, n_steps);
+    const int koff = (lane / 16) * 8;
+    // A fragments of this wave's K steps, rows b0 + lane % 16 (clamped)
+    u32x4 ah[KSW], al[KSW];
+    {
+        const int row = min(lane % 16, nb - 1);
+#pragma unroll
+        for (int i = 0; i < KSW; ++i) {
+            const int k = min(s0 + i, n_steps - 1) * 32 + koff;
+            ah[i] = *reinterpret_cast<const u32x4*>(zh + (int64_t)row * a.hidden + k);
+            al[i] = *reinterpret_cast<const u32x4*>(zl + (int64_t)row * a.hidden + k);
+        }
+    }
+    const uint16_t* E = (const uint16_t*)a.embed;
+    const int n_tiles = (a.vocab + 31) / 32;
+    const int my_row = tid / 16, my_col = (tid % 16) * 2;
+    unsigned long long best = 0ull;
+    for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+        const uint16_t* er[2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+            er[f] = E + (int64_t)min(tile * 32 + f * 16 + lane % 16, a.vocab - 1) * a.hidden + koff;
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int i0 = 0; i0 < KSW; i0 += PD) {
+            u32x4 wb[PD][2];
+#pragma unroll
+            for (int p = 0; p < PD; ++p)
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+                    wb[p][f] = *reinterpret_cast<const u32x4*>(er[f] + min(s0 + i0 + p, n_steps - 1) * 32);
+#pragma unroll
+            for (int p = 0; p < PD; ++p) {
+                if (s0 + i0 + p >= s1) break;
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    const bf16x8 bw = __builtin_bit_cast(bf16x8, wb[p][f]);
+                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah[i0 + p]), bw,
+                                                                     acc[f], 0, 0, 0);
+                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al[i0 + p]), bw,
+                                                                     acc[f], 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave][(lane / 16) * 4 + i][f * 16 + lane % 16] = acc[f][i];
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int col = my_col + c, n = tile * 32 + col;
+            const float v = red[0][my_row][col] + red[1][my_row][col] + red[2][my_row][col] + red[3][my_row][col];
+            if (my_row < nb && n < a.vocab) {
+                const unsigned long long key =
+                    ((unsigned long long)float_order_key(v) << 32) | (unsigned long long)(~(uint32_t)n);
+                best = key > best ? key : best;
+                if (a.logits) a.logits[(int64_t)(b0 + my_row) * a.vocab + n] = v;
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) {
+        const unsigned long long o = __shfl_xor(best, off, WAVE);
+        best = o > best ? o : best;
+    }
+    if (tid % 16 == 0 && my_row < nb) a.partials[(int64_t)(b0 + my_row) * gridDim.x + blockIdx.x] = best;
+    clock_end(a.clk);
+}
+
+// MFMA head for batches: norm to bf16 planes, then 16-row chunks, then the finalize pass.
+static hipError_t launch_head_mfma(const HeadArgs& a, hipStream_t s) {
+    uint16_t* zh = a.zbuf;
+    uint16_t* zl = a.zbuf + (size_t)a.rows * a.hidden;
+    hipError_t e = launch_rmsnorm_rows_bf16(a.x, a.ldx, a.gain, W_BF16, zh, zl, a.hidden, a.rows, a.hidden, a.eps, s);
+    if (e != hipSuccess) return e;
+    const int n_tiles = (a.vocab + 31) / 32;
+    const int grid = n_tiles < a.max_partials ? n_tiles : a.max_partials;
+    const int ksw = (a.hidden / 32 + 3) / 4;
+    for (int b0 = 0; b0 < a.rows; b0 += 16) {
+        const int nb = a.rows - b0 < 16 ? a.rows - b0 : 16;
+        const uint16_t* h = zh + (size_t)b0 * a.hidden;
+        const uint16_t* l = zl + (size_t)b0 * a.hidden;
+        if (ksw <= 4) head_mfma_kernel<4><<<grid, 256, 0, s>>>(a, h, l, b0, nb);
+        else if (ksw <= 8) head_mfma_kernel<8><<<grid, 256, 0, s>>>(a, h, l, b0, nb);
+        else head_mfma_kernel<16><<<grid, 256, 0, s>>>(a, h, l, b0, nb);
+    }
+    lm_head_finalize_kernel<BF16><<<a.rows, 256, 0, s>>>(a, grid);
+    return hipGetLastError();
+}
+
 hipError_t launch_lm_head_argmax(const HeadArgs& args, WType wt, hipStream_t s) {
     if (args.rows <= 0) return hipSuccess;
     HeadArgs a = args;
     a.clk = clock_slot();
+    if (wt == W_BF16 && a.zbuf && a.rows > 4 && a.hidden % 32 == 0 && a.hidden <= 2048) return launch_head_mfma(a, s);
     return wt == W_BF16 ? launch_head_wt<BF16>(a, s) : launch_head_wt<F32>(a, s);
 }
 

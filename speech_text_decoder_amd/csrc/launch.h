@@ -113,6 +113,7 @@ struct HeadArgs {
     unsigned long long* partials;  // [rows][max_partials] per-workgroup best keys
     int max_partials;              // workgroups of the head GEMV (its grid width)
     uint32_t* err;
+    uint16_t* zbuf;      // optional scratch of 2 * rows * hidden bf16: lets batches of rows take the MFMA head
     uint64_t* clk;
 };
 hipError_t launch_lm_head_argmax(const HeadArgs& a, WType wt, hipStream_t s);

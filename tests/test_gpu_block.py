@@ -92,6 +92,14 @@ def test_small_bf16_head128_group8(T):
     log(f"SMALL128 T={T}: {max(errs):.2e}")
 
 
+def test_many_rows_large_tiles_with_row_and_column_tails():
+    """1100 rows take the 256 x 256 MFMA tiles: 4 full row tiles and a ragged one; the
+    hidden size 320 leaves a partial column tile in the O and down projections."""
+    sh = DecoderShape(hidden=320, n_heads=4, n_kv_heads=2, head_dim=64, ffn=768)
+    errs = run_block_case(sh, 15, 1100, 1, 1200)
+    log(f"T=1100 H=320: {max(errs):.2e}")
+
+
 def test_small_fp32_kv_cache_bf16_weights():
     sh = replace(SMALL64, kvdtype="f32")
     errs = run_block_case(sh, 13, 40, 3, 128)
@@ -140,12 +148,14 @@ def test_qwen3_1p7b_block_t153_prefill_then_64_steps():
     log(f"1.7B block T=153: prefill {errs[0]:.2e}, steps max {max(errs[1:]):.2e}")
 
 
-def test_lm_head_argmax_planted_ties_and_feedback():
+@pytest.mark.parametrize("n_rows", [3, 21])
+def test_lm_head_argmax_planted_ties_and_feedback(n_rows):
+    """3 rows take the GEMV head; 21 rows the MFMA head (norm planes, a 16-row and a 5-row chunk)."""
     sh = replace(SMALL64, vocab=5000)
     rng = np.random.default_rng(3)
     E = synth.to_bf16_bits(rng.standard_normal((sh.vocab, sh.hidden)).astype(np.float32) * 0.02)
     g = synth.to_bf16_bits(np.ones(sh.hidden, np.float32))
-    x = rng.standard_normal((3, sh.hidden)).astype(np.float32)
+    x = rng.standard_normal((n_rows, sh.hidden)).astype(np.float32)
     # row 0: rows 4321 and 17 of E both equal the row's direction -> tie, lowest index wins
     z = x[0] / np.sqrt(np.mean(x[0] ** 2) + 1e-6)
     E[4321] = synth.to_bf16_bits(z * 0.5)
@@ -153,23 +163,25 @@ def test_lm_head_argmax_planted_ties_and_feedback():
     # row 1: a single planted maximum at the last vocabulary row
     z1 = x[1] / np.sqrt(np.mean(x[1] ** 2) + 1e-6)
     E[4999] = synth.to_bf16_bits(z1 * 0.5)
-    sess = DecoderSession(sh, [synth.block_weights(16, 0, sh)], embed=E, final_norm=g, n_ctx=16, max_rows=3)
+    sess = DecoderSession(sh, [synth.block_weights(16, 0, sh)], embed=E, final_norm=g, n_ctx=16, max_rows=n_rows)
     xd = dev(x)
-    ids = torch.zeros(3, dtype=torch.int32, device="cuda")
-    logits = torch.zeros(3, sh.vocab, dtype=torch.float32, device="cuda")
-    nx = torch.zeros(3, sh.hidden, dtype=torch.float32, device="cuda")
-    pos = torch.tensor([5, 6, 7], dtype=torch.int32, device="cuda")
+    ids = torch.zeros(n_rows, dtype=torch.int32, device="cuda")
+    logits = torch.zeros(n_rows, sh.vocab, dtype=torch.float32, device="cuda")
+    nx = torch.zeros(n_rows, sh.hidden, dtype=torch.float32, device="cuda")
+    pos0 = np.arange(5, 5 + n_rows, dtype=np.int32)
+    pos = dev(pos0)
+    want_logits = O.final_logits(x, synth.widen(g), synth.widen(E), sh.rms_eps)
     for rep in range(3):        # slots and counters must re-arm themselves between calls
         sess.head(xd, ids, logits=logits, next_x=nx, pos=pos)
         torch.cuda.synchronize()
         got = ids.cpu().numpy()
-        want_logits = O.final_logits(x, synth.widen(g), synth.widen(E), sh.rms_eps)
         check(logits.cpu().numpy(), want_logits, False, "logits")
         assert got[0] == 17, got
         assert got[1] == 4999, got
-        assert got[2] == O.greedy_token(want_logits[2]) or O.top2_margin(want_logits[2]) <= MARGIN
+        for b in range(2, n_rows):
+            assert got[b] == O.greedy_token(want_logits[b]) or O.top2_margin(want_logits[b]) <= MARGIN, b
         np.testing.assert_array_equal(nx.cpu().numpy(), synth.widen(E)[got])
-        assert pos.cpu().numpy().tolist() == [6 + rep, 7 + rep, 8 + rep]
+        assert pos.cpu().numpy().tolist() == (pos0 + 1 + rep).tolist()
     sess.close()
 
 
