@@ -439,159 +439,213 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
     return rows_dispatch_kv<BF16, false>(a, R, s);
 }
 
-// ------------------------------------------------------------------ causal flash prefill (MFMA, f16 cache)
-// Grid (query tile of 64 rows, query head). Each wave owns 16 query rows; the
-// workgroup walks the cache in blocks of 64 keys up to the tile's last
-// position. Per block: K [64 x D] and V transposed [D x 64] are staged in LDS;
-// S = Q K^T with v_mfma_f32_16x16x32_f16 (Q fragments live in registers);
-// online softmax per row (row max and sum across the 16 lanes sharing the
-// row's 4-lane slot); P (f16) goes through a per-wave LDS tile into the A
-// layout; O += P V with the same MFMA. Output rows are rounded to bf16 for the
-// O-projection GEMM.
+// ------------------------------------------------------------------ causal prefill (MFMA flash)
+// A workgroup takes the query tiles of 128 rows of one head in pairs, tile i
+// and tile n - 1 - i, so every workgroup has the same causal work; each of its
+// 4 waves owns 32 rows (two 16-row fragments). Per block of 64 cache rows:
+//   S^T = K Q^T     A: K rows staged in LDS; B: the wave's Q rows, in registers
+//   online softmax; a lane owns one query row of each fragment
+//   O^T += V^T P^T  A: V^T staged in LDS; B: P^T straight from the S^T registers
+// Working on the transposes keeps every per-row quantity (max, sum, the O
+// rescale) in the lanes that own the row. The S^T fragment gives lane l the
+// keys 4g .. 4g + 3 (g = l / 16) of each 16-key tile, so V^T is staged with
+// the keys of each 32-key group permuted to match the B operand: position
+// 8g + j holds key 4g + j (j < 4) or 16 + 4g + j - 4 (j >= 4). K and V^T are
+// double-buffered in LDS; the next block's rows load while the current one
+// computes. Exponentials in base 2 on scores scaled by log2(e) / sqrt(d).
 template <int D>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __restrict__ q16, int64_t ldq, int T,
                                                            int pos0, int seq, int n_heads, KVLayer kv,
                                                            uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo,
                                                            int64_t ldo, uint64_t* clk) {
-    clock_begin(clk);
-    constexpr int KB = 64;                 // keys per block
-    constexpr int KS = D + 8;              // K row stride in LDS (f16)
-    constexpr int VS = KB + 8;             // V^T row stride in LDS
-    constexpr int PS = KB + 8;             // P row stride
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
-    __shared__ __attribute__((aligned(16))) uint16_t Ps[4][16 * PS];
+    constexpr int KB = 64, TQ = 128;
+    constexpr int KS = D + 8, VS = KB + 8;
+    constexpr int KSTEPS = D / 32, DF = D / 16;
+    constexpr int VECS = KB * D / 8 / 256;  // 16-byte vectors per thread per block, for K and for V
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KB * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VS];
 
-    const int tile = gridDim.x - 1 - blockIdx.x;  // heavy (late) tiles first
+    clock_begin(clk);
+    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
+    const int g4 = lane / 16, r16 = lane % 16;
     const int h = blockIdx.y;
     const int j = h / (n_heads / kv.n_kv);
-    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
-    const int t0 = tile * 64 + wave * 16;         // this wave's first row
+    const int n_tiles = (T + TQ - 1) / TQ;
     const int64_t slab = ((int64_t)seq * kv.n_kv + j) * kv.n_ctx * D;
     const uint16_t* Kg = (const uint16_t*)kv.k + slab;
     const uint16_t* Vg = (const uint16_t*)kv.v + slab;
-
-    // Q fragments: row t0 + lane%16, K elements ks*32 + (lane/16)*8 ..
-    f16x8 qf[D / 32];
-    {
-        const int t = t0 + lane % 16;
-        const bool ok = t < T;
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-            const uint16_t* src = q16 + (int64_t)(ok ? t : 0) * ldq + h * D + ks * 32 + (lane / 16) * 8;
-            u32x4 u = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
-            qf[ks] = __builtin_bit_cast(f16x8, u);
-        }
-    }
     const float sl2 = 1.4426950408889634f / sqrtf((float)D);
-    float m_i[4], l_i[4];
-    f32x4 o[D / 16];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        m_i[rr] = -INFINITY;
-        l_i[rr] = 0.f;
-    }
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int tile_last = min(tile * 64 + 63, T - 1);
-    const int n_keys = pos0 + tile_last + 1;       // keys any row of the tile can see
-    const int n_blocks = (n_keys + KB - 1) / KB;
-    for (int kb = 0; kb < n_blocks; ++kb) {
-        const int c0 = kb * KB;
+    for (int pass = 0; pass < 2; ++pass) {
+        const int tile = pass == 0 ? (int)blockIdx.x : n_tiles - 1 - (int)blockIdx.x;
+        if (pass == 1 && tile <= (int)blockIdx.x) break;  // an odd count leaves the middle tile single
+        __syncthreads();                                  // the LDS buffers are free again
+        const int t0 = tile * TQ + wave * 32;             // this wave's first query row
+
+        // Q^T fragments (B operand): query row t0 + 16 rf + r16, dims 32 ks + 8 g4 ..
+        f16x8 qf[2][KSTEPS];
+#pragma unroll
+        for (int rf = 0; rf < 2; ++rf) {
+            const int t = t0 + rf * 16 + r16;
+            const uint16_t* src = q16 + (int64_t)(t < T ? t : T - 1) * ldq + h * D + g4 * 8;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const f16x8 q = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(src + ks * 32));
+#pragma unroll
+                for (int i = 0; i < 8; ++i) qf[rf][ks][i] = (_Float16)((float)q[i] * sl2);  // scores come out scaled
+            }
+        }
+        f32x4 o[DF][2];
+#pragma unroll
+        for (int df = 0; df < DF; ++df) o[df][0] = o[df][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+
+        const int tile_last = min(tile * TQ + TQ - 1, T - 1);
+        const int n_keys = pos0 + tile_last + 1;  // keys any row of the tile can see
+        const int n_blocks = (n_keys + KB - 1) / KB;
+
+        // staging: K as 16-byte row pieces; V as pairs of keys (2c, 2c + 1) over one
+        // 8-dim chunk, written to V^T as 32-bit words (the permutation keeps the
+        // pair adjacent)
+        u32x4 kreg[VECS], vreg[VECS];
+        auto fetch = [&](int kb) {
+#pragma unroll
+            for (int i = 0; i < VECS; ++i) {
+                const int v = tid + i * 256;
+                const int ck = kb * KB + v / (D / 8), ek = (v % (D / 8)) * 8;
+                kreg[i] = ck < n_keys ? *reinterpret_cast<const u32x4*>(Kg + (int64_t)ck * D + ek)
+                                      : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int i = 0; i < VECS / 2; ++i) {
+                const int v = tid + i * 256;
+                const int cv = kb * KB + 2 * (v % (KB / 2)), ev = (v / (KB / 2)) * 8;
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    vreg[2 * i + u] = cv + u < n_keys
+                                          ? *reinterpret_cast<const u32x4*>(Vg + (int64_t)(cv + u) * D + ev)
+                                          : u32x4{0u, 0u, 0u, 0u};
+            }
+        };
+        auto stash = [&](int buf) {
+#pragma unroll
+            for (int i = 0; i < VECS; ++i) {
+                const int v = tid + i * 256;
+                *reinterpret_cast<u32x4*>(&Ks[buf][(v / (D / 8)) * KS + (v % (D / 8)) * 8]) = kreg[i];
+            }
+#pragma unroll
+            for (int i = 0; i < VECS / 2; ++i) {
+                const int v = tid + i * 256;
+                const int c = 2 * (v % (KB / 2)), e = (v / (KB / 2)) * 8, kk = c % 32;
+                const int pp = kk < 16 ? 8 * (kk / 4) + kk % 4 : 8 * ((kk - 16) / 4) + 4 + (kk - 16) % 4;
+                uint32_t* col = reinterpret_cast<uint32_t*>(&Vt[buf][e * VS + (c / 32) * 32 + pp]);
+                const u32x4 a = vreg[2 * i], b = vreg[2 * i + 1];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const uint32_t lo16 = (a[jj / 2] >> (16 * (jj % 2))) & 0xFFFFu;
+                    const uint32_t hi16 = (b[jj / 2] >> (16 * (jj % 2))) & 0xFFFFu;
+                    col[jj * (VS / 2)] = lo16 | (hi16 << 16);
+                }
+            }
+        };
+        fetch(0);
+        stash(0);
+        if (n_blocks > 1) fetch(1);
         __syncthreads();
-        // stage K rows and V^T (rows beyond n_keys are zero; they are masked anyway)
-        for (int v = tid; v < KB * D / 8; v += 256) {
-            const int c = v / (D / 8), e = (v % (D / 8)) * 8;
-            u32x4 ku = u32x4{0u, 0u, 0u, 0u}, vu = u32x4{0u, 0u, 0u, 0u};
-            if (c0 + c < n_keys) {
-                ku = *reinterpret_cast<const u32x4*>(Kg + (int64_t)(c0 + c) * D + e);
-                vu = *reinterpret_cast<const u32x4*>(Vg + (int64_t)(c0 + c) * D + e);
-            }
-            *reinterpret_cast<u32x4*>(&Ks[c * KS + e]) = ku;
+        for (int kb = 0; kb < n_blocks; ++kb) {
+            const int buf = kb & 1, c0 = kb * KB;
+            // S^T: lane holds query row r16 of fragment rf, keys 16 kf + 4 g4 + i
+            f32x4 sc[4][2];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) Vt[(e + i) * VS + c] = (uint16_t)(vu[i / 2] >> (16 * (i % 2)));
+            for (int kf = 0; kf < 4; ++kf) {
+                sc[kf][0] = sc[kf][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks) {
+                    const f16x8 kfr =
+                        *reinterpret_cast<const f16x8*>(&Ks[buf][(kf * 16 + r16) * KS + ks * 32 + g4 * 8]);
+#pragma unroll
+                    for (int rf = 0; rf < 2; ++rf)
+                        sc[kf][rf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kfr, qf[rf][ks], sc[kf][rf], 0, 0, 0);
+                }
+            }
+            // online softmax; P^T packed as the B fragments of the two 32-key steps
+            f16x8 pb[2][2];
+            const bool diag = c0 + KB - 1 > pos0 + t0;  // some key of the block lies past some row of the wave
+#pragma unroll
+            for (int rf = 0; rf < 2; ++rf) {
+                const int t_abs = pos0 + t0 + rf * 16 + r16;  // last key this query row sees
+                float mx = -INFINITY;
+                if (diag) {
+#pragma unroll
+                    for (int kf = 0; kf < 4; ++kf)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (c0 + kf * 16 + g4 * 4 + i > t_abs) sc[kf][rf][i] = -INFINITY;
+                }
+#pragma unroll
+                for (int kf = 0; kf < 4; ++kf)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kf][rf][i]);
+                mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+                const float mn = fmaxf(m[rf], mx);
+                const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[rf] - mn);
+                float sum = 0.f;
+#pragma unroll
+                for (int kf = 0; kf < 4; ++kf)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float e = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[kf][rf][i] - mn);
+                        sc[kf][rf][i] = e;
+                        sum += e;
+                    }
+                l[rf] = l[rf] * alpha + sum;
+                m[rf] = mn;
+#pragma unroll
+                for (int df = 0; df < DF; ++df) o[df][rf] *= alpha;
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        pb[rf][k2][i] = (_Float16)sc[2 * k2][rf][i];
+                        pb[rf][k2][4 + i] = (_Float16)sc[2 * k2 + 1][rf][i];
+                    }
+            }
+            // O^T += V^T P^T
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                for (int df = 0; df < DF; ++df) {
+                    const f16x8 vfr = *reinterpret_cast<const f16x8*>(&Vt[buf][(df * 16 + r16) * VS + k2 * 32 + g4 * 8]);
+#pragma unroll
+                    for (int rf = 0; rf < 2; ++rf)
+                        o[df][rf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vfr, pb[rf][k2], o[df][rf], 0, 0, 0);
+                }
+            if (kb + 1 < n_blocks) {
+                stash(buf ^ 1);  // that buffer was last read before the previous barrier
+                if (kb + 2 < n_blocks) fetch(kb + 2);
+            }
+            __syncthreads();
         }
-        __syncthreads();
-        // S = Q K^T for 4 key tiles of 16
-        f32x4 s[4];
+        // finish: the row sum is spread over the 4 lane groups sharing r16
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            s[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rf = 0; rf < 2; ++rf) {
+            float lsum = l[rf];
+            lsum += __shfl_xor(lsum, 16, WAVE);
+            lsum += __shfl_xor(lsum, 32, WAVE);
+            const int t = t0 + rf * 16 + r16;
+            if (t >= T) continue;
+            const float inv = 1.0f / lsum;
 #pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks) {
-                const f16x8 kf =
-                    *reinterpret_cast<const f16x8*>(&Ks[(nt * 16 + lane % 16) * KS + ks * 32 + (lane / 16) * 8]);
-                s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], kf, s[nt], 0, 0, 0);
-            }
-        }
-        // mask, online softmax; lane holds rows (lane/16)*4 + rr, keys nt*16 + lane%16
-        float p[4][4];
+            for (int df = 0; df < DF; ++df)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int t = t0 + (lane / 16) * 4 + rr;
-            const int pmax = pos0 + t;  // last visible key of this row
-            float mx = -INFINITY;
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int c = c0 + nt * 16 + lane % 16;
-                float v = s[nt][rr] * sl2;
-                if (c > pmax) v = -INFINITY;
-                p[nt][rr] = v;
-                mx = fmaxf(mx, v);
-            }
-#pragma unroll
-            for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, WAVE));
-            const float mn = fmaxf(m_i[rr], mx);
-            const float alpha = mn == -INFINITY ? 1.f : exp2f(m_i[rr] - mn);
-            float rs = 0.f;
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const float e = mn == -INFINITY ? 0.f : exp2f(p[nt][rr] - mn);
-                p[nt][rr] = e;
-                rs += e;
-            }
-            l_i[rr] = l_i[rr] * alpha + rs;
-            m_i[rr] = mn;
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) o[dt][rr] *= alpha;
-        }
-        // P -> LDS (row-major [16][64]) -> A fragments
-        uint16_t* P = Ps[wave];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-                P[((lane / 16) * 4 + rr) * PS + nt * 16 + lane % 16] = f32_to_f16_bits(p[nt][rr]);
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): LDS writes done before the reads below
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int ks = 0; ks < KB / 32; ++ks) {
-            const f16x8 pf = *reinterpret_cast<const f16x8*>(&P[(lane % 16) * PS + ks * 32 + (lane / 16) * 8]);
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) {
-                const f16x8 vf =
-                    *reinterpret_cast<const f16x8*>(&Vt[(dt * 16 + lane % 16) * VS + ks * 32 + (lane / 16) * 8]);
-                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, vf, o[dt], 0, 0, 0);
-            }
-        }
-    }
-    // finish rows: the row sum is spread over the 16 lanes sharing (lane/16)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        float lsum = l_i[rr];
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, WAVE);
-        const int t = t0 + (lane / 16) * 4 + rr;
-        if (t >= T) continue;
-        const float inv = 1.0f / lsum;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-            uint16_t hi, lo;
-            split_bf16(o[dt][rr] * inv, hi, lo);
-            const int64_t idx = (int64_t)t * ldo + h * D + dt * 16 + lane % 16;
-            out[idx] = hi;
-            if (out_lo) out_lo[idx] = lo;
+                for (int i = 0; i < 4; ++i) {
+                    uint16_t hi, lo;
+                    split_bf16(o[df][rf][i] * inv, hi, lo);
+                    const int64_t idx = (int64_t)t * ldo + h * D + df * 16 + g4 * 4 + i;
+                    out[idx] = hi;
+                    if (out_lo) out_lo[idx] = lo;
+                }
         }
     }
     clock_end(clk);
@@ -600,7 +654,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
 hipError_t launch_attn_prefill(const uint16_t* q16, int64_t ldq, int T, int pos0, int seq, int n_heads, KVLayer kv,
                                uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo, hipStream_t s) {
     if (T <= 0) return hipSuccess;
-    dim3 grid((T + 63) / 64, n_heads);
+    const int n_tiles = (T + 127) / 128;
+    dim3 grid((n_tiles + 1) / 2, n_heads);
     if (kv.d == 128)
         attn_prefill_kernel<128><<<grid, 256, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, clock_slot());
     else if (kv.d == 64)

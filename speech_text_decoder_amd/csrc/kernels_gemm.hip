@@ -419,7 +419,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
         for (int f = 0; f < CF; ++f) acc[r][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     u32x4 wb[PD][CF], ab[PD][RF], alb[PD][RF];
-    auto load = [&](int s) {  // batch of PD steps from step s (clamped reads past s1 are not used)
+    for (int s = s0; s < s1; s += PD) {
+        // a batch of PD steps (clamped reads past s1 are loaded but not used)
 #pragma unroll
         for (int p = 0; p < PD; ++p) {
             const int k = min(s + p, n_steps - 1) * 32 + koff;
@@ -431,9 +432,6 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
                 if (lo) alb[p][r] = *reinterpret_cast<const u32x4*>(alrow[r] + k);
             }
         }
-    };
-    for (int s = s0; s < s1; s += PD) {
-        load(s);
 #pragma unroll
         for (int p = 0; p < PD; ++p) {
             if (s + p >= s1) break;
