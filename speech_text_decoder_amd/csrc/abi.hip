@@ -127,6 +127,7 @@ class ProfScope {
 constexpr int kGemvMaxRows = 4;    // rows beyond this take the MFMA GEMMs (bf16 weights)
 constexpr int kSplitMaxRows = 512; // up to here the GEMMs are HBM-bound: split activations (hi + lo)
 constexpr int kMaxSplits = 64;
+constexpr int kMergeMaxSplits = 8;  // up to here the O-projection GEMV merges attention splits itself
 constexpr int kHeadPartials = 1024;  // workgroups of the persistent head GEMV
 
 sttd_status from_hip(hipError_t e) {
@@ -253,13 +254,17 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
         TRY(launch_qk_norm_rope_kv(ws->qkv, qkv_cols, R, wt, qr, s));
     }
     int splits = 1;
+    bool defer = false;
     if (flash) {
         ProfScope ps(STTD_KERN_ATTN_PREFILL, s);
         TRY(launch_attn_prefill((const uint16_t*)ws->qbuf, qd, R, rm.pos0, rm.seq0, nq, kl, ao, ao_lo, qd, s));
     } else {
         splits = choose_splits(R, nkv, pos_bound, ws->part_cap);
         // GEMV path: a split result stays as partials and the O projection merges them on load
-        const bool defer = !mfma && splits > 1;
+        // GEMV path with a few splits: the O projection merges the partials as it loads
+        // them (every one of its workgroups re-reads them all); with many, one combine
+        // pass is cheaper
+        defer = !mfma && splits > 1 && splits <= kMergeMaxSplits;
         ProfScope ps(STTD_KERN_ATTN_ROWS, s);
         TRY(launch_attn_rows(prefill ? (const float*)ws->qbuf : ws->qkv, prefill ? qd : qkv_cols, R, nq, rm, kl,
                              splits, ws->part, mfma || defer ? nullptr : ws->attn_o, mfma ? ao : nullptr,
@@ -277,7 +282,7 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
         GemvArgs a{};
         a.w[0] = w->wo; a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = H;
         a.N = H; a.K = qd; a.x = ws->attn_o; a.ldx = qd; a.rows = R; a.y = x; a.ldy = H; a.resid = x; a.ldr = H;
-        if (splits > 1) {
+        if (defer) {
             a.xpart = ws->part; a.n_splits = splits; a.head_dim = d;
         }
         ProfScope ps(STTD_KERN_O_GEMV, s);

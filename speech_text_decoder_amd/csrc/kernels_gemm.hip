@@ -301,10 +301,13 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, int tiles_
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < nk) {
-            stash(buf ^ 1);  // the other buffer was last read before the previous barrier
-            if (kt + 2 < nk) fetch((int64_t)(kt + 2) * BIG_BK);
+            // between the two K-steps: stage the next tile (the other buffer was last read
+            // before the previous barrier) and start loading the one after, so the LDS
+            // writes and the global loads overlap the second step's MFMAs
+            if (ks == 0 && kt + 1 < nk) {
+                stash(buf ^ 1);
+                if (kt + 2 < nk) fetch((int64_t)(kt + 2) * BIG_BK);
+            }
         }
         __syncthreads();
     }
