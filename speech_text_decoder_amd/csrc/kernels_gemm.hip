@@ -192,11 +192,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 
 // ------------------------------------------------------------------ large-M tiles
 // For prefills of many rows (the GEMMs are MFMA-bound there): 256 x 256 output
-// tiles, 4 waves in 2 x 2 each owning 128 x 128 (8 x 8 fragments of
-// v_mfma_f32_16x16x32_bf16, accumulators in the AGPR half of the register
-// file), K in steps of 64 through two LDS buffers so one barrier per step
-// separates staging from use. Per wave and 32-deep step the fragments cost
-// 16 KB of LDS reads for 64 MFMAs, half of what LDS delivers in that time.
+// tiles, 8 waves in 4 x 2 each owning 64 x 128 (4 x 8 fragments of
+// v_mfma_f32_16x16x32_bf16), two waves per SIMD so one issues MFMAs while the
+// other waits; K in steps of 64 through two LDS buffers so one barrier per
+// step separates staging from use. Per SIMD and 32-deep step the fragments
+// cost 24 KB of LDS reads for 64 MFMAs, about three quarters of what LDS
+// delivers in that time.
 //
 // Tiles are handed out XCD-aware: workgroup i runs on XCD i % 8, so the tile
 // index is remapped to give each XCD a contiguous run of tiles with the row
@@ -209,16 +210,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 // and up (fragments 4..7) of the same columns in its own accumulators.
 constexpr int BIG_BM = 256, BIG_BN = 256, BIG_BK = 64, BIG_STR = BIG_BK + 8;
 
-template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, int tiles_m, int tiles_n) {
-    constexpr int FM = 8, FN = 8;
-    constexpr int VECS = BIG_BM * BIG_BK / 8 / 256;  // 16-byte vectors per thread per operand and step
+template <int EPI, int BN>
+__global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+    static_assert(EPI != GEMM_SWIGLU || BN == BIG_BN, "SwiGLU pairs gate and up inside 256-row weight tiles");
+    constexpr int FM = 4, FN = BN / 32;
+    constexpr int VECS = BIG_BM * BIG_BK / 8 / 512;  // 16-byte vectors per thread and step: A
+    constexpr int BVECS = BN * BIG_BK / 8 / 512;     // and B
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BIG_BM * BIG_STR];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BIG_BN * BIG_STR];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BIG_STR];
 
     clock_begin(g.clk);
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / 2, wn = wave % 2;  // 4 x 2 waves, each 64 x 128
     // XCD-aware tile order when the tile count splits evenly over the 8 XCDs
     const int n_tiles = tiles_m * tiles_n;
     const int id = blockIdx.x;
@@ -227,14 +230,19 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, int tiles_
     const int m0 = tile_m * BIG_BM;
 
     const uint16_t* aptr[VECS];
-    const uint16_t* bptr[VECS];
-    bool bok[VECS];
+    const uint16_t* bptr[BVECS];
+    bool bok[BVECS];
 #pragma unroll
     for (int i = 0; i < VECS; ++i) {
-        const int v = tid + i * 256;
+        const int v = tid + i * 512;
         const int r = v / (BIG_BK / 8), ck = (v % (BIG_BK / 8)) * 8;
         const int am = m0 + r < g.M ? m0 + r : 0;
         aptr[i] = g.A + (int64_t)am * g.lda + ck;
+    }
+#pragma unroll
+    for (int i = 0; i < BVECS; ++i) {
+        const int v = tid + i * 512;
+        const int r = v / (BIG_BK / 8), ck = (v % (BIG_BK / 8)) * 8;
         int grow;
         const uint16_t* W;
         bok[i] = true;
@@ -244,7 +252,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, int tiles_
             grow = within < 64 ? c : g.N + c;
             W = g.w[0];
         } else {
-            const int n0 = tile_n * BIG_BN + r;
+            const int n0 = tile_n * BN + r;
             bok[i] = n0 < g.N;
             const int n = bok[i] ? n0 : 0;
             const bool s2 = n >= g.seg_end[1], s1 = n >= g.seg_end[0];
@@ -253,21 +261,21 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, int tiles_
         }
         bptr[i] = W + (int64_t)grow * g.K + ck;
     }
-    u32x4 areg[VECS], breg[VECS];
+    u32x4 areg[VECS], breg[BVECS];
     auto fetch = [&](int64_t k0) {
 #pragma unroll
         for (int i = 0; i < VECS; ++i) areg[i] = *reinterpret_cast<const u32x4*>(aptr[i] + k0);
 #pragma unroll
-        for (int i = 0; i < VECS; ++i)
+        for (int i = 0; i < BVECS; ++i)
             breg[i] = bok[i] ? *reinterpret_cast<const u32x4*>(bptr[i] + k0) : u32x4{0u, 0u, 0u, 0u};
     };
     auto stash = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < VECS; ++i) {
-            const int v = tid + i * 256;
+            const int v = tid + i * 512;
             const int o = (v / (BIG_BK / 8)) * BIG_STR + (v % (BIG_BK / 8)) * 8;
             *reinterpret_cast<u32x4*>(&As[buf][o]) = areg[i];
-            *reinterpret_cast<u32x4*>(&Bs[buf][o]) = breg[i];
+            if (i < BVECS) *reinterpret_cast<u32x4*>(&Bs[buf][o]) = breg[i < BVECS ? i : 0];
         }
     };
 
@@ -292,10 +300,10 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, int tiles_
             bf16x8 af[FM], bfr[FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(&Ab[(wm * 128 + i * 16 + lane % 16) * BIG_STR + kc]);
+                af[i] = *reinterpret_cast<const bf16x8*>(&Ab[(wm * 64 + i * 16 + lane % 16) * BIG_STR + kc]);
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(&Bb[(wn * 128 + j * 16 + lane % 16) * BIG_STR + kc]);
+                bfr[j] = *reinterpret_cast<const bf16x8*>(&Bb[(wn * (BN / 2) + j * 16 + lane % 16) * BIG_STR + kc]);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -317,7 +325,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, int tiles_
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-            const int m = m0 + wm * 128 + i * 16 + (lane / 16) * 4 + rr;
+            const int m = m0 + wm * 64 + i * 16 + (lane / 16) * 4 + rr;
             if (m >= g.M) continue;
             if (EPI == GEMM_SWIGLU) {
 #pragma unroll
@@ -333,7 +341,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, int tiles_
             } else {
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    const int n = tile_n * BIG_BN + wn * 128 + j * 16 + lane % 16;
+                    const int n = tile_n * BN + wn * (BN / 2) + j * 16 + lane % 16;
                     if (n >= g.N) continue;
                     float* dst = g.C + (int64_t)m * g.ldc + n;
                     if (EPI == GEMM_RESID) *dst += acc[i][j][rr];
@@ -348,20 +356,29 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, int tiles_
 // Whether the large tiles apply: many rows, no split activations, shapes that tile.
 static bool big_tiles_fit(const GemmArgs& g, GemmEpi epi) {
     if (g.A_lo || g.M < 1024 || g.K % BIG_BK) return false;
-    const int tiles_m = (g.M + BIG_BM - 1) / BIG_BM;
-    const int tiles_n = epi == GEMM_SWIGLU ? g.N / 128 : (g.N + BIG_BN - 1) / BIG_BN;
-    return tiles_m > 0 && tiles_n > 0 && !(epi == GEMM_SWIGLU && g.N % 128);
+    return !(epi == GEMM_SWIGLU && g.N % 128);
 }
 
 static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     const int tiles_m = (g.M + BIG_BM - 1) / BIG_BM;
-    const int tiles_n = epi == GEMM_SWIGLU ? g.N / 128 : (g.N + BIG_BN - 1) / BIG_BN;
-    const dim3 grid(tiles_m * tiles_n);
-    if (epi == GEMM_SWIGLU) gemm_big_kernel<GEMM_SWIGLU><<<grid, 256, 0, s>>>(g, tiles_m, tiles_n);
-    else if (epi == GEMM_RESID) gemm_big_kernel<GEMM_RESID><<<grid, 256, 0, s>>>(g, tiles_m, tiles_n);
-    else gemm_big_kernel<GEMM_STORE><<<grid, 256, 0, s>>>(g, tiles_m, tiles_n);
+    if (epi == GEMM_SWIGLU) {
+        const int tiles_n = g.N / 128;
+        gemm_big_kernel<GEMM_SWIGLU, BIG_BN><<<tiles_m * tiles_n, 512, 0, s>>>(g, tiles_m, tiles_n);
+        return;
+    }
+    // narrow outputs: 128-column tiles so that about a full wave of workgroups runs
+    const bool narrow = tiles_m * ((g.N + BIG_BN - 1) / BIG_BN) < 256;
+    const int bn = narrow ? 128 : BIG_BN;
+    const int tiles_n = (g.N + bn - 1) / bn;
+    const int grid = tiles_m * tiles_n;
+    if (epi == GEMM_RESID) {
+        if (narrow) gemm_big_kernel<GEMM_RESID, 128><<<grid, 512, 0, s>>>(g, tiles_m, tiles_n);
+        else gemm_big_kernel<GEMM_RESID, BIG_BN><<<grid, 512, 0, s>>>(g, tiles_m, tiles_n);
+    } else {
+        if (narrow) gemm_big_kernel<GEMM_STORE, 128><<<grid, 512, 0, s>>>(g, tiles_m, tiles_n);
+        else gemm_big_kernel<GEMM_STORE, BIG_BN><<<grid, 512, 0, s>>>(g, tiles_m, tiles_n);
+    }
 }
-
 
 // ------------------------------------------------------------------ few rows (decode batches)
 // C[R, N] (+)= A[R, K] W[N, K]^T for R <= 16 RF rows: weight-stationary MFMA.
