@@ -442,7 +442,7 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
 // ------------------------------------------------------------------ causal prefill (MFMA flash)
 // A workgroup takes the query tiles of 128 rows of one head in pairs, tile i
 // and tile n - 1 - i, so every workgroup has the same causal work; each of its
-// 4 waves owns 32 rows (two 16-row fragments). Per block of 64 cache rows:
+// 8 waves owns 16 rows, two waves per SIMD. Per block of 64 cache rows:
 //   S^T = K Q^T     A: K rows staged in LDS; B: the wave's Q rows, in registers
 //   online softmax; a lane owns one query row of each fragment
 //   O^T += V^T P^T  A: V^T staged in LDS; B: P^T straight from the S^T registers
@@ -454,14 +454,18 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
 // double-buffered in LDS; the next block's rows load while the current one
 // computes. Exponentials in base 2 on scores scaled by log2(e) / sqrt(d).
 template <int D>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __restrict__ q16, int64_t ldq, int T,
+__global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __restrict__ q16, int64_t ldq, int T,
                                                            int pos0, int seq, int n_heads, KVLayer kv,
                                                            uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo,
                                                            int64_t ldo, uint64_t* clk) {
-    constexpr int KB = 64, TQ = 128;
+    constexpr int NT = 512;                // 8 waves, 16 query rows each
+    constexpr int RF = 1;                  // 16-row fragments per wave
+    constexpr int KB = 64, TQ = 8 * 16 * RF;
     constexpr int KS = D + 8, VS = KB + 8;
     constexpr int KSTEPS = D / 32, DF = D / 16;
-    constexpr int VECS = KB * D / 8 / 256;  // 16-byte vectors per thread per block, for K and for V
+    constexpr int KVECS = KB * D / 8 / NT;                  // 16-byte K pieces per thread per block
+    constexpr int VITEMS = (KB / 2) * (D / 8);              // (key pair, 8-dim chunk) items of V per block
+    constexpr int VPAIRS = (VITEMS + NT - 1) / NT;          // per thread
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KB * KS];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VS];
 
@@ -480,12 +484,12 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
         const int tile = pass == 0 ? (int)blockIdx.x : n_tiles - 1 - (int)blockIdx.x;
         if (pass == 1 && tile <= (int)blockIdx.x) break;  // an odd count leaves the middle tile single
         __syncthreads();                                  // the LDS buffers are free again
-        const int t0 = tile * TQ + wave * 32;             // this wave's first query row
+        const int t0 = tile * TQ + wave * 16 * RF;        // this wave's first query row
 
         // Q^T fragments (B operand): query row t0 + 16 rf + r16, dims 32 ks + 8 g4 ..
-        f16x8 qf[2][KSTEPS];
+        f16x8 qf[RF][KSTEPS];
 #pragma unroll
-        for (int rf = 0; rf < 2; ++rf) {
+        for (int rf = 0; rf < RF; ++rf) {
             const int t = t0 + rf * 16 + r16;
             const uint16_t* src = q16 + (int64_t)(t < T ? t : T - 1) * ldq + h * D + g4 * 8;
 #pragma unroll
@@ -495,10 +499,15 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
                 for (int i = 0; i < 8; ++i) qf[rf][ks][i] = (_Float16)((float)q[i] * sl2);  // scores come out scaled
             }
         }
-        f32x4 o[DF][2];
+        f32x4 o[DF][RF];
+        float m[RF], l[RF];
 #pragma unroll
-        for (int df = 0; df < DF; ++df) o[df][0] = o[df][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+        for (int rf = 0; rf < RF; ++rf) {
+            m[rf] = -INFINITY;
+            l[rf] = 0.f;
+#pragma unroll
+            for (int df = 0; df < DF; ++df) o[df][rf] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 
         const int tile_last = min(tile * TQ + TQ - 1, T - 1);
         const int n_keys = pos0 + tile_last + 1;  // keys any row of the tile can see
@@ -507,18 +516,18 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
         // staging: K as 16-byte row pieces; V as pairs of keys (2c, 2c + 1) over one
         // 8-dim chunk, written to V^T as 32-bit words (the permutation keeps the
         // pair adjacent)
-        u32x4 kreg[VECS], vreg[VECS];
+        u32x4 kreg[KVECS], vreg[2 * VPAIRS];
         auto fetch = [&](int kb) {
 #pragma unroll
-            for (int i = 0; i < VECS; ++i) {
-                const int v = tid + i * 256;
+            for (int i = 0; i < KVECS; ++i) {
+                const int v = tid + i * NT;
                 const int ck = kb * KB + v / (D / 8), ek = (v % (D / 8)) * 8;
                 kreg[i] = ck < n_keys ? *reinterpret_cast<const u32x4*>(Kg + (int64_t)ck * D + ek)
                                       : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
-            for (int i = 0; i < VECS / 2; ++i) {
-                const int v = tid + i * 256;
+            for (int i = 0; i < VPAIRS; ++i) {
+                const int v0 = tid + i * NT, v = v0 < VITEMS ? v0 : 0;
                 const int cv = kb * KB + 2 * (v % (KB / 2)), ev = (v / (KB / 2)) * 8;
 #pragma unroll
                 for (int u = 0; u < 2; ++u)
@@ -529,13 +538,14 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
         };
         auto stash = [&](int buf) {
 #pragma unroll
-            for (int i = 0; i < VECS; ++i) {
-                const int v = tid + i * 256;
+            for (int i = 0; i < KVECS; ++i) {
+                const int v = tid + i * NT;
                 *reinterpret_cast<u32x4*>(&Ks[buf][(v / (D / 8)) * KS + (v % (D / 8)) * 8]) = kreg[i];
             }
 #pragma unroll
-            for (int i = 0; i < VECS / 2; ++i) {
-                const int v = tid + i * 256;
+            for (int i = 0; i < VPAIRS; ++i) {
+                const int v = tid + i * NT;
+                if (v >= VITEMS) continue;
                 const int c = 2 * (v % (KB / 2)), e = (v / (KB / 2)) * 8, kk = c % 32;
                 const int pp = kk < 16 ? 8 * (kk / 4) + kk % 4 : 8 * ((kk - 16) / 4) + 4 + (kk - 16) % 4;
                 uint32_t* col = reinterpret_cast<uint32_t*>(&Vt[buf][e * VS + (c / 32) * 32 + pp]);
@@ -555,24 +565,25 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
         for (int kb = 0; kb < n_blocks; ++kb) {
             const int buf = kb & 1, c0 = kb * KB;
             // S^T: lane holds query row r16 of fragment rf, keys 16 kf + 4 g4 + i
-            f32x4 sc[4][2];
+            f32x4 sc[4][RF];
 #pragma unroll
             for (int kf = 0; kf < 4; ++kf) {
-                sc[kf][0] = sc[kf][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int rf = 0; rf < RF; ++rf) sc[kf][rf] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KSTEPS; ++ks) {
                     const f16x8 kfr =
                         *reinterpret_cast<const f16x8*>(&Ks[buf][(kf * 16 + r16) * KS + ks * 32 + g4 * 8]);
 #pragma unroll
-                    for (int rf = 0; rf < 2; ++rf)
+                    for (int rf = 0; rf < RF; ++rf)
                         sc[kf][rf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kfr, qf[rf][ks], sc[kf][rf], 0, 0, 0);
                 }
             }
             // online softmax; P^T packed as the B fragments of the two 32-key steps
-            f16x8 pb[2][2];
+            f16x8 pb[RF][2];
             const bool diag = c0 + KB - 1 > pos0 + t0;  // some key of the block lies past some row of the wave
 #pragma unroll
-            for (int rf = 0; rf < 2; ++rf) {
+            for (int rf = 0; rf < RF; ++rf) {
                 const int t_abs = pos0 + t0 + rf * 16 + r16;  // last key this query row sees
                 float mx = -INFINITY;
                 if (diag) {
@@ -618,7 +629,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
                 for (int df = 0; df < DF; ++df) {
                     const f16x8 vfr = *reinterpret_cast<const f16x8*>(&Vt[buf][(df * 16 + r16) * VS + k2 * 32 + g4 * 8]);
 #pragma unroll
-                    for (int rf = 0; rf < 2; ++rf)
+                    for (int rf = 0; rf < RF; ++rf)
                         o[df][rf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vfr, pb[rf][k2], o[df][rf], 0, 0, 0);
                 }
             if (kb + 1 < n_blocks) {
@@ -629,7 +640,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
         }
         // finish: the row sum is spread over the 4 lane groups sharing r16
 #pragma unroll
-        for (int rf = 0; rf < 2; ++rf) {
+        for (int rf = 0; rf < RF; ++rf) {
             float lsum = l[rf];
             lsum += __shfl_xor(lsum, 16, WAVE);
             lsum += __shfl_xor(lsum, 32, WAVE);
@@ -657,9 +668,9 @@ hipError_t launch_attn_prefill(const uint16_t* q16, int64_t ldq, int T, int pos0
     const int n_tiles = (T + 127) / 128;
     dim3 grid((n_tiles + 1) / 2, n_heads);
     if (kv.d == 128)
-        attn_prefill_kernel<128><<<grid, 256, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, clock_slot());
+        attn_prefill_kernel<128><<<grid, 512, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, clock_slot());
     else if (kv.d == 64)
-        attn_prefill_kernel<64><<<grid, 256, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, clock_slot());
+        attn_prefill_kernel<64><<<grid, 512, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, clock_slot());
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
