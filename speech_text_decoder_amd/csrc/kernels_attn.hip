@@ -441,7 +441,8 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
 
 // ------------------------------------------------------------------ causal prefill (MFMA flash)
 // A workgroup takes the query tiles of 128 rows of one head in pairs, tile i
-// and tile n - 1 - i, so every workgroup has the same causal work; each of its
+// and tile n - 1 - i, so every workgroup has the same causal work (when there
+// are enough tiles to fill the chip; otherwise one tile each); each of its
 // 8 waves owns 16 rows, two waves per SIMD. Per block of 64 cache rows:
 //   S^T = K Q^T     A: K rows staged in LDS; B: the wave's Q rows, in registers
 //   online softmax; a lane owns one query row of each fragment
@@ -457,7 +458,7 @@ template <int D>
 __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __restrict__ q16, int64_t ldq, int T,
                                                            int pos0, int seq, int n_heads, KVLayer kv,
                                                            uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo,
-                                                           int64_t ldo, uint64_t* clk) {
+                                                           int64_t ldo, int paired, uint64_t* clk) {
     constexpr int NT = 512;                // 8 waves, 16 query rows each
     constexpr int RF = 1;                  // 16-row fragments per wave
     constexpr int KB = 64, TQ = 8 * 16 * RF;
@@ -481,8 +482,10 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
     const float sl2 = 1.4426950408889634f / sqrtf((float)D);
 
     for (int pass = 0; pass < 2; ++pass) {
-        const int tile = pass == 0 ? (int)blockIdx.x : n_tiles - 1 - (int)blockIdx.x;
-        if (pass == 1 && tile <= (int)blockIdx.x) break;  // an odd count leaves the middle tile single
+        // paired: tiles x and n - 1 - x; otherwise one tile each, the heavy (late) ones first
+        const int tile = !paired ? n_tiles - 1 - (int)blockIdx.x
+                                 : (pass == 0 ? (int)blockIdx.x : n_tiles - 1 - (int)blockIdx.x);
+        if (pass == 1 && (!paired || tile <= (int)blockIdx.x)) break;  // an odd count leaves the middle tile single
         __syncthreads();                                  // the LDS buffers are free again
         const int t0 = tile * TQ + wave * 16 * RF;        // this wave's first query row
 
@@ -666,11 +669,13 @@ hipError_t launch_attn_prefill(const uint16_t* q16, int64_t ldq, int T, int pos0
                                uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     const int n_tiles = (T + 127) / 128;
-    dim3 grid((n_tiles + 1) / 2, n_heads);
+    // pairing evens out causal work once there are enough tiles to fill the chip
+    const int paired = n_tiles * n_heads >= 512;
+    dim3 grid(paired ? (n_tiles + 1) / 2 : n_tiles, n_heads);
     if (kv.d == 128)
-        attn_prefill_kernel<128><<<grid, 512, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, clock_slot());
+        attn_prefill_kernel<128><<<grid, 512, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, paired, clock_slot());
     else if (kv.d == 64)
-        attn_prefill_kernel<64><<<grid, 512, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, clock_slot());
+        attn_prefill_kernel<64><<<grid, 512, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, paired, clock_slot());
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

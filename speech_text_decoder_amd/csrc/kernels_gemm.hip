@@ -112,8 +112,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = g.K / BK;
+    // K range of this workgroup: split over gridDim.z (RESID only; partial sums add with atomics)
+    const int nk_all = g.K / BK;
+    const int nk_per = (nk_all + gridDim.z - 1) / gridDim.z;
+    const int kt0 = min((int)blockIdx.z * nk_per, nk_all);
+    const int nk = min(nk_per, nk_all - kt0);
+    const int64_t kbase = (int64_t)kt0 * BK;
     auto fetch = [&](int64_t k0) {
+        k0 += kbase;
         fetch_rows<A_VECS>(areg, arow_ptr, arow_ok, k0);
         if (SPLIT) fetch_rows<A_VECS>(alreg, alo_ptr, arow_ok, k0);
         fetch_rows<B_VECS>(breg, brow_ptr, brow_ok, k0);
@@ -123,7 +129,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
         if (SPLIT) stash_rows<A_VECS>(alreg, Als, tid);
         stash_rows<B_VECS>(breg, Bs, tid);
     };
-    fetch(0);
+    if (nk > 0) fetch(0);
     stash();
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
@@ -180,8 +186,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
                     const int n = tile_n * BN + wn * (BN / 2) + j * 16 + lane % 16;
                     if (n >= g.N) continue;
                     float* dst = g.C + (int64_t)m * g.ldc + n;
-                    if (EPI == GEMM_RESID) *dst += acc[i][j][rr];
-                    else *dst = acc[i][j][rr];
+                    if (EPI == GEMM_RESID) {
+                        if (gridDim.z == 1) *dst += acc[i][j][rr];
+                        else atomicAdd(dst, acc[i][j][rr]);
+                    } else {
+                        *dst = acc[i][j][rr];
+                    }
                 }
             }
         }
@@ -531,7 +541,10 @@ static void launch_gemm_skinny(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
 template <bool SPLIT>
 static void launch_gemm_t(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     constexpr int BM = 64, BN = 128;
-    dim3 grid(epi == GEMM_SWIGLU ? g.N / (BN / 2) : (g.N + BN - 1) / BN, (g.M + BM - 1) / BM);
+    dim3 grid(epi == GEMM_SWIGLU ? g.N / (BN / 2) : (g.N + BN - 1) / BN, (g.M + BM - 1) / BM, 1);
+    // RESID: split K over workgroups (atomic adds) while fewer than ~256 run and each keeps >= 4 K-steps
+    if (epi == GEMM_RESID)
+        while (grid.x * grid.y * grid.z * 2 <= 256 && g.K / BK >= (int)grid.z * 2 * 4) grid.z *= 2;
     if (epi == GEMM_SWIGLU) gemm_bf16_kernel<BM, BN, GEMM_SWIGLU, SPLIT><<<grid, 256, 0, s>>>(g);
     else if (epi == GEMM_RESID) gemm_bf16_kernel<BM, BN, GEMM_RESID, SPLIT><<<grid, 256, 0, s>>>(g);
     else gemm_bf16_kernel<BM, BN, GEMM_STORE, SPLIT><<<grid, 256, 0, s>>>(g);
