@@ -539,15 +539,32 @@ static void launch_gemm_skinny(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
 }
 
 template <bool SPLIT>
-static void launch_gemm_t(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
+static hipError_t launch_gemm_t(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     constexpr int BM = 64, BN = 128;
-    dim3 grid(epi == GEMM_SWIGLU ? g.N / (BN / 2) : (g.N + BN - 1) / BN, (g.M + BM - 1) / BM, 1);
-    // RESID: split K over workgroups (atomic adds) while fewer than ~256 run and each keeps >= 4 K-steps
-    if (epi == GEMM_RESID)
-        while (grid.x * grid.y * grid.z * 2 <= 256 && g.K / BK >= (int)grid.z * 2 * 4) grid.z *= 2;
-    if (epi == GEMM_SWIGLU) gemm_bf16_kernel<BM, BN, GEMM_SWIGLU, SPLIT><<<grid, 256, 0, s>>>(g);
-    else if (epi == GEMM_RESID) gemm_bf16_kernel<BM, BN, GEMM_RESID, SPLIT><<<grid, 256, 0, s>>>(g);
-    else gemm_bf16_kernel<BM, BN, GEMM_STORE, SPLIT><<<grid, 256, 0, s>>>(g);
+    const unsigned gy = (g.M + BM - 1) / BM;
+    if (epi == GEMM_SWIGLU) {
+        // 64-column tiles (32 act columns) when 128-column ones would leave CUs idle
+        if ((unsigned)(g.N / (BN / 2)) * gy < 512 && g.N % 32 == 0)
+            gemm_bf16_kernel<BM, 64, GEMM_SWIGLU, SPLIT><<<dim3(g.N / 32, gy, 1), 256, 0, s>>>(g);
+        else
+            gemm_bf16_kernel<BM, BN, GEMM_SWIGLU, SPLIT><<<dim3(g.N / (BN / 2), gy, 1), 256, 0, s>>>(g);
+        return hipSuccess;
+    }
+    dim3 grid((g.N + BN - 1) / BN, gy, 1);
+    // Few workgroups: split K over them (atomic adds into C, which a STORE zeroes first)
+    // while fewer than ~256 run and each keeps >= 4 K-steps
+    while (grid.x * grid.y * grid.z * 2 <= 256 && g.K / BK >= (int)grid.z * 2 * 4) grid.z *= 2;
+    if (epi == GEMM_STORE && grid.z > 1 && g.ldc != g.N) grid.z = 1;  // zeroing needs contiguous rows
+    if (epi == GEMM_STORE && grid.z > 1) {
+        const hipError_t e = launch_fill_zero(g.C, (size_t)g.M * g.N * sizeof(float), s);
+        if (e != hipSuccess) return e;
+        gemm_bf16_kernel<BM, BN, GEMM_RESID, SPLIT><<<grid, 256, 0, s>>>(g);
+    } else if (epi == GEMM_RESID) {
+        gemm_bf16_kernel<BM, BN, GEMM_RESID, SPLIT><<<grid, 256, 0, s>>>(g);
+    } else {
+        gemm_bf16_kernel<BM, BN, GEMM_STORE, SPLIT><<<grid, 256, 0, s>>>(g);
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_gemm(const GemmArgs& args, GemmEpi epi, hipStream_t s) {
@@ -556,8 +573,13 @@ hipError_t launch_gemm(const GemmArgs& args, GemmEpi epi, hipStream_t s) {
     g.clk = clock_slot();
     if (g.M <= kSkinnyMaxRows && g.K % 32 == 0) launch_gemm_skinny(g, epi, s);
     else if (big_tiles_fit(g, epi)) launch_gemm_big(g, epi, s);
-    else if (g.A_lo) launch_gemm_t<true>(g, epi, s);
-    else launch_gemm_t<false>(g, epi, s);
+    else if (g.A_lo) {
+        const hipError_t e = launch_gemm_t<true>(g, epi, s);
+        if (e != hipSuccess) return e;
+    } else {
+        const hipError_t e = launch_gemm_t<false>(g, epi, s);
+        if (e != hipSuccess) return e;
+    }
     return hipGetLastError();
 }
 
