@@ -127,7 +127,6 @@ class ProfScope {
 constexpr int kGemvMaxRows = 4;    // rows beyond this take the MFMA GEMMs (bf16 weights)
 constexpr int kSplitMaxRows = 512; // up to here the GEMMs are HBM-bound: split activations (hi + lo)
 constexpr int kMaxSplits = 64;
-constexpr int kMergeMaxSplits = 8;  // up to here the O-projection GEMV merges attention splits itself
 constexpr int kHeadPartials = 1024;  // workgroups of the persistent head GEMV
 
 sttd_status from_hip(hipError_t e) {

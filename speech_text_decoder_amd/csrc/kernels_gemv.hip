@@ -148,10 +148,13 @@ __device__ __forceinline__ void load_activations(const float* __restrict__ x, in
 }
 
 // Activation chunks merged from attention split partials (see GemvArgs::xpart):
-// one online pass over the splits per 8-element chunk (8 divides head_dim).
+// per 8-element chunk (8 divides head_dim) every split's (m, l, o[8]) is loaded
+// first, up to kMergeMaxSplits of them, so the loads overlap; then
+// o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M the largest m_s.
 template <int KCH, int BT>
 __device__ __forceinline__ void load_activations_merged(const GemvArgs& a, int b0, int nb, const int (&kk)[KCH],
                                                         float (&xv)[KCH][BT][8]) {
+    constexpr int MS = kMergeMaxSplits;
     const int n_heads = a.K / a.head_dim;
     const int rec = a.head_dim + 4;
 #pragma unroll
@@ -163,22 +166,27 @@ __device__ __forceinline__ void load_activations_merged(const GemvArgs& a, int b
         for (int b = 0; b < BT; ++b) {
             const bool use = in && b < nb;
             const float* pr = a.xpart + ((int64_t)((b0 + (b < nb ? b : 0)) * n_heads + h) * a.n_splits) * rec;
-            float M = -INFINITY, L = 0.f, O[8];
+            float ms[MS], ls[MS], os[MS][8];
+#pragma unroll
+            for (int sp = 0; sp < MS; ++sp) {
+                const float* p = pr + (int64_t)(sp < a.n_splits ? sp : 0) * rec;
+                ms[sp] = p[0];
+                ls[sp] = p[1];
+                load8(p + 4 + e0, os[sp], F32());
+            }
+            float M = -INFINITY;
+#pragma unroll
+            for (int sp = 0; sp < MS; ++sp)
+                if (sp < a.n_splits) M = fmaxf(M, ms[sp]);
+            float L = 0.f, O[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) O[i] = 0.f;
-#pragma unroll 4
-            for (int sp = 0; sp < a.n_splits; ++sp) {
-                const float* p = pr + (int64_t)sp * rec;
-                const float ms = p[0], ls = p[1];
-                float os[8];
-                load8(p + 4 + e0, os, F32());
-                const float Mn = fmaxf(M, ms);
-                const float fa = Mn == -INFINITY ? 0.f : exp2f(M - Mn);
-                const float fb = Mn == -INFINITY ? 0.f : exp2f(ms - Mn);
-                L = L * fa + ls * fb;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) O[i] = O[i] * fa + os[i] * fb;
-                M = Mn;
+            for (int sp = 0; sp < MS; ++sp) {
+                const float w = (sp < a.n_splits && M != -INFINITY) ? exp2f(ms[sp] - M) : 0.f;
+                L = fmaf(w, ls[sp], L);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) O[i] = fmaf(w, os[sp][i], O[i]);
             }
             const float inv = L > 0.f ? 1.0f / L : 0.f;
 #pragma unroll

@@ -11,6 +11,10 @@ namespace sttd {
 constexpr int kClockEntries = 16384;
 constexpr int kClockBank1 = 12288;
 
+// Up to this many attention splits the O-projection GEMV merges the partials
+// itself (GemvArgs::xpart); above, a combine pass writes the merged rows.
+constexpr int kMergeMaxSplits = 8;
+
 // Clock slot of the launch being issued when device-clock timing is on, else
 // nullptr (kClockEntries (start, end) pairs, see common.h).
 uint64_t* clock_slot();
