@@ -100,6 +100,21 @@ def test_many_rows_large_tiles_with_row_and_column_tails():
     log(f"T=1100 H=320: {max(errs):.2e}")
 
 
+@pytest.mark.parametrize("T", [513, 700])
+def test_mid_size_prefill_plain_bf16_rows_with_split_k(T):
+    """513-1023 rows: the 64x128-tile GEMMs without the split activations, with K split
+    over workgroups (atomic adds) where few of them run."""
+    errs = run_block_case(SMALL128, 18, T, 1, 768)
+    log(f"SMALL128 T={T}: {max(errs):.2e}")
+
+
+def test_chunked_prefill_with_a_large_tile_chunk():
+    """A 1030-row chunk (256x256 MFMA tiles, flash attention at pos0 = 70) after a 70-row one."""
+    sh = DecoderShape(hidden=320, n_heads=4, n_kv_heads=2, head_dim=64, ffn=768)
+    errs = run_block_case(sh, 19, 1100, 1, 1200, chunks=[70, 1030])
+    log(f"chunks [70, 1030] H=320: {max(errs):.2e}")
+
+
 def test_small_fp32_kv_cache_bf16_weights():
     sh = replace(SMALL64, kvdtype="f32")
     errs = run_block_case(sh, 13, 40, 3, 128)
@@ -112,7 +127,7 @@ def test_chunked_prefill_matches_single_shot(chunks):
     log(f"chunks {chunks}: {max(errs):.2e}")
 
 
-@pytest.mark.parametrize("Bn", [1, 2, 3, 4, 5, 16])
+@pytest.mark.parametrize("Bn", [1, 2, 3, 4, 5, 16, 40])
 def test_batched_decode_rows_match_independent_rows(Bn):
     """Rows of one step sit in distinct slabs at different positions."""
     sh = SMALL64
