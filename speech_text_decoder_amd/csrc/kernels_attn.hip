@@ -602,14 +602,16 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
                     for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kf][rf][i]);
                 mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
                 mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+                // every row sees key 0 in block 0, so mn is finite from the first block on;
+                // masked scores (-inf) and the first alpha (m = -inf) come out as 0
                 const float mn = fmaxf(m[rf], mx);
-                const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[rf] - mn);
+                const float alpha = __builtin_amdgcn_exp2f(m[rf] - mn);
                 float sum = 0.f;
 #pragma unroll
                 for (int kf = 0; kf < 4; ++kf)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float e = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[kf][rf][i] - mn);
+                        const float e = __builtin_amdgcn_exp2f(sc[kf][rf][i] - mn);
                         sc[kf][rf][i] = e;
                         sum += e;
                     }
@@ -618,12 +620,17 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
 #pragma unroll
                 for (int df = 0; df < DF; ++df) o[df][rf] *= alpha;
 #pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        pb[rf][k2][i] = (_Float16)sc[2 * k2][rf][i];
-                        pb[rf][k2][4 + i] = (_Float16)sc[2 * k2 + 1][rf][i];
-                    }
+                for (int k2 = 0; k2 < 2; ++k2) {
+                    // two probabilities per conversion (round toward zero; they lie in [0, 1])
+                    const u32x4 pk{
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(sc[2 * k2][rf][0], sc[2 * k2][rf][1])),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(sc[2 * k2][rf][2], sc[2 * k2][rf][3])),
+                        __builtin_bit_cast(uint32_t,
+                                           __builtin_amdgcn_cvt_pkrtz(sc[2 * k2 + 1][rf][0], sc[2 * k2 + 1][rf][1])),
+                        __builtin_bit_cast(uint32_t,
+                                           __builtin_amdgcn_cvt_pkrtz(sc[2 * k2 + 1][rf][2], sc[2 * k2 + 1][rf][3]))};
+                    pb[rf][k2] = __builtin_bit_cast(f16x8, pk);
+                }
             }
             // O^T += V^T P^T
 #pragma unroll
