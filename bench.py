@@ -534,7 +534,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the decoder block is not sharded; "
+        print(json.dumps({"error": "one GPU only: the decoder block is not sharded across GPUs; "
                                    "run with --gpus 1", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
