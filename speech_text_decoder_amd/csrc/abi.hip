@@ -188,11 +188,12 @@ KVLayer kv_layer(const sttd_kv_cache* kv, int layer) {
 // Splits of the rows-attention grid: about 256 cache rows per split at the
 // host bound (16-wave workgroups read them two rows per 16-lane group per
 // step), one split (no merge kernel) up to 256 positions.
-// Splits of each row's cache span over workgroups: about 256 positions each,
+// Splits of each row's cache span over workgroups: about 128 positions each,
 // but for batches of rows no more than keeps about two waves of workgroups
 // (512) busy, so each workgroup streams a longer run of rows.
 int choose_splits(int rows, int n_kv, int pos_bound, int part_cap) {
-    int s = (pos_bound + 255) / 256;
+    int s = (pos_bound + 127) / 128;
+    if (s > 32) s = 32;  // long single rows: fewer, longer splits (8-wave workgroups) and one combine
     const int fill = (512 + rows * n_kv - 1) / (rows * n_kv);
     if (rows > 1 && s > fill) s = fill;
     if (s > kMaxSplits) s = kMaxSplits;
@@ -265,8 +266,9 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
         // pass is cheaper
         defer = !mfma && splits > 1 && splits <= kMergeMaxSplits;
         ProfScope ps(STTD_KERN_ATTN_ROWS, s);
+        const int span = ((prefill ? rm.pos0 + R : pos_bound) + splits - 1) / splits;
         TRY(launch_attn_rows(prefill ? (const float*)ws->qbuf : ws->qkv, prefill ? qd : qkv_cols, R, nq, rm, kl,
-                             splits, ws->part, mfma || defer ? nullptr : ws->attn_o, mfma ? ao : nullptr,
+                             splits, span, ws->part, mfma || defer ? nullptr : ws->attn_o, mfma ? ao : nullptr,
                              mfma ? ao_lo : nullptr, qd, ws->err, prefill ? nullptr : &qr, wt, s));
     }
     // --- O projection + residual

@@ -388,13 +388,14 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
 }
 
 template <class KT, class GT, int D, bool FUSE>
-static hipError_t rows_dispatch(const RowsArgs& a, int R, hipStream_t s) {
+static hipError_t rows_dispatch(const RowsArgs& a, int R, bool wide, hipStream_t s) {
     const int G = a.n_heads / a.kv.n_kv;
     const dim3 grid(R, a.kv.n_kv, a.n_splits);
-    // one row: 8 waves per workgroup; batches of rows: 4, so two workgroups share a CU
+    // 4 waves per workgroup for groups of up to 2 query heads (the shorter merge tail beats
+    // the extra rows in flight) unless one row's split spans many cache rows; 8 for larger groups
 #define ROWS_LAUNCH(G_)                                                                             \
     do {                                                                                            \
-        if (G_ <= 2 && R > 1)                                                                       \
+        if (G_ <= 2 && !wide)                                                                       \
             attn_rows_kernel<KT, GT, D, G_, 4, FUSE><<<grid, 4 * 64, 0, s>>>(a);                    \
         else                                                                                        \
             attn_rows_kernel<KT, GT, D, G_, 8, FUSE><<<grid, 8 * 64, 0, s>>>(a);                    \
@@ -414,17 +415,19 @@ static hipError_t rows_dispatch(const RowsArgs& a, int R, hipStream_t s) {
 }
 
 template <class GT, bool FUSE>
-static hipError_t rows_dispatch_kv(const RowsArgs& a, int R, hipStream_t s) {
+static hipError_t rows_dispatch_kv(const RowsArgs& a, int R, bool wide, hipStream_t s) {
     if (a.kv.d == 128)
-        return a.kv.type == KV_F16 ? rows_dispatch<F16, GT, 128, FUSE>(a, R, s) : rows_dispatch<F32, GT, 128, FUSE>(a, R, s);
+        return a.kv.type == KV_F16 ? rows_dispatch<F16, GT, 128, FUSE>(a, R, wide, s)
+                                   : rows_dispatch<F32, GT, 128, FUSE>(a, R, wide, s);
     if (a.kv.d == 64)
-        return a.kv.type == KV_F16 ? rows_dispatch<F16, GT, 64, FUSE>(a, R, s) : rows_dispatch<F32, GT, 64, FUSE>(a, R, s);
+        return a.kv.type == KV_F16 ? rows_dispatch<F16, GT, 64, FUSE>(a, R, wide, s)
+                                   : rows_dispatch<F32, GT, 64, FUSE>(a, R, wide, s);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, RowMap rm, KVLayer kv, int n_splits,
-                            float* part, float* out_f32, uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo,
-                            uint32_t* err, const QkRope* fuse, WType gt, hipStream_t s) {
+                            int span_bound, float* part, float* out_f32, uint16_t* out_bf16, uint16_t* out_bf16_lo,
+                            int64_t ldo, uint32_t* err, const QkRope* fuse, WType gt, hipStream_t s) {
     if (R <= 0) return hipSuccess;
     if (n_splits < 1 || n_splits > 64 || (fuse && (!rm.pos || !rm.seq))) return hipErrorInvalidValue;
     RowsArgs a{};
@@ -434,9 +437,10 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
     if (fuse) {
         a.q_gain = fuse->q_gain; a.k_gain = fuse->k_gain; a.eps = fuse->eps; a.rope = fuse->rope;
         a.max_pos = fuse->max_pos;
-        return gt == W_BF16 ? rows_dispatch_kv<BF16, true>(a, R, s) : rows_dispatch_kv<F32, true>(a, R, s);
+        const bool wide = R == 1 && span_bound > 128;
+        return gt == W_BF16 ? rows_dispatch_kv<BF16, true>(a, R, wide, s) : rows_dispatch_kv<F32, true>(a, R, wide, s);
     }
-    return rows_dispatch_kv<BF16, false>(a, R, s);
+    return rows_dispatch_kv<BF16, false>(a, R, false, s);
 }
 
 // ------------------------------------------------------------------ causal prefill (MFMA flash)
