@@ -398,6 +398,35 @@ def bench_block(args, wl):
                    "decode_steps": n_steps, "batch": 1, "kv_dtype": sh.kvdtype, "wdtype": sh.wdtype,
                    "parallelism": "none (1 GPU)"},
     }
+    if R > 1:
+        # the same job on one replica: its 100.7 MB of weights then stay in the 256 MB MALL
+        # between steps (labelled separately; the headline uses the replicas above)
+        with torch.cuda.stream(stream):
+            g1 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g1, stream=stream):
+                for k in range(n_steps):
+                    sess.step(rows[k:k + 1], pos_all[k], pos_bound=T + k + 1, layers=[0])
+        torch.cuda.synchronize()
+        ev1 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.warmup + args.steps):
+            with torch.cuda.stream(stream):
+                x.copy_(x0)
+                rows.copy_(r0)
+                if i >= args.warmup:
+                    ev1[i - args.warmup][0].record(stream)
+                sess.prefill(x, layers=[0])
+                if i >= args.warmup:
+                    ev1[i - args.warmup][1].record(stream)
+                g1.replay()
+                if i >= args.warmup:
+                    ev1[i - args.warmup][2].record(stream)
+        torch.cuda.synchronize()
+        p1 = float(np.median([e[0].elapsed_time(e[1]) for e in ev1]))
+        d1 = float(np.median([e[1].elapsed_time(e[2]) for e in ev1])) / n_steps
+        res["mall_resident_one_replica"] = {
+            "prefill_ms_per_block": round(p1, 5), "decode_us_per_block_step": round(d1 * 1e3, 3),
+            "decode_hbm_frac_equiv": round(step_bytes / (d1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del g1
     if not args.no_kernel_profile:
         n_prof = min(n_steps, 16)
 
