@@ -466,13 +466,15 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
     constexpr int NT = 512;                // 8 waves, 16 query rows each
     constexpr int RF = 1;                  // 16-row fragments per wave
     constexpr int KB = 64, TQ = 8 * 16 * RF;
-    constexpr int KS = D + 8, VS = KB + 8;
+    constexpr int KS = D, VS = KB;  // unpadded rows; 16-byte chunks XOR-swizzled by the row (swz below)
     constexpr int KSTEPS = D / 32, DF = D / 16;
     constexpr int KVECS = KB * D / 8 / NT;                  // 16-byte K pieces per thread per block
     constexpr int VITEMS = (KB / 2) * (D / 8);              // (key pair, 8-dim chunk) items of V per block
     constexpr int VPAIRS = (VITEMS + NT - 1) / NT;          // per thread
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KB * KS];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VS];
+    // element offset of 16-byte chunk c of an LDS row r of `stride` elements
+    auto swz = [](int r, int c, int stride) { return r * stride + ((c ^ (r & 7)) * 8); };
 
     clock_begin(clk);
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
@@ -547,7 +549,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
 #pragma unroll
             for (int i = 0; i < KVECS; ++i) {
                 const int v = tid + i * NT;
-                *reinterpret_cast<u32x4*>(&Ks[buf][(v / (D / 8)) * KS + (v % (D / 8)) * 8]) = kreg[i];
+                *reinterpret_cast<u32x4*>(&Ks[buf][swz(v / (D / 8), v % (D / 8), KS)]) = kreg[i];
             }
 #pragma unroll
             for (int i = 0; i < VPAIRS; ++i) {
@@ -555,13 +557,13 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
                 if (v >= VITEMS) continue;
                 const int c = 2 * (v % (KB / 2)), e = (v / (KB / 2)) * 8, kk = c % 32;
                 const int pp = kk < 16 ? 8 * (kk / 4) + kk % 4 : 8 * ((kk - 16) / 4) + 4 + (kk - 16) % 4;
-                uint32_t* col = reinterpret_cast<uint32_t*>(&Vt[buf][e * VS + (c / 32) * 32 + pp]);
+                const int pos = (c / 32) * 32 + pp;  // even: the pair shares one 32-bit word
                 const u32x4 a = vreg[2 * i], b = vreg[2 * i + 1];
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) {
                     const uint32_t lo16 = (a[jj / 2] >> (16 * (jj % 2))) & 0xFFFFu;
                     const uint32_t hi16 = (b[jj / 2] >> (16 * (jj % 2))) & 0xFFFFu;
-                    col[jj * (VS / 2)] = lo16 | (hi16 << 16);
+                    *reinterpret_cast<uint32_t*>(&Vt[buf][swz(e + jj, pos / 8, VS) + pos % 8]) = lo16 | (hi16 << 16);
                 }
             }
         };
@@ -580,7 +582,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
 #pragma unroll
                 for (int ks = 0; ks < KSTEPS; ++ks) {
                     const f16x8 kfr =
-                        *reinterpret_cast<const f16x8*>(&Ks[buf][(kf * 16 + r16) * KS + ks * 32 + g4 * 8]);
+                        *reinterpret_cast<const f16x8*>(&Ks[buf][swz(kf * 16 + r16, ks * 4 + g4, KS)]);
 #pragma unroll
                     for (int rf = 0; rf < RF; ++rf)
                         sc[kf][rf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kfr, qf[rf][ks], sc[kf][rf], 0, 0, 0);
@@ -641,7 +643,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
             for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
                 for (int df = 0; df < DF; ++df) {
-                    const f16x8 vfr = *reinterpret_cast<const f16x8*>(&Vt[buf][(df * 16 + r16) * VS + k2 * 32 + g4 * 8]);
+                    const f16x8 vfr = *reinterpret_cast<const f16x8*>(&Vt[buf][swz(df * 16 + r16, k2 * 4 + g4, VS)]);
 #pragma unroll
                     for (int rf = 0; rf < RF; ++rf)
                         o[df][rf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vfr, pb[rf][k2], o[df][rf], 0, 0, 0);
