@@ -6,8 +6,8 @@
 //
 // Tile BM x BN x 64 per workgroup of 4 waves (2 x 2); each wave computes a
 // (BM/2) x (BN/2) block with v_mfma_f32_16x16x32_bf16. A and W tiles are staged
-// through LDS (rows padded to 72 bf16 so the 16-lane column reads of the
-// fragments hit distinct banks); the next K tile is fetched into registers
+// through LDS (16-byte chunks of each row XOR-swizzled by the row so the
+// fragment reads hit distinct banks); the next K tile is fetched into registers
 // while the current one feeds the MFMAs.
 //
 // Split activations (A_lo given): every MFMA step runs twice, on the bf16
@@ -23,7 +23,11 @@
 namespace sttd {
 
 constexpr int BK = 64;
-constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per staged row
+constexpr int LDS_STRIDE = BK;  // bf16 elements per staged row (unpadded; chunks swizzled)
+
+// LDS offset (elements) of 16-byte chunk c of staged row r: the chunk index is
+// XOR-swizzled by the row so fragment reads and staging writes avoid bank conflicts.
+__device__ __forceinline__ int lds_off(int r, int c) { return r * LDS_STRIDE + ((c ^ (r & 7)) * 8); }
 
 template <int V>
 __device__ __forceinline__ void fetch_rows(u32x4 (&reg)[V], const uint16_t* const (&p)[V], const bool (&ok)[V],
@@ -37,7 +41,7 @@ __device__ __forceinline__ void stash_rows(const u32x4 (&reg)[V], uint16_t* lds,
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         const int v = tid + i * 256;
-        *reinterpret_cast<u32x4*>(&lds[(v / (BK / 8)) * LDS_STRIDE + (v % (BK / 8)) * 8]) = reg[i];
+        *reinterpret_cast<u32x4*>(&lds[lds_off(v / (BK / 8), v % (BK / 8))]) = reg[i];
     }
 }
 
@@ -140,13 +144,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
             const int kc = ks * 32 + (lane / 16) * 8;
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                const int o = (wm * (BM / 2) + i * 16 + lane % 16) * LDS_STRIDE + kc;
+                const int o = lds_off(wm * (BM / 2) + i * 16 + lane % 16, kc / 8);
                 af[i] = *reinterpret_cast<const bf16x8*>(&As[o]);
                 if (SPLIT) afl[i] = *reinterpret_cast<const bf16x8*>(&Als[o]);
             }
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[(bfrag_row[j] + lane % 16) * LDS_STRIDE + kc]);
+                bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[lds_off(bfrag_row[j] + lane % 16, kc / 8)]);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
