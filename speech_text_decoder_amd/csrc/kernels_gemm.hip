@@ -423,10 +423,11 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
     for (int f = 0; f < CF; ++f) {
         if (EPI == GEMM_SWIGLU) {
-            const int c = ct * 16 + lane % 16;  // act column
+            // fragments [0, CF/2): gate rows of act columns 16 (ct CF/2 + f) ..; [CF/2, CF): their up rows
+            const int c = (ct * (CF / 2) + f % (CF / 2)) * 16 + lane % 16;  // act column
             wok[f] = c < g.N;
             const int cc = wok[f] ? c : 0;
-            wrow[f] = g.w[0] + (int64_t)(f == 0 ? cc : g.N + cc) * g.K;
+            wrow[f] = g.w[0] + (int64_t)(f < CF / 2 ? cc : g.N + cc) * g.K;
         } else {
             const int n0 = (ct * CF + f) * 16 + lane % 16;
             wok[f] = n0 < g.N;
@@ -503,11 +504,12 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
         if (row >= g.M) continue;
         const float v = red[0][row][col] + red[1][row][col] + red[2][row][col] + red[3][row][col];
         if (EPI == GEMM_SWIGLU) {
-            if (col >= 16) continue;  // the up half is read with its gate
-            const int c = ct * 16 + col;
+            constexpr int GC = CF / 2 * 16;  // gate columns of the tile; the up ones follow
+            if (col >= GC) continue;  // the up half is read with its gate
+            const int c = ct * GC + col;
             if (c >= g.N) continue;
-            const float up = red[0][row][col + 16] + red[1][row][col + 16] + red[2][row][col + 16] +
-                             red[3][row][col + 16];
+            const float up = red[0][row][col + GC] + red[1][row][col + GC] + red[2][row][col + GC] +
+                             red[3][row][col + GC];
             const float a = v / (1.0f + expf(-v)) * up;
             uint16_t hi, lo16;
             split_bf16(a, hi, lo16);
@@ -537,7 +539,7 @@ static void launch_skinny_rf(const GemmArgs& g, dim3 grid, hipStream_t s) {
 
 static void launch_gemm_skinny(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     if (epi == GEMM_SWIGLU) {
-        launch_skinny_rf<GEMM_SWIGLU, 2>(g, dim3((g.N + 15) / 16, 1), s);
+        launch_skinny_rf<GEMM_SWIGLU, 4>(g, dim3((g.N + 31) / 32, 1), s);
         return;
     }
     const int tiles = (g.N + 15) / 16;
