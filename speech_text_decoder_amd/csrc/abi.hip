@@ -185,16 +185,14 @@ KVLayer kv_layer(const sttd_kv_cache* kv, int layer) {
     return l;
 }
 
-// Splits of the rows-attention grid: about 256 cache rows per split at the
-// host bound (16-wave workgroups read them two rows per 16-lane group per
-// step), one split (no merge kernel) up to 256 positions.
 // Splits of each row's cache span over workgroups: about 128 positions each,
-// but for batches of rows no more than keeps about two waves of workgroups
-// (512) busy, so each workgroup streams a longer run of rows.
+// but for batches of rows no more than about one 8-wave workgroup per CU
+// (256), so each workgroup streams a longer run of rows (measured on 16 rows of
+// 150-1500 positions: 256 workgroups of 8 waves beat 512 of 4 and any larger grid).
 int choose_splits(int rows, int n_kv, int pos_bound, int part_cap) {
     int s = (pos_bound + 127) / 128;
     if (s > 32) s = 32;  // long single rows: fewer, longer splits (8-wave workgroups) and one combine
-    const int fill = (512 + rows * n_kv - 1) / (rows * n_kv);
+    const int fill = (256 + rows * n_kv - 1) / (rows * n_kv);
     if (rows > 1 && s > fill) s = fill;
     if (s > kMaxSplits) s = kMaxSplits;
     if (s > part_cap / rows) s = part_cap / rows;

@@ -392,7 +392,7 @@ static hipError_t rows_dispatch(const RowsArgs& a, int R, bool wide, hipStream_t
     const int G = a.n_heads / a.kv.n_kv;
     const dim3 grid(R, a.kv.n_kv, a.n_splits);
     // 4 waves per workgroup for groups of up to 2 query heads (the shorter merge tail beats
-    // the extra rows in flight) unless one row's split spans many cache rows; 8 for larger groups
+    // the extra rows in flight) unless a split spans more than 128 cache rows; 8 for larger groups
 #define ROWS_LAUNCH(G_)                                                                             \
     do {                                                                                            \
         if (G_ <= 2 && !wide)                                                                       \
@@ -437,7 +437,7 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
     if (fuse) {
         a.q_gain = fuse->q_gain; a.k_gain = fuse->k_gain; a.eps = fuse->eps; a.rope = fuse->rope;
         a.max_pos = fuse->max_pos;
-        const bool wide = R == 1 && span_bound > 128;
+        const bool wide = span_bound > 128;
         return gt == W_BF16 ? rows_dispatch_kv<BF16, true>(a, R, wide, s) : rows_dispatch_kv<F32, true>(a, R, wide, s);
     }
     return rows_dispatch_kv<BF16, false>(a, R, false, s);
