@@ -446,11 +446,16 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
 // ------------------------------------------------------------------ causal prefill (MFMA flash)
 // A workgroup takes the query tiles of 128 rows of one head in pairs, tile i
 // and tile n - 1 - i, so every workgroup has the same causal work (when there
-// are enough tiles to fill the chip; otherwise one tile each); each of its
-// 8 waves owns 16 rows, two waves per SIMD. Per block of 64 cache rows:
+// are enough tiles to fill the chip; otherwise one tile each). Its 8 waves
+// are 4 row groups of 32 query rows (two 16-row fragments) times 2 key groups:
+// key group k takes keys 32k .. 32k + 31 of every 64-key block, so each K and
+// V^T fragment read from LDS feeds two MFMAs (one per row fragment), half the
+// LDS reads per MFMA of one 16-row fragment per wave. Per block and wave:
 //   S^T = K Q^T     A: K rows staged in LDS; B: the wave's Q rows, in registers
 //   online softmax; a lane owns one query row of each fragment
 //   O^T += V^T P^T  A: V^T staged in LDS; B: P^T straight from the S^T registers
+// At the end the second key group hands its (m, l, O) state to the first
+// through LDS, which merges the two and writes the rows.
 // Working on the transposes keeps every per-row quantity (max, sum, the O
 // rescale) in the lanes that own the row. The S^T fragment gives lane l the
 // keys 4g .. 4g + 3 (g = l / 16) of each 16-key tile, so V^T is staged with
@@ -458,29 +463,40 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
 // 8g + j holds key 4g + j (j < 4) or 16 + 4g + j - 4 (j >= 4). K and V^T are
 // double-buffered in LDS; the next block's rows load while the current one
 // computes. Exponentials in base 2 on scores scaled by log2(e) / sqrt(d).
+constexpr float kLazy = 8.f;  // lazy-rescale threshold of the flash kernel (base-2 exponent)
+
 template <int D>
 __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __restrict__ q16, int64_t ldq, int T,
                                                            int pos0, int seq, int n_heads, KVLayer kv,
                                                            uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo,
                                                            int64_t ldo, int paired, uint64_t* clk) {
-    constexpr int NT = 512;                // 8 waves, 16 query rows each
-    constexpr int RF = 1;                  // 16-row fragments per wave
-    constexpr int KB = 64, TQ = 8 * 16 * RF;
+    constexpr int NT = 512;                // 8 waves: 4 row groups x 2 key groups
+    constexpr int RF = 2;                  // 16-row fragments per wave
+    constexpr int KB = 64, TQ = 4 * 16 * RF;
     constexpr int KS = D, VS = KB;  // unpadded rows; 16-byte chunks XOR-swizzled by the row (swz below)
     constexpr int KSTEPS = D / 32, DF = D / 16;
     constexpr int KVECS = KB * D / 8 / NT;                  // 16-byte K pieces per thread per block
     constexpr int VITEMS = (KB / 2) * (D / 8);              // (key pair, 8-dim chunk) items of V per block
     constexpr int VPAIRS = (VITEMS + NT - 1) / NT;          // per thread
+    constexpr int HO = DF / 2 * RF * 4;                     // O values per lane in each half of the hand-over
+    static_assert(HO * 256 * 4 <= 2 * KB * KS * 2 && HO * 256 * 4 <= 2 * D * VS * 2, "hand-over fits the buffers");
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KB * KS];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VS];
+    __shared__ float ml[2][RF][256];
     // element offset of 16-byte chunk c of an LDS row r of `stride` elements
     auto swz = [](int r, int c, int stride) { return r * stride + ((c ^ (r & 7)) * 8); };
 
     clock_begin(clk);
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
     const int g4 = lane / 16, r16 = lane % 16;
-    const int h = blockIdx.y;
-    const int j = h / (n_heads / kv.n_kv);
+    const int kg = wave / 4, wr = wave % 4;  // key group, row group
+    // XCD-aware order: workgroup b runs on XCD b % 8, so each XCD is given a
+    // contiguous run of logical ids, KV head major; the XCD's workgroups then
+    // re-read one KV head's rows, which stay in its L2, instead of all of them
+    const int nx = gridDim.x, nwg = nx * gridDim.y, b = blockIdx.x + nx * blockIdx.y;
+    const int L = nwg % 8 ? b : (b % 8) * (nwg / 8) + b / 8;
+    const int G = n_heads / kv.n_kv;
+    const int j = L / (G * nx), h = j * G + (L / nx) % G, px = L % nx;
     const int n_tiles = (T + TQ - 1) / TQ;
     const int64_t slab = ((int64_t)seq * kv.n_kv + j) * kv.n_ctx * D;
     const uint16_t* Kg = (const uint16_t*)kv.k + slab;
@@ -489,11 +505,10 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
 
     for (int pass = 0; pass < 2; ++pass) {
         // paired: tiles x and n - 1 - x; otherwise one tile each, the heavy (late) ones first
-        const int tile = !paired ? n_tiles - 1 - (int)blockIdx.x
-                                 : (pass == 0 ? (int)blockIdx.x : n_tiles - 1 - (int)blockIdx.x);
-        if (pass == 1 && (!paired || tile <= (int)blockIdx.x)) break;  // an odd count leaves the middle tile single
+        const int tile = !paired ? n_tiles - 1 - px : (pass == 0 ? px : n_tiles - 1 - px);
+        if (pass == 1 && (!paired || tile <= px)) break;  // an odd count leaves the middle tile single
         __syncthreads();                                  // the LDS buffers are free again
-        const int t0 = tile * TQ + wave * 16 * RF;        // this wave's first query row
+        const int t0 = tile * TQ + wr * 16 * RF;          // this wave's first query row
 
         // Q^T fragments (B operand): query row t0 + 16 rf + r16, dims 32 ks + 8 g4 ..
         f16x8 qf[RF][KSTEPS];
@@ -572,107 +587,136 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
         if (n_blocks > 1) fetch(1);
         __syncthreads();
         for (int kb = 0; kb < n_blocks; ++kb) {
-            const int buf = kb & 1, c0 = kb * KB;
-            // S^T: lane holds query row r16 of fragment rf, keys 16 kf + 4 g4 + i
-            f32x4 sc[4][RF];
+            const int buf = kb & 1, c0 = kb * KB + kg * 32;  // this key group's first key of the block
+            // S^T: lane holds query row r16 of fragment rf, keys c0 + 16 kf + 4 g4 + i
+            f32x4 sc[2][RF];
 #pragma unroll
-            for (int kf = 0; kf < 4; ++kf) {
+            for (int kf = 0; kf < 2; ++kf) {
 #pragma unroll
                 for (int rf = 0; rf < RF; ++rf) sc[kf][rf] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KSTEPS; ++ks) {
                     const f16x8 kfr =
-                        *reinterpret_cast<const f16x8*>(&Ks[buf][swz(kf * 16 + r16, ks * 4 + g4, KS)]);
+                        *reinterpret_cast<const f16x8*>(&Ks[buf][swz(kg * 32 + kf * 16 + r16, ks * 4 + g4, KS)]);
 #pragma unroll
                     for (int rf = 0; rf < RF; ++rf)
                         sc[kf][rf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kfr, qf[rf][ks], sc[kf][rf], 0, 0, 0);
                 }
             }
-            // online softmax; P^T packed as the B fragments of the two 32-key steps
-            f16x8 pb[RF][2];
-            const bool diag = c0 + KB - 1 > pos0 + t0;  // some key of the block lies past some row of the wave
+            // online softmax; P^T packed as the B fragment of the group's 32-key step
+            f16x8 pb[RF];
+            const bool diag = c0 + 31 > pos0 + t0;  // some key of the group lies past some row of the wave
 #pragma unroll
             for (int rf = 0; rf < RF; ++rf) {
                 const int t_abs = pos0 + t0 + rf * 16 + r16;  // last key this query row sees
                 float mx = -INFINITY;
                 if (diag) {
 #pragma unroll
-                    for (int kf = 0; kf < 4; ++kf)
+                    for (int kf = 0; kf < 2; ++kf)
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
                             if (c0 + kf * 16 + g4 * 4 + i > t_abs) sc[kf][rf][i] = -INFINITY;
                 }
 #pragma unroll
-                for (int kf = 0; kf < 4; ++kf)
+                for (int kf = 0; kf < 2; ++kf)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kf][rf][i]);
-                mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-                // every row sees key 0 in block 0, so mn is finite from the first block on;
-                // masked scores (-inf) and the first alpha (m = -inf) come out as 0
-                const float mn = fmaxf(m[rf], mx);
-                const float alpha = __builtin_amdgcn_exp2f(m[rf] - mn);
+                mx = fmaxf(mx, xor16(mx));
+                mx = fmaxf(mx, xor32(mx));
+                // lazy rescale: the reference m moves only when a score exceeds it by more
+                // than kLazy (base 2), so probabilities stay below 2^kLazy (exact in f16's
+                // range) and the O rescale is skipped by every wave whose rows need none
+                if (__ballot(mx > m[rf] + kLazy) != 0ull) {
+                    const float mn = mx > m[rf] + kLazy ? mx : m[rf];
+                    // a row may see no key of its group yet (m = -inf): its state is empty,
+                    // so any finite factor (here 0) leaves it so
+                    const float alpha = m[rf] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[rf] - mn);
+                    l[rf] *= alpha;
+#pragma unroll
+                    for (int df = 0; df < DF; ++df) o[df][rf] *= alpha;
+                    m[rf] = mn;
+                }
+                // exponents against 0 while the row has seen no key: masked scores give 0
+                const float mref = m[rf] == -INFINITY ? 0.f : m[rf];
                 float sum = 0.f;
 #pragma unroll
-                for (int kf = 0; kf < 4; ++kf)
+                for (int kf = 0; kf < 2; ++kf)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float e = __builtin_amdgcn_exp2f(sc[kf][rf][i] - mn);
+                        const float e = __builtin_amdgcn_exp2f(sc[kf][rf][i] - mref);
                         sc[kf][rf][i] = e;
                         sum += e;
                     }
-                l[rf] = l[rf] * alpha + sum;
-                m[rf] = mn;
-#pragma unroll
-                for (int df = 0; df < DF; ++df) o[df][rf] *= alpha;
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) {
-                    // two probabilities per conversion (round toward zero; they lie in [0, 1])
-                    const u32x4 pk{
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(sc[2 * k2][rf][0], sc[2 * k2][rf][1])),
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(sc[2 * k2][rf][2], sc[2 * k2][rf][3])),
-                        __builtin_bit_cast(uint32_t,
-                                           __builtin_amdgcn_cvt_pkrtz(sc[2 * k2 + 1][rf][0], sc[2 * k2 + 1][rf][1])),
-                        __builtin_bit_cast(uint32_t,
-                                           __builtin_amdgcn_cvt_pkrtz(sc[2 * k2 + 1][rf][2], sc[2 * k2 + 1][rf][3]))};
-                    pb[rf][k2] = __builtin_bit_cast(f16x8, pk);
-                }
+                l[rf] += sum;
+                // two probabilities per conversion (round toward zero; they lie in [0, 1])
+                const u32x4 pk{
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(sc[0][rf][0], sc[0][rf][1])),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(sc[0][rf][2], sc[0][rf][3])),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(sc[1][rf][0], sc[1][rf][1])),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(sc[1][rf][2], sc[1][rf][3]))};
+                pb[rf] = __builtin_bit_cast(f16x8, pk);
             }
-            // O^T += V^T P^T
+            // O^T += V^T P^T over the group's 32 keys
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2)
+            for (int df = 0; df < DF; ++df) {
+                const f16x8 vfr = *reinterpret_cast<const f16x8*>(&Vt[buf][swz(df * 16 + r16, kg * 4 + g4, VS)]);
 #pragma unroll
-                for (int df = 0; df < DF; ++df) {
-                    const f16x8 vfr = *reinterpret_cast<const f16x8*>(&Vt[buf][swz(df * 16 + r16, k2 * 4 + g4, VS)]);
-#pragma unroll
-                    for (int rf = 0; rf < RF; ++rf)
-                        o[df][rf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vfr, pb[rf][k2], o[df][rf], 0, 0, 0);
-                }
+                for (int rf = 0; rf < RF; ++rf)
+                    o[df][rf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vfr, pb[rf], o[df][rf], 0, 0, 0);
+            }
             if (kb + 1 < n_blocks) {
                 stash(buf ^ 1);  // that buffer was last read before the previous barrier
                 if (kb + 2 < n_blocks) fetch(kb + 2);
             }
             __syncthreads();
         }
-        // finish: the row sum is spread over the 4 lane groups sharing r16
+        // hand-over: key group 1 leaves m, its per-lane l and O in LDS (the K/V
+        // buffers are free after the loop's last barrier), lane-minor so that a
+        // wave's 64 stores hit 64 consecutive words
+        float* xo0 = reinterpret_cast<float*>(&Ks[0][0]);  // O values of df < DF / 2
+        float* xo1 = reinterpret_cast<float*>(&Vt[0][0]);  // and of the rest
+        const int slot = wr * WAVE + lane;
+        if (kg == 1) {
 #pragma unroll
-        for (int rf = 0; rf < RF; ++rf) {
-            float lsum = l[rf];
-            lsum += __shfl_xor(lsum, 16, WAVE);
-            lsum += __shfl_xor(lsum, 32, WAVE);
-            const int t = t0 + rf * 16 + r16;
-            if (t >= T) continue;
-            const float inv = 1.0f / lsum;
+            for (int rf = 0; rf < RF; ++rf) {
+                ml[0][rf][slot] = m[rf];
+                ml[1][rf][slot] = l[rf];
 #pragma unroll
-            for (int df = 0; df < DF; ++df)
+                for (int df = 0; df < DF; ++df)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    uint16_t hi, lo;
-                    split_bf16(o[df][rf][i] * inv, hi, lo);
-                    const int64_t idx = (int64_t)t * ldo + h * D + df * 16 + g4 * 4 + i;
-                    out[idx] = hi;
-                    if (out_lo) out_lo[idx] = lo;
-                }
+                    for (int i = 0; i < 4; ++i) {
+                        float* x = df < DF / 2 ? xo0 : xo1;
+                        x[(((df % (DF / 2)) * RF + rf) * 4 + i) * 256 + slot] = o[df][rf][i];
+                    }
+            }
+        }
+        __syncthreads();
+        if (kg == 0) {
+#pragma unroll
+            for (int rf = 0; rf < RF; ++rf) {
+                const float m2 = ml[0][rf][slot], l2 = ml[1][rf][slot];
+                const float M = fmaxf(m[rf], m2);
+                const float mref = M == -INFINITY ? 0.f : M;
+                const float a = __builtin_amdgcn_exp2f(m[rf] - mref), b = __builtin_amdgcn_exp2f(m2 - mref);
+                float lsum = l[rf] * a + l2 * b;
+                lsum += xor16(lsum);  // the row sum is spread over the 4 lane groups sharing r16
+                lsum += xor32(lsum);
+                const int t = t0 + rf * 16 + r16;
+                if (t >= T) continue;
+                const float inv = 1.0f / lsum;
+#pragma unroll
+                for (int df = 0; df < DF; ++df)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float* x = df < DF / 2 ? xo0 : xo1;
+                        const float v = (o[df][rf][i] * a + x[(((df % (DF / 2)) * RF + rf) * 4 + i) * 256 + slot] * b) * inv;
+                        uint16_t hi, lo;
+                        split_bf16(v, hi, lo);
+                        const int64_t idx = (int64_t)t * ldo + h * D + df * 16 + g4 * 4 + i;
+                        out[idx] = hi;
+                        if (out_lo) out_lo[idx] = lo;
+                    }
+            }
         }
     }
     clock_end(clk);
