@@ -523,15 +523,20 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
                 for (int i = 0; i < 8; ++i) qf[rf][ks][i] = (_Float16)((float)q[i] * sl2);  // scores come out scaled
             }
         }
-        f32x4 o[DF][RF];
-        float m[RF], l[RF];
+        // O^T, and the row sums as one more MFMA product: a fragment of ones times
+        // P^T puts the sum of the row's (f16) probabilities in every element
+        f32x4 o[DF][RF], lacc[RF];
+        float m[RF];
 #pragma unroll
         for (int rf = 0; rf < RF; ++rf) {
             m[rf] = -INFINITY;
-            l[rf] = 0.f;
+            lacc[rf] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int df = 0; df < DF; ++df) o[df][rf] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        f16x8 ones;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ones[i] = (_Float16)1.0f;
 
         const int tile_last = min(tile * TQ + TQ - 1, T - 1);
         const int n_keys = pos0 + tile_last + 1;  // keys any row of the tile can see
@@ -539,15 +544,16 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
 
         // staging: K as 16-byte row pieces; V as pairs of keys (2c, 2c + 1) over one
         // 8-dim chunk, written to V^T as 32-bit words (the permutation keeps the
-        // pair adjacent)
+        // pair adjacent). Rows past the tile's last key are clamped to it: they are
+        // real, finite cache rows whose scores the diagonal mask sets to -inf, so
+        // they add 0 to O
         u32x4 kreg[KVECS], vreg[2 * VPAIRS];
         auto fetch = [&](int kb) {
 #pragma unroll
             for (int i = 0; i < KVECS; ++i) {
                 const int v = tid + i * NT;
-                const int ck = kb * KB + v / (D / 8), ek = (v % (D / 8)) * 8;
-                kreg[i] = ck < n_keys ? *reinterpret_cast<const u32x4*>(Kg + (int64_t)ck * D + ek)
-                                      : u32x4{0u, 0u, 0u, 0u};
+                const int ck = min(kb * KB + v / (D / 8), n_keys - 1), ek = (v % (D / 8)) * 8;
+                kreg[i] = *reinterpret_cast<const u32x4*>(Kg + (int64_t)ck * D + ek);
             }
 #pragma unroll
             for (int i = 0; i < VPAIRS; ++i) {
@@ -555,9 +561,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
                 const int cv = kb * KB + 2 * (v % (KB / 2)), ev = (v / (KB / 2)) * 8;
 #pragma unroll
                 for (int u = 0; u < 2; ++u)
-                    vreg[2 * i + u] = cv + u < n_keys
-                                          ? *reinterpret_cast<const u32x4*>(Vg + (int64_t)(cv + u) * D + ev)
-                                          : u32x4{0u, 0u, 0u, 0u};
+                    vreg[2 * i + u] = *reinterpret_cast<const u32x4*>(Vg + (int64_t)min(cv + u, n_keys - 1) * D + ev);
             }
         };
         auto stash = [&](int buf) {
@@ -576,9 +580,9 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
                 const u32x4 a = vreg[2 * i], b = vreg[2 * i + 1];
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) {
-                    const uint32_t lo16 = (a[jj / 2] >> (16 * (jj % 2))) & 0xFFFFu;
-                    const uint32_t hi16 = (b[jj / 2] >> (16 * (jj % 2))) & 0xFFFFu;
-                    *reinterpret_cast<uint32_t*>(&Vt[buf][swz(e + jj, pos / 8, VS) + pos % 8]) = lo16 | (hi16 << 16);
+                    // dim e + jj of keys c (low half) and c + 1 (high half): one byte permute
+                    const uint32_t w = __builtin_amdgcn_perm(b[jj / 2], a[jj / 2], jj % 2 ? 0x07060302u : 0x05040100u);
+                    *reinterpret_cast<uint32_t*>(&Vt[buf][swz(e + jj, pos / 8, VS) + pos % 8]) = w;
                 }
             }
         };
@@ -631,23 +635,17 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
                     // a row may see no key of its group yet (m = -inf): its state is empty,
                     // so any finite factor (here 0) leaves it so
                     const float alpha = m[rf] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[rf] - mn);
-                    l[rf] *= alpha;
+                    lacc[rf] *= alpha;
 #pragma unroll
                     for (int df = 0; df < DF; ++df) o[df][rf] *= alpha;
                     m[rf] = mn;
                 }
                 // exponents against 0 while the row has seen no key: masked scores give 0
                 const float mref = m[rf] == -INFINITY ? 0.f : m[rf];
-                float sum = 0.f;
 #pragma unroll
                 for (int kf = 0; kf < 2; ++kf)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float e = __builtin_amdgcn_exp2f(sc[kf][rf][i] - mref);
-                        sc[kf][rf][i] = e;
-                        sum += e;
-                    }
-                l[rf] += sum;
+                    for (int i = 0; i < 4; ++i) sc[kf][rf][i] = __builtin_amdgcn_exp2f(sc[kf][rf][i] - mref);
                 // two probabilities per conversion (round toward zero; they lie in [0, 1])
                 const u32x4 pk{
                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(sc[0][rf][0], sc[0][rf][1])),
@@ -656,7 +654,9 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(sc[1][rf][2], sc[1][rf][3]))};
                 pb[rf] = __builtin_bit_cast(f16x8, pk);
             }
-            // O^T += V^T P^T over the group's 32 keys
+            // O^T += V^T P^T over the group's 32 keys; the row sums likewise
+#pragma unroll
+            for (int rf = 0; rf < RF; ++rf) lacc[rf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[rf], lacc[rf], 0, 0, 0);
 #pragma unroll
             for (int df = 0; df < DF; ++df) {
                 const f16x8 vfr = *reinterpret_cast<const f16x8*>(&Vt[buf][swz(df * 16 + r16, kg * 4 + g4, VS)]);
@@ -670,7 +670,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
             }
             __syncthreads();
         }
-        // hand-over: key group 1 leaves m, its per-lane l and O in LDS (the K/V
+        // hand-over: key group 1 leaves m, l and O in LDS (the K/V
         // buffers are free after the loop's last barrier), lane-minor so that a
         // wave's 64 stores hit 64 consecutive words
         float* xo0 = reinterpret_cast<float*>(&Ks[0][0]);  // O values of df < DF / 2
@@ -680,7 +680,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
 #pragma unroll
             for (int rf = 0; rf < RF; ++rf) {
                 ml[0][rf][slot] = m[rf];
-                ml[1][rf][slot] = l[rf];
+                ml[1][rf][slot] = lacc[rf][0];
 #pragma unroll
                 for (int df = 0; df < DF; ++df)
 #pragma unroll
@@ -698,9 +698,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
                 const float M = fmaxf(m[rf], m2);
                 const float mref = M == -INFINITY ? 0.f : M;
                 const float a = __builtin_amdgcn_exp2f(m[rf] - mref), b = __builtin_amdgcn_exp2f(m2 - mref);
-                float lsum = l[rf] * a + l2 * b;
-                lsum += xor16(lsum);  // the row sum is spread over the 4 lane groups sharing r16
-                lsum += xor32(lsum);
+                const float lsum = lacc[rf][0] * a + l2 * b;
                 const int t = t0 + rf * 16 + r16;
                 if (t >= T) continue;
                 const float inv = 1.0f / lsum;
