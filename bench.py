@@ -52,7 +52,7 @@ def traffic_bytes(name, rows):
 
 
 KERNEL_NAMES = ["rmsnorm", "qkv_gemv", "qkv_gemm", "qk_rope_kv", "attn_rows", "attn_prefill", "o_gemv", "o_gemm",
-                "gateup_gemv", "gateup_gemm", "down_gemv", "down_gemm", "lm_head"]
+                "gateup_gemv", "gateup_gemm", "down_gemv", "down_gemm", "lm_head", "block_step"]
 
 
 def parse():
@@ -65,6 +65,8 @@ def parse():
                     help="independent weight/KV replicas stacked for single-block workloads (MALL honesty)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-profile", action="store_true")
+    ap.add_argument("--fused-step", action="store_true",
+                    help="single-row decode steps as one persistent launch per block (STTD_OPT_FUSED_STEP)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 3 times (scales HBM byte counters)")
     return ap.parse_args()
@@ -95,6 +97,10 @@ def kernel_cost(name, sh, rows, mean_keys=0.0):
         return rows * (2 * qd * 4 + 2 * kvd * kvb), 4.0 * qd * rows * (rows + 1) / 2
     if name == "rmsnorm":
         return rows * H * (4 + 4) + H * wb, 4.0 * rows * H
+    if name == "block_step":     # the fused single-row step: every stage of one block in one launch
+        parts = [kernel_cost(n, sh, rows, mean_keys) for n in ("qkv_gemv", "attn_rows", "o_gemv", "gateup_gemv",
+                                                               "down_gemv")]
+        return sum(p[0] for p in parts), sum(p[1] for p in parts)
     return 0, 0.0
 
 
@@ -202,6 +208,7 @@ def bench_greedy_stack(args, wl):
     g = synth.final_norm(wl.cfg_id, sh)
     x_host = synth.prefill_rows(wl.cfg_id, T, sh.hidden)
     sess = DecoderSession(sh, layers, embed=E, final_norm=g, n_ctx=wl.n_ctx, max_rows=T)
+    sess.set_fused_step(args.fused_step)
     x0 = torch.from_numpy(x_host).cuda()
     x = torch.empty_like(x0)
     xs = torch.zeros(1, sh.hidden, device="cuda")
@@ -272,7 +279,7 @@ def bench_greedy_stack(args, wl):
         "config": {"workload": wl.name, "layers": sh.n_layers, "hidden": sh.hidden, "heads": sh.n_heads,
                    "kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim, "ffn": sh.ffn, "vocab": sh.vocab,
                    "prefill_rows": T, "new_tokens": new_tokens, "batch": 1, "kv_dtype": sh.kvdtype,
-                   "n_ctx": wl.n_ctx, "parallelism": "none (1 GPU)"},
+                   "n_ctx": wl.n_ctx, "parallelism": "none (1 GPU)", "fused_step": args.fused_step},
     }
     if not args.no_kernel_profile:
         # device-clock spans: the prefill part eagerly, the decode step+head as a replayed graph
@@ -336,6 +343,7 @@ def bench_block(args, wl):
     x_host = synth.prefill_rows(wl.cfg_id, T, sh.hidden)
     rows_host = np.stack([synth.step_rows(wl.cfg_id, k, 1, sh.hidden)[0] for k in range(n_steps)])
     sess = DecoderSession(sh, layers, n_ctx=wl.n_ctx, max_rows=T)
+    sess.set_fused_step(args.fused_step)
     x0 = torch.from_numpy(x_host).cuda()
     x = torch.empty_like(x0)
     r0 = torch.from_numpy(rows_host).cuda()
@@ -396,7 +404,7 @@ def bench_block(args, wl):
         "config": {"workload": wl.name, "replicas": R, "hidden": sh.hidden, "heads": sh.n_heads,
                    "kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim, "ffn": sh.ffn, "prefill_rows": T,
                    "decode_steps": n_steps, "batch": 1, "kv_dtype": sh.kvdtype, "wdtype": sh.wdtype,
-                   "parallelism": "none (1 GPU)"},
+                   "parallelism": "none (1 GPU)", "fused_step": args.fused_step},
     }
     if R > 1:
         # the same job on one replica: its 100.7 MB of weights then stay in the 256 MB MALL
@@ -541,7 +549,7 @@ def bench_batched(args, wl):
         "decode_step_hbm_frac": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "config": {"workload": wl.name, "layers": sh.n_layers, "batch": Bn, "steps": n_steps,
                    "ctx_len_range": list(wl.ctx_len_range), "mean_ctx": float(lens.mean()), "n_ctx": n_ctx,
-                   "kv_dtype": sh.kvdtype, "parallelism": "none (1 GPU)"},
+                   "kv_dtype": sh.kvdtype, "parallelism": "none (1 GPU)", "fused_step": args.fused_step},
     }
     if not args.no_kernel_profile:
         with torch.cuda.stream(stream):

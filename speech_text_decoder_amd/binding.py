@@ -15,11 +15,13 @@ LIB_PATH = os.path.join(_HERE, "libsttd.so")
 OK, ERR_INVALID_ARG, ERR_OOM, ERR_BACKEND, ERR_CONTEXT_FULL, ERR_UNSUPPORTED = range(6)
 F32, BF16, F16 = 0, 1, 2
 LAST_ROW_FFN_ONLY = 1
-DEVERR_POSITION, DEVERR_SLAB, DEVERR_TOKEN = 1, 2, 4
+DEVERR_POSITION, DEVERR_SLAB, DEVERR_TOKEN, DEVERR_SYNC = 1, 2, 4, 8
+OPT_FUSED_STEP = 1
 
 EXPORTS = [
     "sttd_status_string", "sttd_kv_cache_alloc", "sttd_kv_cache_free", "sttd_kv_cache_clear", "sttd_kv_cache_view",
-    "sttd_workspace_alloc", "sttd_workspace_free", "sttd_workspace_error", "sttd_embed_gather",
+    "sttd_workspace_alloc", "sttd_workspace_free", "sttd_workspace_error", "sttd_workspace_set_option",
+    "sttd_embed_gather",
     "sttd_block_prefill", "sttd_block_step", "sttd_lm_head_argmax", "sttd_profile_enable", "sttd_profile_read",
     "sttd_clock_enable", "sttd_clock_disable", "sttd_clock_reset", "sttd_clock_read", "sttd_clock_spans",
 ]
@@ -65,6 +67,7 @@ def lib():
             "sttd_workspace_alloc": [P(BlockParams), i32, i32, i32, P(vp)],
             "sttd_workspace_free": [vp],
             "sttd_workspace_error": [vp, P(ctypes.c_uint32)],
+            "sttd_workspace_set_option": [vp, i32, i32],
             "sttd_embed_gather": [vp, i32, i32, i32, i32, vp, vp, vp, vp],
             "sttd_block_prefill": [P(BlockParams), P(BlockWeights), vp, vp, i32, i32, i32, i32, vp, ctypes.c_uint32,
                                    vp],
@@ -136,6 +139,10 @@ def workspace_alloc(params, max_rows, max_pos, vocab):
 
 def workspace_free(ws):
     _check(lib().sttd_workspace_free(ws), "sttd_workspace_free")
+
+
+def workspace_set_option(ws, option, value):
+    _check(lib().sttd_workspace_set_option(ws, option, value), "sttd_workspace_set_option")
 
 
 def workspace_error(ws):

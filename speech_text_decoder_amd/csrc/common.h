@@ -76,6 +76,28 @@ __device__ __forceinline__ void load8(const float* p, float* o, F32) {
     o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
 }
 
+// Access policies for fp32 data exchanged between workgroups. PlainMem uses
+// ordinary loads and stores. PubMem ("publish") uses ordinary loads but
+// device-scope relaxed atomic stores (sc1 on gfx950), which write through the
+// writer's L2 to memory. The fused decode step writes every value that another
+// workgroup of the same launch reads with PubMem, waits for the stores to
+// complete, then counts the hand-off. Each such buffer is written once per
+// launch, in one stage, and read only after that stage's hand-off. Kernel
+// boundaries invalidate the L2s, so no L2 holds a stale copy of its lines, and
+// the readers' plain loads fill from memory and share the fill across the XCD.
+struct PlainMem {
+    static __device__ __forceinline__ float ld(const float* p) { return *p; }
+    static __device__ __forceinline__ void ld8(const float* p, float* o) { load8(p, o, F32()); }
+    static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+};
+struct PubMem {
+    static __device__ __forceinline__ float ld(const float* p) { return *p; }
+    static __device__ __forceinline__ void ld8(const float* p, float* o) { load8(p, o, F32()); }
+    static __device__ __forceinline__ void st(float* p, float v) {
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+};
+
 // ------------------------------------------------------------ reductions
 // Cross-lane moves stay in the VALU (no LDS round trip). Inside a 16-lane row,
 // DPP: row_mirror pairs lane i with 15 - i, row_half_mirror i with 7 - i

@@ -6,350 +6,18 @@
 // page, file header; the causal mask of run() on the model page keeps
 // columns c <= r). Masked columns are never read, so no mask tensor exists.
 // Exponentials run in base 2 on scores pre-scaled by log2(e)/sqrt(d).
+#include "attn_rows.h"
 #include "common.h"
 #include "launch.h"
 
 namespace sttd {
 
 // ------------------------------------------------------------------ rows attention (decode)
-// Grid (row, kv head, split), NW waves per workgroup. The split's share of
-// cache rows [0, p] is ceil((p + 1) / n_splits) rows, so the work follows the
-// actual position although the grid is sized from a host bound.
-//
-// FUSE (decode rows, one row per slab): the workgroup starts from the raw
-// Q|K|V projection of its row: waves RMSNorm + rotate the G query heads of
-// the group into LDS, and the workgroup whose split holds position p also
-// norms + rotates the new key, writes key and value to cache row p and keeps
-// them in LDS, so no other kernel or workgroup is waited on. Without FUSE the
-// query rows come normed and rotated and the cache already holds every key
-// (prefill rows on an f32 cache).
-//
-// Groups of LPK = d/8 lanes read one cache row (16 bytes per lane for f16,
-// coalesced), two rows per step, and keep a running (max, sum, output) per
-// query head; groups merge by shuffles inside a wave and through LDS across
-// waves. One split: the workgroup writes o = O / L. Several: it writes the
-// partial (M, L, O); attn_combine merges the splits into o, or, when no
-// output is given, the consumer (the O-projection GEMV) merges them as it
-// loads its activations.
-struct RowsArgs {
-    const float* q;      // FUSE: raw projection rows [R][(nq + 2 nkv) d]; else q rows [R][nq d]
-    int64_t ldq;
-    int n_heads;
-    RowMap rm;
-    KVLayer kv;
-    int n_splits;
-    float* part;
-    float* out_f32;
-    uint16_t* out_bf16;
-    uint16_t* out_lo;
-    int64_t ldo;
-    uint32_t* err;
-    const void* q_gain;  // FUSE only
-    const void* k_gain;
-    float eps;
-    const float* rope;
-    int max_pos;
-    uint64_t* clk;
-};
-
-// One head vector of D values: RMSNorm with `gain`, NeoX rotation at `pos`,
-// times `scale`, into dst (LDS); one wave. Lane i < D/2 owns the pair (i, i + D/2).
-template <class GT, int D>
-__device__ __forceinline__ void norm_rope_head(const float* __restrict__ src, const typename GT::T* gain, float eps,
-                                               const float* __restrict__ rope, int pos, float scale, float* dst) {
-    constexpr int HALF = D / 2;
-    const int lane = threadIdx.x % WAVE;
-    const bool act = lane < HALF;
-    const float u0 = act ? src[lane] : 0.f, u1 = act ? src[lane + HALF] : 0.f;
-    const float rs = 1.0f / sqrtf(wave_sum(u0 * u0 + u1 * u1) / (float)D + eps);
-    if (act) {
-        const float a = u0 * rs * GT::ld(gain, lane), b = u1 * rs * GT::ld(gain, lane + HALF);
-        const float2 cs = reinterpret_cast<const float2*>(rope)[(int64_t)pos * HALF + lane];
-        dst[lane] = (a * cs.x - b * cs.y) * scale;
-        dst[lane + HALF] = (a * cs.y + b * cs.x) * scale;
-    }
-}
-
-// Fold another (m, l, o) running state into this one (base-2 exponents).
-template <int G>
-__device__ __forceinline__ void merge_state(float (&m)[G], float (&l)[G], float (&o)[G][8], const float (&m2)[G],
-                                            const float (&l2)[G], const float (&o2)[G][8]) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float M = fmaxf(m[g], m2[g]);
-        const float a = M == -INFINITY ? 0.f : exp2f(m[g] - M);
-        const float b = M == -INFINITY ? 0.f : exp2f(m2[g] - M);
-        l[g] = l[g] * a + l2[g] * b;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[g][i] = o[g][i] * a + o2[g][i] * b;
-        m[g] = M;
-    }
-}
-
-template <int G>
-__device__ __forceinline__ void step_state(float (&m)[G], float (&l)[G], float (&o)[G][8], const float (&s)[G],
-                                           const float (&vr)[8]) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float mn = fmaxf(m[g], s[g]);
-        const float alpha = exp2f(m[g] - mn);
-        const float p = exp2f(s[g] - mn);
-        l[g] = l[g] * alpha + p;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[g][i] = fmaf(o[g][i], alpha, p * vr[i]);
-        m[g] = mn;
-    }
-}
-
-// Sum over the LPK lanes that share one cache row.
-template <int LPK>
-__device__ __forceinline__ float group_sum(float v) {
-    return LPK == 16 ? row16_sum(v) : row8_sum(v);
-}
-
+// The item body (attn_rows.h) runs one (row, KV head, split) per workgroup.
 template <class KT, class GT, int D, int G, int NW, bool FUSE>
 __global__ __launch_bounds__(NW * 64) void attn_rows_kernel(RowsArgs a) {
-    typedef typename KT::T T;
-    constexpr int LPK = D / 8;                 // lanes per cache row
-    constexpr int GPW = WAVE / LPK;            // groups per wave
-    constexpr int NG = NW * GPW;               // groups per workgroup
-    constexpr int HALF = D / 2;
-    constexpr int SLOTS = NW * (16 / LPK);     // states per workgroup after the in-wave merge
-    static_assert(LPK == 8 || LPK == 16, "head_dim 64 or 128");
-    __shared__ float q_lds[G][D];
-    __shared__ float kn_lds[D], vn_lds[D];
-    __shared__ float wm_lds[SLOTS][G], wl_lds[SLOTS][G];
-    __shared__ float wo_lds[SLOTS][G][D];
-
     clock_begin(a.clk);
-    const int r = blockIdx.x, j = blockIdx.y, split = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
-    const int grp = tid / LPK, sub = tid % LPK;
-    const float scale = 1.4426950408889634f / sqrtf((float)D);
-
-    // 1. the row's position and slab, this wave's raw head items of the
-    //    projection (items: G query heads, then the key, then the value; wave w
-    //    takes items w, w + NW, ...) and their gains: independent loads, all
-    //    issued before the first wait (addresses clamped, not branched around)
-    //    (decode rows always come with device position and slab arrays)
-    const int pos_v = FUSE ? a.rm.pos[r] : row_pos(a.rm, r);
-    const int seq_v = FUSE ? a.rm.seq[r] : row_seq(a.rm, r);
-    constexpr int IPW = (G + 2 + NW - 1) / NW;  // items per wave
-    const int lc = lane < HALF ? lane : 0;
-    float u0[IPW], u1[IPW];
-    typename GT::T g0r[IPW], g1r[IPW];
-    if (FUSE) {
-        const float* src = a.q + (int64_t)r * a.ldq;
-#pragma unroll
-        for (int k = 0; k < IPW; ++k) {
-            const int it = wave + k * NW;
-            const int itc = it < G + 2 ? it : 0;
-            const int col = itc < G ? (j * G + itc) * D
-                                    : (itc == G ? (a.n_heads + j) * D : (a.n_heads + a.kv.n_kv + j) * D);
-            u0[k] = src[col + lc];
-            u1[k] = src[col + lc + HALF];
-            const typename GT::T* gain = (const typename GT::T*)(itc < G ? a.q_gain : a.k_gain);
-            g0r[k] = gain[lc];
-            g1r[k] = gain[lc + HALF];
-        }
-    }
-    // keep the scheduler from pulling the first use of a loaded value (and its
-    // wait) above the loads issued after it
-    __builtin_amdgcn_sched_barrier(0);
-    // 2. position-dependent loads: the rotation row, then the first cache rows of each group
-    const int pos = pos_v, seq = seq_v;
-    const bool ok = pos >= 0 && pos < a.kv.n_ctx && pos < (FUSE ? a.max_pos : a.kv.n_ctx) && seq >= 0 &&
-                    seq < a.kv.n_seq;
-    if (!ok && tid == 0 && split == 0 && j == 0) record_error(a.err, pos < 0 || pos >= a.kv.n_ctx ? 1u : 2u);
-    float2 cs = make_float2(1.f, 0.f);
-    if (FUSE) cs = reinterpret_cast<const float2*>(a.rope)[(int64_t)(ok ? pos : 0) * HALF + lc];
-    const int n_keys = ok ? pos + 1 : 0;
-    const int chunk = (n_keys + a.n_splits - 1) / a.n_splits;
-    const int c0 = split * chunk;
-    const int c1 = min(c0 + chunk, n_keys);
-    const bool owner = FUSE && ok && c0 <= pos && pos < c1;  // this split holds the new key
-    const int64_t slab = ((int64_t)(ok ? seq : 0) * a.kv.n_kv + j) * a.kv.n_ctx * D;
-    const T* Kp = (const T*)a.kv.k + slab + sub * 8;
-    const T* Vp = (const T*)a.kv.v + slab + sub * 8;
-    const int cend = owner ? pos : c1;  // the new key (owner) is folded in from LDS below
-    // RIF rows per group in flight: row c + q * NG for q < RIF (clamped to row 0 past the end)
-    constexpr int RIF = G <= 2 ? 4 : (G == 4 ? 2 : 1);
-    constexpr int STEP = RIF * NG;
-    int c = c0 + grp;
-    float kr[RIF][8], vr[RIF][8];
-#pragma unroll
-    for (int q = 0; q < RIF; ++q) {
-        const int cq = c + q * NG < cend ? c + q * NG : 0;
-        load8(Kp + (int64_t)cq * D, kr[q], KT());
-        load8(Vp + (int64_t)cq * D, vr[q], KT());
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // 3. finish the head items: RMSNorm + rotation (queries, key); the owner
-    //    writes key and value to cache row pos
-    if (FUSE) {
-#pragma unroll
-        for (int k = 0; k < IPW; ++k) {
-            const int it = wave + k * NW;
-            if (it >= G + 2 || !ok) continue;
-            const float v0 = lane < HALF ? u0[k] : 0.f, v1 = lane < HALF ? u1[k] : 0.f;
-            if (it <= G) {
-                const float rs = 1.0f / sqrtf(wave_sum(v0 * v0 + v1 * v1) / (float)D + a.eps);
-                if (lane < HALF) {
-                    const float x0 = v0 * rs * GT::cvt(g0r[k]), x1 = v1 * rs * GT::cvt(g1r[k]);
-                    const float r0 = x0 * cs.x - x1 * cs.y, r1 = x0 * cs.y + x1 * cs.x;
-                    if (it < G) {
-                        q_lds[it][lane] = r0 * scale;
-                        q_lds[it][lane + HALF] = r1 * scale;
-                    } else if (owner) {
-                        kn_lds[lane] = r0;
-                        kn_lds[lane + HALF] = r1;
-                        KT::st((T*)a.kv.k, slab + (int64_t)pos * D + lane, r0);
-                        KT::st((T*)a.kv.k, slab + (int64_t)pos * D + lane + HALF, r1);
-                    }
-                }
-            } else if (owner && lane < HALF) {
-                vn_lds[lane] = v0;
-                vn_lds[lane + HALF] = v1;
-                KT::st((T*)a.kv.v, slab + (int64_t)pos * D + lane, v0);
-                KT::st((T*)a.kv.v, slab + (int64_t)pos * D + lane + HALF, v1);
-            }
-        }
-    } else {
-        for (int t = tid; t < G * D; t += NW * 64)
-            q_lds[t / D][t % D] = ok ? a.q[(int64_t)r * a.ldq + (j * G + t / D) * D + t % D] * scale : 0.f;
-    }
-    __syncthreads();
-
-    float qv[G][8];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qv[g][i] = q_lds[g][sub * 8 + i];
-    float m[G], l[G], o[G][8];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        m[g] = -INFINITY;
-        l[g] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[g][i] = 0.f;
-    }
-    // 4. cache rows [c0, cend): RIF per group per step, the next RIF in flight
-    for (; c < cend; c += STEP) {
-        float sc[RIF][G];
-#pragma unroll
-        for (int q = 0; q < RIF; ++q) {
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float t = 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) t = fmaf(qv[g][i], kr[q][i], t);
-                sc[q][g] = group_sum<LPK>(t);
-            }
-        }
-        float vcur[RIF][8];
-#pragma unroll
-        for (int q = 0; q < RIF; ++q)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) vcur[q][i] = vr[q][i];
-        const int cn = c + STEP;
-        if (cn < cend) {
-#pragma unroll
-            for (int q = 0; q < RIF; ++q) {
-                const int cq = cn + q * NG < cend ? cn + q * NG : cn;
-                load8(Kp + (int64_t)cq * D, kr[q], KT());
-                load8(Vp + (int64_t)cq * D, vr[q], KT());
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < RIF; ++q)
-            if (c + q * NG < cend) step_state<G>(m, l, o, sc[q], vcur[q]);
-    }
-    // 5. the new key (held in LDS by the owner), folded in by group 0
-    if (owner && grp == 0) {
-        float kn[8], vn[8], s[G];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            kn[i] = kn_lds[sub * 8 + i];
-            vn[i] = vn_lds[sub * 8 + i];
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float t1 = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) t1 = fmaf(qv[g][i], kn[i], t1);
-            s[g] = group_sum<LPK>(t1);
-        }
-        step_state<G>(m, l, o, s, vn);
-    }
-    // 6. merge across rows of the wave (lane bits 4, 5) with permlane swaps; the
-    //    16-lane rows (for head_dim 64: both 8-lane groups of a row) then go to LDS
-    {
-        float m2[G], l2[G], o2[G][8];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            m2[g] = xor16(m[g]);
-            l2[g] = xor16(l[g]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o2[g][i] = xor16(o[g][i]);
-        }
-        merge_state<G>(m, l, o, m2, l2, o2);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            m2[g] = xor32(m[g]);
-            l2[g] = xor32(l[g]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o2[g][i] = xor32(o[g][i]);
-        }
-        merge_state<G>(m, l, o, m2, l2, o2);
-    }
-    if (lane < 16) {
-        const int slot = wave * (16 / LPK) + lane / LPK;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            if (sub == 0) {
-                wm_lds[slot][g] = m[g];
-                wl_lds[slot][g] = l[g];
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) wo_lds[slot][g][sub * 8 + i] = o[g][i];
-        }
-    }
-    __syncthreads();
-    // 7. merge the slots; write o (one split) or the split's partial record
-    for (int t = tid; t < G * D; t += NW * 64) {
-        const int g = t / D, e = t % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < SLOTS; ++w) M = fmaxf(M, wm_lds[w][g]);
-        float L = 0.f, O = 0.f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int w = 0; w < SLOTS; ++w) {
-                const float f = exp2f(wm_lds[w][g] - M);
-                L += f * wl_lds[w][g];
-                O += f * wo_lds[w][g][e];
-            }
-        }
-        if (a.n_splits == 1) {
-            const float v = L > 0.f ? O / L : 0.f;
-            const int64_t idx = (int64_t)r * a.ldo + (j * G + g) * D + e;
-            if (a.out_f32) {
-                a.out_f32[idx] = v;
-            } else {
-                uint16_t hi, lo;
-                split_bf16(v, hi, lo);
-                a.out_bf16[idx] = hi;
-                if (a.out_lo) a.out_lo[idx] = lo;
-            }
-        } else {
-            float* pp = a.part + (((int64_t)r * a.n_heads + j * G + g) * a.n_splits + split) * (D + 4);
-            if (e == 0) {
-                pp[0] = M;
-                pp[1] = L;
-            }
-            pp[4 + e] = O;
-        }
-    }
+    attn_rows_item<KT, GT, D, G, NW, FUSE>(a, blockIdx.x, blockIdx.y, blockIdx.z);
     clock_end(a.clk);
 }
 

@@ -94,6 +94,10 @@ class DecoderSession:
         return (_wrap(k, n, dt, self.device).view(sh.n_kv_heads, self.n_ctx, sh.head_dim),
                 _wrap(v, n, dt, self.device).view(sh.n_kv_heads, self.n_ctx, sh.head_dim))
 
+    def set_fused_step(self, enabled: bool):
+        """STTD_OPT_FUSED_STEP: single-row steps as one persistent launch per block (default on)."""
+        B.workspace_set_option(self.ws, B.OPT_FUSED_STEP, 1 if enabled else 0)
+
     def error_bits(self):
         return B.workspace_error(self.ws)
 
