@@ -157,6 +157,21 @@ sttd_status sttd_workspace_error(sttd_workspace *ws, uint32_t *bits /* host */);
 sttd_status sttd_embed_gather(const void *embed, sttd_dtype wtype, int vocab, int hidden, int B,
                               const int32_t *ids, float *x, sttd_workspace *ws, void *stream);
 
+/* Prompt/audio injection before the first block: the elementwise blend of the
+ * batched prefill graphs on the Qwen3-ASR model page (build_prefill_graph_batched:
+ * x = x * keep_mask + audio_dense) and of the MOSS page (build_injection and
+ * its chunked prefill): x[t, :] = embed[ids[t], :] * keep[t] + audio_dense[t, :]
+ * for t < T. ids [T] int32; keep [T] fp32 (the pages put 0 at the audio
+ * positions and 1 elsewhere); audio_dense [T, hidden] fp32 (the encoder's rows
+ * scattered to the audio positions, zero elsewhere); x [T, hidden] fp32 out.
+ * With one contiguous audio block this equals the 3-way concat of prefix
+ * embeddings, audio rows and suffix embeddings in the single-sequence
+ * build_prefill_graph. A device id outside [0, vocab) contributes a zero row
+ * and records STTD_DEVERR_TOKEN when ws is non-NULL. */
+sttd_status sttd_embed_inject(const void *embed, sttd_dtype wtype, int vocab, int hidden, int T,
+                              const int32_t *ids, const float *keep, const float *audio_dense, float *x,
+                              sttd_workspace *ws, void *stream);
+
 /* Causal prefill of T rows of one sequence through one block
  * (causal_lm::block_prefill as called by build_prefill_graph).
  * Row t sits at position pos0 + t; its K and V are written at cache row
@@ -168,6 +183,23 @@ sttd_status sttd_embed_gather(const void *embed, sttd_dtype wtype, int vocab, in
 sttd_status sttd_block_prefill(const sttd_block_params *p, const sttd_block_weights *w, sttd_workspace *ws,
                                sttd_kv_cache *kv, int layer, int seq, int pos0, int T, float *x, uint32_t flags,
                                void *stream);
+
+/* Causal prefill of n sequences through one block in one call: the batched
+ * prefill of the Qwen3-ASR model page (run_batch: build_prefill_graph_batched
+ * over block_prefill_batched), with the prompts packed back to back instead of
+ * padded to the longest. Sequence i (host arrays, i < n <= 64) has T[i] >= 1
+ * rows at positions pos0[i] .. pos0[i] + T[i] - 1 in slab seq[i] (distinct);
+ * its rows attend only cache rows [0, position] of its own slab (rows below
+ * pos0[i] must hold earlier positions). x [sum T[i], hidden] fp32 holds the
+ * sequences' rows in order and is overwritten with the block outputs. The
+ * projections run once over all rows, so the weights are read once for the
+ * batch. sum T[i] <= the workspace's max_rows; pos0[i] + T[i] > n_ctx:
+ * STTD_ERR_CONTEXT_FULL; n outside [1, 64], a bad or repeated slab, T[i] < 1
+ * or pos0[i] < 0: STTD_ERR_INVALID_ARG. */
+sttd_status sttd_block_prefill_batched(const sttd_block_params *p, const sttd_block_weights *w, sttd_workspace *ws,
+                                       sttd_kv_cache *kv, int layer, int n, const int32_t *seq /* host */,
+                                       const int32_t *pos0 /* host */, const int32_t *T /* host */, float *x,
+                                       void *stream);
 
 /* One decode step of B rows through one block (causal_lm::block_step and
  * block_step_batched in build_step_graph / build_step_graph_batched).

@@ -202,6 +202,17 @@ def block_rows_subset(x, pos0, w, p, cache, layer, sample_rows):
 
 # ---------------------------------------------------------------- head
 
+def inject(embed, ids, keep, audio_dense):
+    """Prompt/audio injection ahead of the first block. The batched prefill
+    graph on the Qwen3-ASR model page (build_prefill_graph_batched) and the
+    MOSS page (build_injection, prefill_chunked) blend the token embeddings
+    with the encoder rows: x = embed[ids] * keep + audio_dense. keep is 0 at
+    the audio positions and 1 elsewhere, and audio_dense holds the encoder
+    rows at the audio positions and zeros elsewhere."""
+    rows = f64(embed)[np.asarray(ids)]
+    return rows * f64(keep)[:, None] + f64(audio_dense)
+
+
 def final_logits(x_rows, final_gain, embed, eps):
     """Final RMSNorm then the tied lm_head: logits = E @ (RMSNorm(x) * g)."""
     z = rms_norm(x_rows, final_gain, eps)

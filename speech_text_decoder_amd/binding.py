@@ -21,8 +21,9 @@ OPT_FUSED_STEP = 1
 EXPORTS = [
     "sttd_status_string", "sttd_kv_cache_alloc", "sttd_kv_cache_free", "sttd_kv_cache_clear", "sttd_kv_cache_view",
     "sttd_workspace_alloc", "sttd_workspace_free", "sttd_workspace_error", "sttd_workspace_set_option",
-    "sttd_embed_gather",
-    "sttd_block_prefill", "sttd_block_step", "sttd_lm_head_argmax", "sttd_profile_enable", "sttd_profile_read",
+    "sttd_embed_gather", "sttd_embed_inject",
+    "sttd_block_prefill", "sttd_block_prefill_batched", "sttd_block_step", "sttd_lm_head_argmax",
+    "sttd_profile_enable", "sttd_profile_read",
     "sttd_clock_enable", "sttd_clock_disable", "sttd_clock_reset", "sttd_clock_read", "sttd_clock_spans",
 ]
 
@@ -69,8 +70,11 @@ def lib():
             "sttd_workspace_error": [vp, P(ctypes.c_uint32)],
             "sttd_workspace_set_option": [vp, i32, i32],
             "sttd_embed_gather": [vp, i32, i32, i32, i32, vp, vp, vp, vp],
+            "sttd_embed_inject": [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp],
             "sttd_block_prefill": [P(BlockParams), P(BlockWeights), vp, vp, i32, i32, i32, i32, vp, ctypes.c_uint32,
                                    vp],
+            "sttd_block_prefill_batched": [P(BlockParams), P(BlockWeights), vp, vp, i32, i32, P(i32), P(i32), P(i32),
+                                           vp, vp],
             "sttd_block_step": [P(BlockParams), P(BlockWeights), vp, vp, i32, i32, vp, vp, i32, vp, vp],
             "sttd_lm_head_argmax": [vp, vp, i32, i32, i32, f32, vp, i32, vp, i64, vp, vp, vp, vp, vp],
             "sttd_profile_enable": [ctypes.c_uint32],
@@ -155,9 +159,22 @@ def embed_gather(embed, wtype, vocab, hidden, B, ids, x, ws=0, stream=0):
     _check(lib().sttd_embed_gather(embed, wtype, vocab, hidden, B, ids, x, ws, stream), "sttd_embed_gather")
 
 
+def embed_inject(embed, wtype, vocab, hidden, T, ids, keep, audio_dense, x, ws=0, stream=0):
+    _check(lib().sttd_embed_inject(embed, wtype, vocab, hidden, T, ids, keep, audio_dense, x, ws, stream),
+           "sttd_embed_inject")
+
+
 def block_prefill(params, weights, ws, kv, layer, seq, pos0, T, x, flags=0, stream=0):
     _check(lib().sttd_block_prefill(ctypes.byref(params), ctypes.byref(weights), ws, kv, layer, seq, pos0, T, x,
                                     flags, stream), "sttd_block_prefill")
+
+
+def block_prefill_batched(params, weights, ws, kv, layer, seq, pos0, T, x, stream=0):
+    """seq, pos0, T: host sequences of ints (one entry per packed sequence)."""
+    n = len(T)
+    arr = ctypes.c_int32 * n
+    _check(lib().sttd_block_prefill_batched(ctypes.byref(params), ctypes.byref(weights), ws, kv, layer, n,
+                                            arr(*seq), arr(*pos0), arr(*T), x, stream), "sttd_block_prefill_batched")
 
 
 def block_step(params, weights, ws, kv, layer, B, seq, pos, pos_bound, x, stream=0):

@@ -1,6 +1,8 @@
 // abi.hip - the C ABI of include/sttd.h: validation, allocation, and the
 // kernel sequences of one block call.
 #include <math.h>
+
+#include <algorithm>
 #include <string.h>
 
 #include <mutex>
@@ -39,6 +41,8 @@ struct sttd_workspace {
     uint32_t* err;                 // [1]
     int32_t* iota;                 // [max_rows]: 0, 1, ... (slab b of row b when no slab ids are given)
     float* hbuf;                   // [hidden]: the fused step's attention residual
+    int32_t* rowpos;               // [max_rows]: per-row positions of a packed batched prefill
+    int32_t* rowseq;               // [max_rows]: per-row slabs of a packed batched prefill
     uint32_t* sync;                // [kStepSyncWords] hand-off counters of the fused step (zero between launches)
     bool fused_step;               // STTD_OPT_FUSED_STEP
 };
@@ -203,18 +207,21 @@ int choose_splits(int rows, int n_kv, int pos_bound, int part_cap) {
     return s < 1 ? 1 : s;
 }
 
-// One block over R rows. prefill_seq >= 0: a causal prefill of one slab at
-// positions rm.pos0.. (may use the MFMA flash kernel); otherwise decode rows.
+// One block over R rows. prefill: a causal prefill, of one slab at positions
+// rm.pos0.. or, with segs, of several sequences packed back to back (rm then
+// holds the expanded per-row positions and slabs); otherwise decode rows.
 sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, sttd_workspace* ws,
                       const sttd_kv_cache* kv, int layer, int R, RowMap rm, int pos_bound, bool prefill,
-                      bool last_row_only, float* x, hipStream_t s) {
+                      bool last_row_only, float* x, hipStream_t s, const Segments* segs = nullptr) {
     const WType wt = p->wtype == STTD_BF16 ? W_BF16 : W_F32;
     const int H = p->hidden, nq = p->n_heads, nkv = p->n_kv_heads, d = p->head_dim, I = p->ffn;
     const int qd = nq * d, kvd = nkv * d, qkv_cols = qd + 2 * kvd;
     const float eps = p->rms_eps;
     const KVLayer kl = kv_layer(kv, layer);
     const bool mfma = wt == W_BF16 && R > kGemvMaxRows;
-    const bool flash = mfma && prefill && kl.type == KV_F16;
+    bool flash = mfma && prefill && kl.type == KV_F16;
+    if (flash && segs)  // every packed sequence must be long enough for the flash tiles' query layout
+        for (int i = 0; i < segs->n; ++i) flash = flash && segs->len[i] > kGemvMaxRows;
     const bool split = R <= kSplitMaxRows;
     uint16_t* xn_lo = split ? ws->xn + (size_t)ws->max_rows * H : nullptr;
     uint16_t* ao = (uint16_t*)ws->attn_o;
@@ -278,7 +285,26 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
     }
     int splits = 1;
     bool defer = false;
-    if (flash) {
+    if (segs) {
+        // packed sequences: each attends its own slab, causally from its pos0
+        for (int i = 0; i < segs->n; ++i) {
+            const int r0 = segs->start[i], Ti = segs->len[i], p0 = segs->pos0[i];
+            uint16_t* aoi = mfma ? ao + (size_t)r0 * qd : nullptr;
+            uint16_t* aoli = mfma && ao_lo ? ao_lo + (size_t)r0 * qd : nullptr;
+            if (flash) {
+                ProfScope ps(STTD_KERN_ATTN_PREFILL, s);
+                TRY(launch_attn_prefill((const uint16_t*)ws->qbuf + (size_t)r0 * qd, qd, Ti, p0, segs->seq[i], nq,
+                                        kl, aoi, aoli, qd, s));
+            } else {
+                const RowMap ri{rm.pos + r0, rm.seq + r0, 0, 0};
+                const int sp = choose_splits(Ti, nkv, p0 + Ti, ws->part_cap);
+                ProfScope ps(STTD_KERN_ATTN_ROWS, s);
+                TRY(launch_attn_rows((const float*)ws->qbuf + (size_t)r0 * qd, qd, Ti, nq, ri, kl, sp,
+                                     (p0 + Ti + sp - 1) / sp, ws->part, mfma ? nullptr : ws->attn_o + (size_t)r0 * qd,
+                                     aoi, aoli, qd, ws->err, nullptr, wt, s));
+            }
+        }
+    } else if (flash) {
         ProfScope ps(STTD_KERN_ATTN_PREFILL, s);
         TRY(launch_attn_prefill((const uint16_t*)ws->qbuf, qd, R, rm.pos0, rm.seq0, nq, kl, ao, ao_lo, qd, s));
     } else {
@@ -463,6 +489,8 @@ sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int m
     const size_t o_iota = take(R * sizeof(int32_t));
     const size_t o_sync = take(kStepSyncWords * sizeof(uint32_t));
     const size_t o_h = take((size_t)H * sizeof(float));
+    const size_t o_rowpos = take(R * sizeof(int32_t));
+    const size_t o_rowseq = take(R * sizeof(int32_t));
     sttd_workspace* ws = new (std::nothrow) sttd_workspace();
     if (!ws) return STTD_ERR_OOM;
     ws->p = *p;
@@ -489,6 +517,8 @@ sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int m
     ws->iota = (int32_t*)(b + o_iota);
     ws->sync = (uint32_t*)(b + o_sync);
     ws->hbuf = (float*)(b + o_h);
+    ws->rowpos = (int32_t*)(b + o_rowpos);
+    ws->rowseq = (int32_t*)(b + o_rowseq);
     ws->fused_step = false;
     // RoPE table in fp64 on the host: pair i of position pos turns by pos * theta^(-2i/d)
     std::vector<float> table((size_t)max_pos * d);
@@ -542,7 +572,18 @@ sttd_status sttd_embed_gather(const void* embed, sttd_dtype wtype, int vocab, in
                               float* x, sttd_workspace* ws, void* stream) {
     if (!embed || !ids || !x || vocab <= 0 || hidden <= 0 || B <= 0) return STTD_ERR_INVALID_ARG;
     if (wtype != STTD_BF16 && wtype != STTD_F32) return STTD_ERR_UNSUPPORTED;
-    TRY(launch_embed_gather(embed, wtype == STTD_BF16 ? W_BF16 : W_F32, vocab, hidden, B, ids, x,
+    TRY(launch_embed_gather(embed, wtype == STTD_BF16 ? W_BF16 : W_F32, vocab, hidden, B, ids, nullptr, nullptr, x,
+                            ws ? ws->err : nullptr, (hipStream_t)stream));
+    return STTD_OK;
+}
+
+sttd_status sttd_embed_inject(const void* embed, sttd_dtype wtype, int vocab, int hidden, int T, const int32_t* ids,
+                              const float* keep, const float* audio_dense, float* x, sttd_workspace* ws,
+                              void* stream) {
+    if (!embed || !ids || !keep || !audio_dense || !x || vocab <= 0 || hidden <= 0 || T <= 0)
+        return STTD_ERR_INVALID_ARG;
+    if (wtype != STTD_BF16 && wtype != STTD_F32) return STTD_ERR_UNSUPPORTED;
+    TRY(launch_embed_gather(embed, wtype == STTD_BF16 ? W_BF16 : W_F32, vocab, hidden, T, ids, keep, audio_dense, x,
                             ws ? ws->err : nullptr, (hipStream_t)stream));
     return STTD_OK;
 }
@@ -570,6 +611,38 @@ sttd_status sttd_block_prefill(const sttd_block_params* p, const sttd_block_weig
     RowMap rm{nullptr, nullptr, pos0, seq};
     return run_block(p, w, ws, kv, layer, T, rm, pos0 + T, true, (flags & STTD_LAST_ROW_FFN_ONLY) != 0, x,
                      (hipStream_t)stream);
+}
+
+sttd_status sttd_block_prefill_batched(const sttd_block_params* p, const sttd_block_weights* w, sttd_workspace* ws,
+                                       sttd_kv_cache* kv, int layer, int n, const int32_t* seq, const int32_t* pos0,
+                                       const int32_t* T, float* x, void* stream) {
+    if (!seq || !pos0 || !T || n < 1 || n > kMaxSegments) return STTD_ERR_INVALID_ARG;
+    Segments sg{};
+    sg.n = n;
+    int64_t rows = 0;
+    for (int i = 0; i < n; ++i) {
+        if (T[i] < 1 || pos0[i] < 0 || !kv || seq[i] < 0 || seq[i] >= kv->n_seq) return STTD_ERR_INVALID_ARG;
+        for (int j = 0; j < i; ++j)
+            if (seq[j] == seq[i]) return STTD_ERR_INVALID_ARG;  // two sequences in one slab
+        sg.start[i] = (int)rows;
+        sg.len[i] = T[i];
+        sg.pos0[i] = pos0[i];
+        sg.seq[i] = seq[i];
+        rows += T[i];
+    }
+    if (rows > INT32_MAX) return STTD_ERR_INVALID_ARG;
+    const sttd_status st = check_block(p, w, ws, kv, layer, (int)rows, x);
+    if (st != STTD_OK) return st;
+    int bound = 0;
+    for (int i = 0; i < n; ++i) {
+        if ((int64_t)pos0[i] + T[i] > kv->n_ctx || (int64_t)pos0[i] + T[i] > ws->max_pos)
+            return STTD_ERR_CONTEXT_FULL;
+        bound = std::max(bound, pos0[i] + T[i]);
+    }
+    hipStream_t s = (hipStream_t)stream;
+    TRY(launch_expand_segments(sg, (int)rows, ws->rowpos, ws->rowseq, s));
+    RowMap rm{ws->rowpos, ws->rowseq, 0, 0};
+    return run_block(p, w, ws, kv, layer, (int)rows, rm, bound, true, false, x, s, &sg);
 }
 
 sttd_status sttd_block_step(const sttd_block_params* p, const sttd_block_weights* w, sttd_workspace* ws,

@@ -89,26 +89,56 @@ hipError_t launch_qk_norm_rope_kv(const float* qkv, int64_t ldqkv, int R, WType 
 
 // ------------------------------------------------------------------ embedding gather
 // x[b, :] = embed[ids[b], :] widened to fp32 (the tied table's get_rows in
-// build_step_graph). An id outside [0, vocab) gives a zero row and an error bit.
+// build_step_graph). With keep and/or dense, the prompt/audio injection blend
+// of the batched prefill graphs: x[b, :] = embed[ids[b], :] * keep[b] +
+// dense[b, :] (keep broadcasts over the hidden axis). An id outside
+// [0, vocab) contributes a zero row and sets an error bit.
 template <class WT>
 __global__ __launch_bounds__(256) void embed_gather_kernel(const typename WT::T* __restrict__ E, int vocab,
                                                            int hidden, const int32_t* __restrict__ ids,
-                                                           float* __restrict__ x, uint32_t* err) {
+                                                           const float* __restrict__ keep,
+                                                           const float* __restrict__ dense, float* __restrict__ x,
+                                                           uint32_t* err) {
     const int b = blockIdx.x;
     const int id = ids[b];
     const bool ok = id >= 0 && id < vocab;
     if (!ok && threadIdx.x == 0) record_error(err, 4u);
+    const float kb = keep ? keep[b] : 1.f;
     float* xr = x + (int64_t)b * hidden;
-    for (int i = threadIdx.x; i < hidden; i += 256) xr[i] = ok ? WT::ld(E, (int64_t)id * hidden + i) : 0.f;
+    const float* dr = dense ? dense + (int64_t)b * hidden : nullptr;
+    for (int i = threadIdx.x; i < hidden; i += 256) {
+        const float e = ok ? WT::ld(E, (int64_t)id * hidden + i) : 0.f;
+        xr[i] = dense ? e * kb + dr[i] : (keep ? e * kb : e);
+    }
 }
 
 hipError_t launch_embed_gather(const void* embed, WType wt, int vocab, int hidden, int B, const int32_t* ids,
-                               float* x, uint32_t* err, hipStream_t s) {
+                               const float* keep, const float* dense, float* x, uint32_t* err, hipStream_t s) {
     if (B <= 0) return hipSuccess;
     if (wt == W_BF16)
-        embed_gather_kernel<BF16><<<B, 256, 0, s>>>((const uint16_t*)embed, vocab, hidden, ids, x, err);
+        embed_gather_kernel<BF16><<<B, 256, 0, s>>>((const uint16_t*)embed, vocab, hidden, ids, keep, dense, x, err);
     else
-        embed_gather_kernel<F32><<<B, 256, 0, s>>>((const float*)embed, vocab, hidden, ids, x, err);
+        embed_gather_kernel<F32><<<B, 256, 0, s>>>((const float*)embed, vocab, hidden, ids, keep, dense, x, err);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ packed-sequence row maps
+// Row r of a packed batched prefill: its sequence is the last one starting at
+// or before r; position pos0 + (r - start), slab seq.
+__global__ __launch_bounds__(256) void expand_segments_kernel(Segments sg, int R, int32_t* __restrict__ pos,
+                                                              int32_t* __restrict__ seq) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= R) return;
+    int i = 0;
+    for (int k = 1; k < sg.n; ++k)
+        if (sg.start[k] <= r) i = k;
+    pos[r] = sg.pos0[i] + (r - sg.start[i]);
+    seq[r] = sg.seq[i];
+}
+
+hipError_t launch_expand_segments(const Segments& sg, int R, int32_t* pos, int32_t* seq, hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    expand_segments_kernel<<<(R + 255) / 256, 256, 0, s>>>(sg, R, pos, seq);
     return hipGetLastError();
 }
 

@@ -35,6 +35,16 @@ struct RowMap {
 __device__ __forceinline__ int row_pos(const RowMap& m, int r) { return m.pos ? m.pos[r] : m.pos0 + r; }
 __device__ __forceinline__ int row_seq(const RowMap& m, int r) { return m.seq ? m.seq[r] : (m.seq0 < 0 ? r : m.seq0); }
 
+// Sequences packed back to back in one batched prefill call: sequence i holds
+// rows [start[i], start[i] + len[i]) at positions pos0[i].. of slab seq[i].
+constexpr int kMaxSegments = 64;
+struct Segments {
+    int n;
+    int start[kMaxSegments], len[kMaxSegments], pos0[kMaxSegments], seq[kMaxSegments];
+};
+// pos[r], seq[r] of every packed row r < R.
+hipError_t launch_expand_segments(const Segments& sg, int R, int32_t* pos, int32_t* seq, hipStream_t s);
+
 // KV slab addressing for one layer: slab s, head j, row c at
 // base + ((s * n_kv + j) * n_ctx + c) * d elements.
 struct KVLayer {
@@ -70,8 +80,9 @@ hipError_t launch_rmsnorm_rows_bf16(const float* x, int64_t ldx, const void* gai
 // Per-head Q/K RMSNorm + NeoX RoPE (table) + K/V cache write; q written to q_out
 // as fp32 (q_f16 false) or f16 (q_f16 true) with row stride ldq.
 hipError_t launch_qk_norm_rope_kv(const float* qkv, int64_t ldqkv, int R, WType gt, const QkRope& q, hipStream_t s);
+// x[b] = embed[ids[b]] * (keep ? keep[b] : 1) + (dense ? dense[b] : 0), b < B
 hipError_t launch_embed_gather(const void* embed, WType wt, int vocab, int hidden, int B, const int32_t* ids,
-                               float* x, uint32_t* err, hipStream_t s);
+                               const float* keep, const float* dense, float* x, uint32_t* err, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 // ---- GEMV family (kernels_gemv.hip): rows <= 4 per group, fp32 activations.

@@ -60,6 +60,24 @@ class DecoderSession:
                             flags, s)
         return x
 
+    def prefill_batched(self, x, T, seq, pos0=None, layers=None, stream=None):
+        """x: cuda float32 [sum(T), hidden], the sequences packed back to back;
+        sequence i has T[i] rows at positions pos0[i].. of slab seq[i]."""
+        s = stream_handle(stream)
+        pos0 = [0] * len(T) if pos0 is None else list(pos0)
+        idx = range(len(self.layer_weights)) if layers is None else layers
+        for l in idx:
+            B.block_prefill_batched(self.params, self.layer_weights[l], self.ws, self.kv, l, list(seq), pos0,
+                                    list(T), x.data_ptr(), s)
+        return x
+
+    def inject(self, ids, keep, audio_dense, x, stream=None):
+        """x[t] = embed[ids[t]] * keep[t] + audio_dense[t] (cuda tensors)."""
+        B.embed_inject(self.embed.data_ptr(), WT_CODE[self.shape.wdtype], self.vocab, self.shape.hidden, ids.shape[0],
+                       ids.data_ptr(), keep.data_ptr(), audio_dense.data_ptr(), x.data_ptr(), self.ws,
+                       stream_handle(stream))
+        return x
+
     def step(self, x, pos, seq=None, pos_bound=None, layers=None, stream=None):
         """x: cuda float32 [B, hidden]; pos: cuda int32 [B]; seq: cuda int32 [B] or None (row b -> slab b)."""
         s = stream_handle(stream)

@@ -9,6 +9,15 @@ Head counts (16 query, 8 KV), head dim 128, FFN width 6144 and the 151936-row
 vocabulary are not printed on the pages; they are the standard Qwen3-1.7B
 sizes. eps 1e-6 and theta 1e6 follow the Qwen3-ASR decoder page
 (src/arch/qwen3_asr/decoder.cpp, file header).
+
+The 0.6B-shaped decoder: the MOSS-Transcribe-Diarize page
+(src/arch/moss/model.cpp, file header) drives a Qwen3-0.6B causal LM through
+the same causal_lm driver. Its sizes are not printed either. They are the
+standard Qwen3-0.6B sizes: hidden 1024, 16 query heads and 8 KV heads of
+128, so the attention width (2048) is twice the hidden width; FFN 3072; 28
+blocks; the same tied vocabulary. The page's own figure, a ~14 GiB worst-case
+cache at 131072 tokens in its run() comment, fixes n_kv_heads * head_dim *
+n_layers = 28672 for f16 KV, which these sizes meet.
 """
 from dataclasses import dataclass, field, replace
 
@@ -65,6 +74,7 @@ class Workload:
 TINY = DecoderShape(hidden=256, n_heads=4, n_kv_heads=2, head_dim=64, ffn=704, wdtype="f32", kvdtype="f32")
 QWEN3_1P7B_BLOCK = DecoderShape(hidden=2048, n_heads=16, n_kv_heads=8, head_dim=128, ffn=6144)
 QWEN3_1P7B = replace(QWEN3_1P7B_BLOCK, n_layers=28, vocab=151936)
+QWEN3_0P6B = DecoderShape(hidden=1024, n_heads=16, n_kv_heads=8, head_dim=128, ffn=3072, n_layers=28, vocab=151936)
 
 WORKLOADS = {
     w.name: w
@@ -83,5 +93,9 @@ WORKLOADS = {
                              "[150, 1500], 128 lockstep greedy decode steps"),
         Workload("qwen3_1p7b_block_long4096", 5, QWEN3_1P7B_BLOCK, prefill_rows=4096, steps=256, n_ctx=8192,
                  description="one 1.7B-shaped bf16 block: 4096-row causal prefill then 256 decode steps"),
+        Workload("qwen3_0p6b_stack28_greedy256", 6, QWEN3_0P6B, prefill_rows=153, steps=255, n_ctx=1024,
+                 slice_last=True, greedy=True,
+                 description="28-block 0.6B-shaped stack (the MOSS decoder) + final norm + tied lm_head: "
+                             "153-row prefill, then greedy argmax to 256 new tokens, batch 1"),
     ]
 }

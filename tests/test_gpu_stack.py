@@ -1,8 +1,10 @@
 """GPU parity at the full workload sizes, on outputs the oracle can afford:
 
-* 28-block 1.7B-shaped stack, 153-row prefill (last-row slice on), tied head,
-  then 8 teacher-forced greedy steps (the oracle's tokens are fed back):
-  first-block output, last-row output, logits and ids.
+* 28-block 1.7B-shaped stack and 28-block 0.6B-shaped stack (the MOSS
+  decoder: attention width 2048 over a 1024-wide residual), 153-row prefill
+  (last-row slice on), tied head, then 8 teacher-forced greedy steps (the
+  oracle's tokens are fed back): first-block output, last-row output, logits
+  and ids.
 * batched decode, B = 16 slabs with seeded context lengths in [150, 1500]
   and seeded KV fills: the GPU steps all 16 rows; three sampled rows are
   recomputed by the oracle for two steps.
@@ -27,8 +29,9 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def test_stack28_prefill153_head_and_teacher_forced_steps():
-    wl = WORKLOADS["qwen3_1p7b_stack28_greedy256"]
+@pytest.mark.parametrize("workload", ["qwen3_1p7b_stack28_greedy256", "qwen3_0p6b_stack28_greedy256"])
+def test_stack28_prefill153_head_and_teacher_forced_steps(workload):
+    wl = WORKLOADS[workload]
     sh = wl.shape
     T, n_check = wl.prefill_rows, 8
     log("generating 28 blocks + embedding")

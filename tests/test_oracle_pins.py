@@ -367,3 +367,48 @@ def test_kv_bytes_per_token_matches_pages_figure():
     c = O.KVCache(vals["n_layers"], 1, 1, vals["n_kv_heads"], vals["head_dim"])
     assert c.bytes_per_token(vals["elem_bytes"]) * vals["tokens"] == vals["bytes"]
     assert c.bytes_per_token(2) == 114688
+
+
+def test_0p6b_shape_meets_the_moss_pages_cache_figure():
+    """The MOSS page's ~14 GiB at 131072 tokens is a figure about its own
+    Qwen3-0.6B decoder: the supplied 0.6B sizes must reproduce it."""
+    from speech_text_decoder_amd.workloads import QWEN3_0P6B
+    vals = {}
+    with open(os.path.join(GOLDEN, "kv_bytes_per_token.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].split()
+            if line:
+                vals[line[0]] = int(line[1])
+    assert QWEN3_0P6B.kv_bytes_per_token() * vals["tokens"] == vals["bytes"]
+    assert QWEN3_0P6B.q_dim == 2 * QWEN3_0P6B.hidden   # attention wider than the residual stream
+
+
+def test_injection_blend_equals_the_three_way_concat():
+    """The pages give the audio injection in two forms: the single-sequence
+    prefill graph concatenates prefix embeddings, the encoder rows and suffix
+    embeddings (Qwen3-ASR decoder page, build_prefill_graph); the batched
+    graphs blend embed[ids] * keep + audio_dense. With one contiguous audio
+    block they must agree, and with no audio the blend is the plain gather."""
+    rng = np.random.default_rng(7)
+    V, H, pre, n_audio, suf = 50, 16, 5, 7, 3
+    T = pre + n_audio + suf
+    E = rng.standard_normal((V, H))
+    ids = rng.integers(0, V, T)
+    audio = rng.standard_normal((n_audio, H))
+    keep = np.ones(T)
+    keep[pre:pre + n_audio] = 0.0
+    dense = np.zeros((T, H))
+    dense[pre:pre + n_audio] = audio
+    concat = np.concatenate([E[ids[:pre]], audio, E[ids[pre + n_audio:]]], axis=0)
+    assert np.array_equal(O.inject(E, ids, keep, dense), concat)
+    assert np.array_equal(O.inject(E, ids, np.ones(T), np.zeros((T, H))), E[ids])
+    # non-contiguous audio positions (MOSS): rows land where keep is 0
+    pos = np.array([1, 4, 9])
+    keep2 = np.ones(T)
+    keep2[pos] = 0.0
+    dense2 = np.zeros((T, H))
+    dense2[pos] = audio[:3]
+    out = O.inject(E, ids, keep2, dense2)
+    assert np.array_equal(out[pos], audio[:3])
+    rest = np.setdiff1d(np.arange(T), pos)
+    assert np.array_equal(out[rest], E[ids[rest]])
