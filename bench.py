@@ -327,6 +327,103 @@ def cpu_baseline_greedy(wl, layers, E, g, x_host, new_tokens):
             "prefill_tok_s": round(T / (t1 - t0), 2), "decode_tok_s": round(1.0 / step_s, 4)}
 
 
+# ---------------------------------------------------------------- packed batched prefill
+def bench_packed_prefill(args, wl):
+    """B prompts: token embeddings with an injected audio block each, packed back to
+    back through one prefill call per block of the stack, then every prompt's last row
+    through the tied head. value = prompt rows per second of the whole job; the same
+    prompts one at a time are timed beside it."""
+    import torch
+    from speech_text_decoder_amd import binding, synth
+    from speech_text_decoder_amd.device import DecoderSession
+
+    sh = wl.shape
+    Bn, T = wl.batch, wl.prefill_rows
+    pre, n_audio, suf = wl.prompt_split
+    assert pre + n_audio + suf == T
+    layers = [synth.block_weights(wl.cfg_id, l, sh) for l in range(sh.n_layers)]
+    E = synth.embedding(wl.cfg_id, sh)
+    g = synth.final_norm(wl.cfg_id, sh)
+    ids_h, keep_h, dense_h = synth.injected_prompts(wl.cfg_id, Bn, wl.prompt_split, sh.hidden, sh.vocab)
+    sess = DecoderSession(sh, layers, embed=E, final_norm=g, n_ctx=wl.n_ctx, n_seq=Bn, max_rows=Bn * T)
+    ids_d = torch.from_numpy(ids_h).cuda()
+    keep_d = torch.from_numpy(keep_h).cuda()
+    dense_d = torch.from_numpy(dense_h).cuda()
+    x = torch.empty(Bn * T, sh.hidden, device="cuda")
+    out_ids = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def packed_job():
+        sess.inject(ids_d, keep_d, dense_d, x, stream=stream)
+        sess.prefill_batched(x, [T] * Bn, list(range(Bn)), stream=stream)
+        sess.head(x[T - 1:], out_ids, row_stride=T * sh.hidden, rows=Bn, stream=stream)
+
+    def separate_job():
+        for b in range(Bn):
+            r = slice(b * T, (b + 1) * T)
+            sess.inject(ids_d[r], keep_d[r], dense_d[r], x[r], stream=stream)
+            sess.prefill(x[r], seq=b, stream=stream)
+            sess.head(x[(b + 1) * T - 1:], out_ids[b:b + 1], stream=stream)
+
+    def timed(job):
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                job()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        with torch.cuda.stream(stream):
+            for i in range(args.steps):
+                evs[i][0].record(stream)
+                job()
+                evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+
+    t0 = time.perf_counter()
+    ms = timed(packed_job)
+    wall = time.perf_counter() - t0
+    packed_ids = out_ids.cpu().numpy().tolist()
+    ms_sep = timed(separate_job)
+    assert out_ids.cpu().numpy().tolist() == packed_ids, "packed and one-at-a-time prefills chose different ids"
+    rows = Bn * T
+    res = {
+        "value": round(rows / (ms * 1e-3), 1),
+        "ms_per_step": round(ms, 3),
+        "wall_ms_per_step": round(wall * 1e3 / (args.steps + args.warmup), 3),
+        "prefill_tok_s": round(rows / (ms * 1e-3), 1),
+        "one_at_a_time_ms": round(ms_sep, 3),
+        "one_at_a_time_tok_s": round(rows / (ms_sep * 1e-3), 1),
+        "ids": packed_ids,
+        "config": {"workload": wl.name, "layers": sh.n_layers, "hidden": sh.hidden, "heads": sh.n_heads,
+                   "kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim, "ffn": sh.ffn, "vocab": sh.vocab,
+                   "prompts": Bn, "prompt_rows": T, "prompt_split": list(wl.prompt_split), "kv_dtype": sh.kvdtype,
+                   "n_ctx": wl.n_ctx, "parallelism": "none (1 GPU)"},
+    }
+    if not args.no_kernel_profile:
+        prof = clock_profile(binding, torch, stream, eager=packed_job)
+        torch.cuda.synchronize()
+        rws = lambda n: rows if n.endswith("gemm") or n in ("rmsnorm", "qk_rope_kv") else (
+            T if n == "attn_prefill" else Bn)
+        res["kernels"] = {"prefill": kernel_table(prof, sh, rws, lambda n: T)}
+        res["kernel_timing"] = "device clock (s_memrealtime, 100 MHz): first-workgroup start to last-workgroup end"
+        res["roofline"] = roofline_entry(res["kernels"]["prefill"], "gateup_gemm", "mfma")
+    if not args.no_cpu_baseline:
+        import oracle as O
+        ol = [{k: synth.widen(v).astype(np.float64) for k, v in w.items()} for w in layers]
+        Ef = synth.widen(E).astype(np.float64)
+        cache = O.KVCache(sh.n_layers, 1, T, sh.n_kv_heads, sh.head_dim)
+        t0 = time.perf_counter()
+        x0 = O.inject(Ef, ids_h[:T], keep_h[:T], dense_h[:T])
+        last = O.prefill_stack(x0, ol, sh, cache)[-1:]
+        O.greedy_token(O.final_logits(last, synth.widen(g), Ef, sh.rms_eps)[0])
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(T / dt, 2), "unit": "tokens/s", "cores": cpu_threads(),
+                               "kind": "oracle", "sample": f"fp64 oracle: one of the {Bn} prompts ({T} rows: "
+                               f"injection, 28 blocks, head) in {dt:.1f} s"}
+    sess.close()
+    return res
+
+
 # ---------------------------------------------------------------- single-block workloads (replicated)
 def bench_block(args, wl):
     """One 1.7B-shaped block, timed as R independent replicas (distinct weights and KV)
@@ -591,7 +688,10 @@ def main():
         print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": 3}}), flush=True)
         return
     wl = WORKLOADS[args.workload]
-    if wl.greedy and wl.prefill_rows > 0:
+    if wl.packed:
+        res = bench_packed_prefill(args, wl)
+        unit = "tokens/s"
+    elif wl.greedy and wl.prefill_rows > 0:
         res = bench_greedy_stack(args, wl)
         unit = "tokens/s"
     elif wl.batch > 1:

@@ -25,7 +25,7 @@ SLOT = dict(attn_norm=0, wq=1, wk=2, wv=3, q_norm=4, k_norm=5, wo=6, ffn_norm=7,
             w_gate=8, w_up=9, w_down=10, kv_fill_k=12, kv_fill_v=13)
 # workload-wide tensors live under layer 31
 GLOBAL_LAYER = 31
-GSLOT = dict(embed=0, final_norm=1, x_prefill=2, x_step=3, ctx_len=6)
+GSLOT = dict(embed=0, final_norm=1, x_prefill=2, x_step=3, ctx_len=6, prompt_ids=7, audio_rows=8)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsttd_synth.so")
@@ -141,6 +141,25 @@ def prefill_rows(cfg_id: int, n_rows: int, hidden: int) -> np.ndarray:
 def step_rows(cfg_id: int, step: int, n_rows: int, hidden: int) -> np.ndarray:
     """Fresh N(0,1) decode input rows for step `step` (non-greedy workloads)."""
     return normal(stream_id(cfg_id, GLOBAL_LAYER, GSLOT["x_step"]), (n_rows, hidden), offset=step * n_rows * hidden)
+
+
+def injected_prompts(cfg_id: int, n_prompts: int, split, hidden: int, vocab: int):
+    """n_prompts prompts of prefix + audio + suffix rows, packed back to back:
+    token ids uniform over the vocabulary, keep 0 at the audio rows and 1
+    elsewhere, N(0,1) audio rows at the audio positions (zero elsewhere), the
+    inputs of the injection blend. Returns (ids int32 [n*T], keep f32 [n*T],
+    dense f32 [n*T, hidden])."""
+    pre, n_audio, suf = split
+    T = pre + n_audio + suf
+    ids = uniform_int(stream_id(cfg_id, GLOBAL_LAYER, GSLOT["prompt_ids"]), n_prompts * T, 0, vocab - 1)
+    keep = np.ones(n_prompts * T, dtype=np.float32)
+    dense = np.zeros((n_prompts * T, hidden), dtype=np.float32)
+    audio = normal(stream_id(cfg_id, GLOBAL_LAYER, GSLOT["audio_rows"]), (n_prompts * n_audio, hidden))
+    for b in range(n_prompts):
+        r = slice(b * T + pre, b * T + pre + n_audio)
+        keep[r] = 0.0
+        dense[r] = audio[b * n_audio:(b + 1) * n_audio]
+    return ids, keep, dense
 
 
 def context_lengths(cfg_id: int, batch: int, lo: int, hi: int) -> np.ndarray:

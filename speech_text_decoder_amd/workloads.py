@@ -68,6 +68,8 @@ class Workload:
     ctx_len_range: tuple = ()    # (lo, hi) inclusive: batched decode context lengths
     slice_last: bool = False     # last block runs FFN on the final row only
     greedy: bool = False         # decode rows come from the tied table (argmax feedback)
+    packed: bool = False         # batch prompts packed back to back through one prefill call per block
+    prompt_split: tuple = ()     # (prefix, audio, suffix) rows of each prompt: token ids / injected rows / ids
     description: str = ""
 
 
@@ -93,6 +95,11 @@ WORKLOADS = {
                              "[150, 1500], 128 lockstep greedy decode steps"),
         Workload("qwen3_1p7b_block_long4096", 5, QWEN3_1P7B_BLOCK, prefill_rows=4096, steps=256, n_ctx=8192,
                  description="one 1.7B-shaped bf16 block: 4096-row causal prefill then 256 decode steps"),
+        Workload("qwen3_1p7b_stack28_packed_prefill_b8", 7, QWEN3_1P7B, prefill_rows=153, steps=0, batch=8,
+                 packed=True, prompt_split=(9, 138, 6),
+                 description="28-block 1.7B-shaped stack + tied head: 8 prompts of 153 rows (9 prefix token "
+                             "embeddings, 138 injected audio rows, 6 suffix token embeddings) injected, packed "
+                             "through one prefill call per block, each prompt's last row through the head"),
         Workload("qwen3_0p6b_stack28_greedy256", 6, QWEN3_0P6B, prefill_rows=153, steps=255, n_ctx=1024,
                  slice_last=True, greedy=True,
                  description="28-block 0.6B-shaped stack (the MOSS decoder) + final norm + tied lm_head: "
