@@ -107,6 +107,13 @@ const char *sttd_status_string(sttd_status s);
 sttd_status sttd_kv_cache_alloc(int n_layers, int n_seq, int n_ctx, int n_kv_heads, int head_dim,
                                 sttd_dtype kv_type, sttd_kv_cache **out /* host */);
 sttd_status sttd_kv_cache_free(sttd_kv_cache *kv);
+/* Cache context for a session that needs `needed` positions (prompt plus
+ * generation budget), the sizing rule described in run() on the MOSS page:
+ * short inputs keep the 1024 / 2048 / 4096 buckets, longer ones grow in steps
+ * of 4096 (so crossing 32K does not jump to the full 131072-token worst case),
+ * and the result is clamped to `ceiling`. Host function, no device work.
+ * Returns 0 when needed < 1 or ceiling < 1. */
+int sttd_kv_context_for(int needed, int ceiling);
 /* Zero every slab (the buffer clear before a fresh prefill, run() on the
  * Qwen3-ASR model page). Enqueued as a fill kernel on `stream`. */
 sttd_status sttd_kv_cache_clear(sttd_kv_cache *kv, void *stream);
@@ -208,7 +215,9 @@ sttd_status sttd_block_prefill_batched(const sttd_block_params *p, const sttd_bl
  * go to cache row pos[b]; it attends rows [0, pos[b]]. pos_bound (host) is
  * an upper bound on every pos[b] + 1 (<= n_ctx) used to size the launch;
  * the work done follows the actual pos[b]. x [B, hidden] fp32 in/out.
- * 1 <= B <= max_rows. */
+ * 1 <= B <= max_rows. pos[b] = -1 marks a row whose greedy loop has stopped
+ * (sttd_greedy_stop): its attention and cache write are skipped and its
+ * output row is undefined. */
 sttd_status sttd_block_step(const sttd_block_params *p, const sttd_block_weights *w, sttd_workspace *ws,
                             sttd_kv_cache *kv, int layer, int B, const int32_t *seq, const int32_t *pos,
                             int pos_bound, float *x, void *stream);
@@ -225,6 +234,32 @@ sttd_status sttd_block_step(const sttd_block_params *p, const sttd_block_weights
 sttd_status sttd_lm_head_argmax(const void *final_norm, const void *embed, sttd_dtype wtype, int vocab, int hidden,
                                 float rms_eps, sttd_workspace *ws, int B, const float *x, int64_t x_row_stride,
                                 int32_t *ids, float *logits, float *next_x, int32_t *pos, void *stream);
+
+/* Greedy stopping rules on the device, per row (the step loop of run() on
+ * the Qwen3-ASR model page, and per row in its batched step loop): a row goes
+ * on while its newest token is not eos_id, it has fewer than max_new tokens
+ * and its next input position is inside the context (position + 1 <= n_ctx);
+ * a row that stops for another reason than EOS is truncated. The repetition
+ * guard of the MOSS page is not defined on the pages and is not applied.
+ * Call it after each sttd_lm_head_argmax, whose pos argument must then be
+ * NULL: this call owns the positions. State (device int32 [B], set by the
+ * caller before the first call): active = 1, n_gen = 0, truncated = 0,
+ * pos = the prompt length (the first step's input position). For each active
+ * row b the chosen ids[b] is stored at tokens[b * max_new + n_gen[b]] and
+ * n_gen[b] is incremented; with advance = 1 (every call after a decode step;
+ * 0 for the call after the prefill) pos[b] moves on by one. A row that stops
+ * gets active 0, truncated = (ids[b] != eos_id) and pos = -1, which marks it
+ * for sttd_block_step to skip (no cache write, no error; its outputs are
+ * undefined). Inactive rows are left unchanged. n_active (device int32 [1],
+ * may be NULL) receives the number of rows still active. The call is
+ * graph-capturable, so the whole loop can be replayed and the host reads
+ * n_active between replays. */
+typedef struct {
+    int32_t eos_id, max_new, n_ctx;
+} sttd_stop_rules;
+sttd_status sttd_greedy_stop(const sttd_stop_rules *r /* host */, int B, const int32_t *ids, int advance,
+                             int32_t *pos, int32_t *active, int32_t *n_gen, int32_t *tokens, int32_t *truncated,
+                             int32_t *n_active, void *stream);
 
 /* ---------------------------------------------------------------- per-kernel timing
  * The per-op profiler of the MOSS-Transcribe-Diarize page (src/arch/moss/

@@ -213,6 +213,22 @@ def inject(embed, ids, keep, audio_dense):
     return rows * f64(keep)[:, None] + f64(audio_dense)
 
 
+def greedy_loop(first, next_token, prompt_len, eos_id, max_new, n_ctx):
+    """The step loop of run() on the Qwen3-ASR model page. It starts from the
+    prefill's token and steps while the newest token is not EOS, fewer than
+    max_new tokens exist and the next input position (the prompt length plus
+    the steps taken) still fits: position + 1 <= n_ctx. next_token(position,
+    token) gives the token a step at that input position produces. Returns
+    (tokens, truncated), where truncated means the loop ended other than on
+    EOS."""
+    tokens = [int(first)]
+    cur = int(prompt_len)
+    while tokens[-1] != eos_id and len(tokens) < max_new and cur + 1 <= n_ctx:
+        tokens.append(int(next_token(cur, tokens[-1])))
+        cur += 1
+    return tokens, tokens[-1] != eos_id
+
+
 def final_logits(x_rows, final_gain, embed, eps):
     """Final RMSNorm then the tied lm_head: logits = E @ (RMSNorm(x) * g)."""
     z = rms_norm(x_rows, final_gain, eps)

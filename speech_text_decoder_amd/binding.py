@@ -19,11 +19,11 @@ DEVERR_POSITION, DEVERR_SLAB, DEVERR_TOKEN, DEVERR_SYNC = 1, 2, 4, 8
 OPT_FUSED_STEP = 1
 
 EXPORTS = [
-    "sttd_status_string", "sttd_kv_cache_alloc", "sttd_kv_cache_free", "sttd_kv_cache_clear", "sttd_kv_cache_view",
+    "sttd_status_string", "sttd_kv_context_for", "sttd_kv_cache_alloc", "sttd_kv_cache_free", "sttd_kv_cache_clear", "sttd_kv_cache_view",
     "sttd_workspace_alloc", "sttd_workspace_free", "sttd_workspace_error", "sttd_workspace_set_option",
     "sttd_embed_gather", "sttd_embed_inject",
     "sttd_block_prefill", "sttd_block_prefill_batched", "sttd_block_step", "sttd_lm_head_argmax",
-    "sttd_profile_enable", "sttd_profile_read",
+    "sttd_greedy_stop", "sttd_profile_enable", "sttd_profile_read",
     "sttd_clock_enable", "sttd_clock_disable", "sttd_clock_reset", "sttd_clock_read", "sttd_clock_spans",
 ]
 
@@ -32,6 +32,10 @@ class SttdError(RuntimeError):
     def __init__(self, status, what):
         self.status = status
         super().__init__(f"{what}: status {status} ({status_string(status)})")
+
+
+class StopRules(ctypes.Structure):
+    _fields_ = [("eos_id", ctypes.c_int32), ("max_new", ctypes.c_int32), ("n_ctx", ctypes.c_int32)]
 
 
 class BlockParams(ctypes.Structure):
@@ -60,6 +64,8 @@ def lib():
         P = ctypes.POINTER
         L.sttd_status_string.restype = ctypes.c_char_p
         L.sttd_status_string.argtypes = [i32]
+        L.sttd_kv_context_for.restype = i32
+        L.sttd_kv_context_for.argtypes = [i32, i32]
         sigs = {
             "sttd_kv_cache_alloc": [i32, i32, i32, i32, i32, i32, P(vp)],
             "sttd_kv_cache_free": [vp],
@@ -77,6 +83,7 @@ def lib():
                                            vp, vp],
             "sttd_block_step": [P(BlockParams), P(BlockWeights), vp, vp, i32, i32, vp, vp, i32, vp, vp],
             "sttd_lm_head_argmax": [vp, vp, i32, i32, i32, f32, vp, i32, vp, i64, vp, vp, vp, vp, vp],
+            "sttd_greedy_stop": [P(StopRules), i32, vp, i32, vp, vp, vp, vp, vp, vp, vp],
             "sttd_profile_enable": [ctypes.c_uint32],
             "sttd_profile_read": [i32, P(i64), P(ctypes.c_double)],
             "sttd_clock_enable": [ctypes.c_uint32, i32],
@@ -116,6 +123,10 @@ def kv_cache_alloc(n_layers, n_seq, n_ctx, n_kv_heads, head_dim, kv_type):
     _check(lib().sttd_kv_cache_alloc(n_layers, n_seq, n_ctx, n_kv_heads, head_dim, kv_type, ctypes.byref(h)),
            "sttd_kv_cache_alloc")
     return h.value
+
+
+def kv_context_for(needed, ceiling):
+    return lib().sttd_kv_context_for(needed, ceiling)
 
 
 def kv_cache_free(kv):
@@ -180,6 +191,13 @@ def block_prefill_batched(params, weights, ws, kv, layer, seq, pos0, T, x, strea
 def block_step(params, weights, ws, kv, layer, B, seq, pos, pos_bound, x, stream=0):
     _check(lib().sttd_block_step(ctypes.byref(params), ctypes.byref(weights), ws, kv, layer, B, seq, pos, pos_bound,
                                  x, stream), "sttd_block_step")
+
+
+def greedy_stop(eos_id, max_new, n_ctx, B, ids, advance, pos, active, n_gen, tokens, truncated, n_active=0,
+                stream=0):
+    r = StopRules(eos_id, max_new, n_ctx)
+    _check(lib().sttd_greedy_stop(ctypes.byref(r), B, ids, advance, pos, active, n_gen, tokens, truncated, n_active,
+                                  stream), "sttd_greedy_stop")
 
 
 def profile_enable(mask):

@@ -433,6 +433,15 @@ sttd_status sttd_kv_cache_alloc(int n_layers, int n_seq, int n_ctx, int n_kv_hea
     return STTD_OK;
 }
 
+int sttd_kv_context_for(int needed, int ceiling) {
+    if (needed < 1 || ceiling < 1) return 0;
+    int n;
+    if (needed <= 1024) n = 1024;
+    else if (needed <= 2048) n = 2048;
+    else n = (int)(((int64_t)needed + 4095) / 4096 * 4096 > INT32_MAX ? INT32_MAX : ((int64_t)needed + 4095) / 4096 * 4096);
+    return n < ceiling ? n : ceiling;
+}
+
 sttd_status sttd_kv_cache_free(sttd_kv_cache* kv) {
     if (!kv) return STTD_ERR_INVALID_ARG;
     const hipError_t a = hipFree(kv->k), b = hipFree(kv->v);
@@ -671,6 +680,16 @@ sttd_status sttd_lm_head_argmax(const void* final_norm, const void* embed, sttd_
     a.zbuf = hidden <= ws->p.hidden ? ws->xn : nullptr;  // 2 * B * hidden bf16 fit in the normed-row planes
     ProfScope ps(STTD_KERN_LM_HEAD, (hipStream_t)stream);
     TRY(launch_lm_head_argmax(a, wtype == STTD_BF16 ? W_BF16 : W_F32, (hipStream_t)stream));
+    return STTD_OK;
+}
+
+sttd_status sttd_greedy_stop(const sttd_stop_rules* r, int B, const int32_t* ids, int advance, int32_t* pos,
+                             int32_t* active, int32_t* n_gen, int32_t* tokens, int32_t* truncated, int32_t* n_active,
+                             void* stream) {
+    if (!r || !ids || !pos || !active || !n_gen || !tokens || !truncated || B <= 0) return STTD_ERR_INVALID_ARG;
+    if (r->max_new < 1 || r->n_ctx < 1 || (advance != 0 && advance != 1)) return STTD_ERR_INVALID_ARG;
+    TRY(launch_greedy_stop(B, ids, r->eos_id, r->max_new, r->n_ctx, advance, pos, active, n_gen, tokens, truncated,
+                           n_active, (hipStream_t)stream));
     return STTD_OK;
 }
 

@@ -155,7 +155,9 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
     const int pos = pos_v, seq = seq_v;
     const bool ok = pos >= 0 && pos < a.kv.n_ctx && pos < (FUSE ? a.max_pos : a.kv.n_ctx) && seq >= 0 &&
                     seq < a.kv.n_seq;
-    if (!ok && tid == 0 && split == 0 && j == 0) record_error(a.err, pos < 0 || pos >= a.kv.n_ctx ? 1u : 2u);
+    // pos -1 marks a row whose greedy loop has stopped: skipped, not an error
+    if (!ok && pos != -1 && tid == 0 && split == 0 && j == 0)
+        record_error(a.err, pos < 0 || pos >= a.kv.n_ctx ? 1u : 2u);
     float2 cs = make_float2(1.f, 0.f);
     if (FUSE) cs = reinterpret_cast<const float2*>(a.rope)[(int64_t)(ok ? pos : 0) * HALF + lc];
     const int n_keys = ok ? pos + 1 : 0;

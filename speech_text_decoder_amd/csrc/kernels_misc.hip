@@ -142,6 +142,53 @@ hipError_t launch_expand_segments(const Segments& sg, int R, int32_t* pos, int32
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ greedy stopping rules
+// One workgroup walks the rows. An active row appends its token. With
+// `advance` its next input position moves on by one; the first call after the
+// prefill leaves it at the prompt length. The row goes on while the token is
+// not EOS, fewer than max_new tokens exist and the next position is inside the
+// context (the step loop's condition in run() on the Qwen3-ASR model page).
+// A row that stops gets pos -1, which the block step skips, and is truncated
+// unless it stopped on EOS.
+__global__ __launch_bounds__(256) void greedy_stop_kernel(int B, const int32_t* __restrict__ ids, int eos_id,
+                                                          int max_new, int n_ctx, int advance, int32_t* pos,
+                                                          int32_t* active, int32_t* n_gen, int32_t* tokens,
+                                                          int32_t* truncated, int32_t* n_active) {
+    __shared__ int count;
+    if (threadIdx.x == 0) count = 0;
+    __syncthreads();
+    int mine = 0;
+    for (int b = threadIdx.x; b < B; b += 256) {
+        if (!active[b]) continue;
+        const int tok = ids[b];
+        const int n = n_gen[b];
+        if (n < max_new) tokens[(int64_t)b * max_new + n] = tok;
+        n_gen[b] = n + 1;
+        const int next = pos[b] + (advance ? 1 : 0);
+        const bool go = tok != eos_id && n + 1 < max_new && next + 1 <= n_ctx;
+        if (go) {
+            pos[b] = next;
+            ++mine;
+        } else {
+            pos[b] = -1;
+            active[b] = 0;
+            truncated[b] = tok != eos_id ? 1 : 0;
+        }
+    }
+    if (mine) atomicAdd(&count, mine);
+    __syncthreads();
+    if (threadIdx.x == 0 && n_active) *n_active = count;
+}
+
+hipError_t launch_greedy_stop(int B, const int32_t* ids, int eos_id, int max_new, int n_ctx, int advance,
+                              int32_t* pos, int32_t* active, int32_t* n_gen, int32_t* tokens, int32_t* truncated,
+                              int32_t* n_active, hipStream_t s) {
+    if (B <= 0) return hipSuccess;
+    greedy_stop_kernel<<<1, 256, 0, s>>>(B, ids, eos_id, max_new, n_ctx, advance, pos, active, n_gen, tokens,
+                                          truncated, n_active);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ zero fill
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint4* __restrict__ p, size_t n16, uint8_t* tail,
                                                         size_t ntail) {

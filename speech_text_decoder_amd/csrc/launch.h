@@ -84,6 +84,10 @@ hipError_t launch_qk_norm_rope_kv(const float* qkv, int64_t ldqkv, int R, WType 
 hipError_t launch_embed_gather(const void* embed, WType wt, int vocab, int hidden, int B, const int32_t* ids,
                                const float* keep, const float* dense, float* x, uint32_t* err, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// Greedy stopping rules after a head call (see sttd_greedy_stop).
+hipError_t launch_greedy_stop(int B, const int32_t* ids, int eos_id, int max_new, int n_ctx, int advance,
+                              int32_t* pos, int32_t* active, int32_t* n_gen, int32_t* tokens, int32_t* truncated,
+                              int32_t* n_active, hipStream_t s);
 
 // ---- GEMV family (kernels_gemv.hip): rows <= 4 per group, fp32 activations.
 enum GemvEpi { GEMV_STORE = 0, GEMV_RESID = 1, GEMV_SWIGLU = 2 };

@@ -63,3 +63,17 @@ def test_null_and_bad_arguments_rejected_on_host():
     assert L.sttd_workspace_alloc(ctypes.byref(bad), 4, 16, 0, ctypes.byref(out)) == B.ERR_UNSUPPORTED
     bad = B.block_params(256, 72, 9, 128, 512, 1e-6, 1e6, B.BF16)     # n_heads * head_dim = 9216
     assert L.sttd_workspace_alloc(ctypes.byref(bad), 4, 16, 0, ctypes.byref(out)) == B.ERR_UNSUPPORTED
+
+
+def test_kv_context_policy():
+    """The cache sizing of the MOSS page's run(): 1K / 2K / 4K buckets, then
+    4K steps, clamped to the ceiling (host function, no GPU)."""
+    f = B.kv_context_for
+    assert [f(n, 131072) for n in (1, 1024, 1025, 2048, 2049, 4096, 4097, 8192, 32769)] == \
+        [1024, 1024, 2048, 2048, 4096, 4096, 8192, 8192, 36864]
+    assert f(200000, 131072) == 131072 and f(3000, 2500) == 2500
+    assert f(0, 1024) == 0 and f(10, 0) == 0
+    # grow-only in 4K steps past 4096: never more than 4095 positions of slack
+    for n in range(4097, 70000, 997):
+        c = f(n, 1 << 30)
+        assert c >= n and c - n < 4096 and c % 4096 == 0

@@ -412,3 +412,18 @@ def test_injection_blend_equals_the_three_way_concat():
     assert np.array_equal(out[pos], audio[:3])
     rest = np.setdiff1d(np.arange(T), pos)
     assert np.array_equal(out[rest], E[ids[rest]])
+
+
+def test_greedy_loop_stopping_rules_closed_forms():
+    """The step loop's three exits (run() on the Qwen3-ASR model page): EOS,
+    the token budget, the end of the context; truncated unless EOS."""
+    seq = lambda pos, tok: 100 + pos          # a token per input position
+    assert O.greedy_loop(7, seq, 10, 7, 50, 64) == ([7], False)              # the prefill's token is EOS
+    toks, tr = O.greedy_loop(1, seq, 10, 999, 5, 64)                          # budget: 5 tokens in all
+    assert toks == [1, 110, 111, 112, 113] and tr
+    toks, tr = O.greedy_loop(1, seq, 60, 999, 50, 64)                         # context: steps at 60..63
+    assert toks == [1, 160, 161, 162, 163] and tr
+    toks, tr = O.greedy_loop(1, seq, 10, 113, 50, 64)                         # EOS produced at position 13
+    assert toks == [1, 110, 111, 112, 113] and not tr
+    assert O.greedy_loop(1, seq, 64, 999, 50, 64) == ([1], True)            # context already full
+    assert O.greedy_loop(1, seq, 10, 999, 1, 64) == ([1], True)             # budget of one token
