@@ -231,9 +231,14 @@ constexpr int BIG_BM = 256, BIG_BN = 256, BIG_BK = 64, BIG_STR = BIG_BK;
 // SQ_LDS_BANK_CONFLICT counter reads 0, against 37% of LDS cycles with padded rows.
 __device__ __forceinline__ int big_lds_off(int r, int c) { return r * BIG_BK + ((c ^ (r & 7)) * 8); }
 
-template <int EPI, int BN>
+// KSPLIT > 1 (residual outputs only): the grid holds KSPLIT copies of the tile
+// grid, copy s taking the s-th part of K and adding its partial sums into C
+// (which already holds the residual) with fp32 atomics. Copies follow one
+// another in the grid, so each keeps the XCD-aware tile order.
+template <int EPI, int BN, int KSPLIT = 1>
 __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     static_assert(EPI != GEMM_SWIGLU || BN == BIG_BN, "SwiGLU pairs gate and up inside 256-row weight tiles");
+    static_assert(KSPLIT == 1 || EPI == GEMM_RESID, "split K adds into a residual");
     constexpr int FM = 4, FN = BN / 32;
     constexpr int VECS = BIG_BM * BIG_BK / 8 / 512;  // 16-byte vectors per thread and step: A
     constexpr int BVECS = BN * BIG_BK / 8 / 512;     // and B
@@ -245,7 +250,9 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
     const int wm = wave / 2, wn = wave % 2;  // 4 x 2 waves, each 64 x 128
     // XCD-aware tile order when the tile count splits evenly over the 8 XCDs
     const int n_tiles = tiles_m * tiles_n;
-    const int id = blockIdx.x;
+    const int id = KSPLIT > 1 ? (int)blockIdx.x % n_tiles : (int)blockIdx.x;
+    const int k_part = KSPLIT > 1 ? (int)blockIdx.x / n_tiles : 0;
+    const int64_t k_begin = (int64_t)k_part * (g.K / KSPLIT);
     const int t = n_tiles % 8 ? id : (id % 8) * (n_tiles / 8) + id / 8;
     const int tile_m = t % tiles_m, tile_n = t / tiles_m;
     const int m0 = tile_m * BIG_BM;
@@ -258,7 +265,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
         const int v = tid + i * 512;
         const int r = v / (BIG_BK / 8), ck = (v % (BIG_BK / 8)) * 8;
         const int am = m0 + r < g.M ? m0 + r : 0;
-        aptr[i] = g.A + (int64_t)am * g.lda + ck;
+        aptr[i] = g.A + (int64_t)am * g.lda + k_begin + ck;
     }
 #pragma unroll
     for (int i = 0; i < BVECS; ++i) {
@@ -280,7 +287,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
             grow = n - (s2 ? g.seg_end[1] : (s1 ? g.seg_end[0] : 0));
             W = s2 ? g.w[2] : (s1 ? g.w[1] : g.w[0]);
         }
-        bptr[i] = W + (int64_t)grow * g.K + ck;
+        bptr[i] = W + (int64_t)grow * g.K + k_begin + ck;
     }
     u32x4 areg[VECS], breg[BVECS];
     auto fetch = [&](int64_t k0) {
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = g.K / BIG_BK;
+    const int nk = g.K / BIG_BK / KSPLIT;
     fetch(0);
     stash(0);
     if (nk > 1) fetch(BIG_BK);
@@ -365,7 +372,8 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
                     const int n = tile_n * BN + wn * (BN / 2) + j * 16 + lane % 16;
                     if (n >= g.N) continue;
                     float* dst = g.C + (int64_t)m * g.ldc + n;
-                    if (EPI == GEMM_RESID) *dst += acc[i][j][rr];
+                    if (KSPLIT > 1) atomicAdd(dst, acc[i][j][rr]);
+                    else if (EPI == GEMM_RESID) *dst += acc[i][j][rr];
                     else *dst = acc[i][j][rr];
                 }
             }
@@ -387,8 +395,20 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
         gemm_big_kernel<GEMM_SWIGLU, BIG_BN><<<tiles_m * tiles_n, 512, 0, s>>>(g, tiles_m, tiles_n);
         return;
     }
+    // residual outputs too narrow to fill the CUs even with 256 x 128 tiles: two
+    // K halves of each 256 x 256 tile, added into the residual with atomics
+    // (measured at 1224 rows and 2048 columns: down 104 -> 89 us, O 46 -> 38 us;
+    // at 4096 rows, where 256 x 128 tiles already make 256 workgroups, the split
+    // was slower: O 55 -> 68 us)
+    const int tiles256 = tiles_m * ((g.N + BIG_BN - 1) / BIG_BN);
+    const int tiles128 = tiles_m * ((g.N + 127) / 128);
+    if (epi == GEMM_RESID && tiles128 < 256 && tiles256 % 8 == 0 && (g.K / BIG_BK) % 2 == 0 &&
+        g.K / BIG_BK >= 16) {
+        gemm_big_kernel<GEMM_RESID, BIG_BN, 2><<<tiles256 * 2, 512, 0, s>>>(g, tiles_m, (g.N + BIG_BN - 1) / BIG_BN);
+        return;
+    }
     // narrow outputs: 128-column tiles so that about a full wave of workgroups runs
-    const bool narrow = tiles_m * ((g.N + BIG_BN - 1) / BIG_BN) < 256;
+    const bool narrow = tiles256 < 256;
     const int bn = narrow ? 128 : BIG_BN;
     const int tiles_n = (g.N + bn - 1) / bn;
     const int grid = tiles_m * tiles_n;
