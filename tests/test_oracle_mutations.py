@@ -25,12 +25,14 @@ MUTATIONS = {
     "argmax_highest_index": ('return int(np.argmax(l32))', 'return int(len(l32) - 1 - np.argmax(l32[::-1]))'),
     "silu_sign": ('return z / (1.0 + np.exp(-z))', 'return z / (1.0 + np.exp(z))'),
     "down_rows_permuted": ('(silu(gate) * up) @ f64(w["w_down"]).T', '(silu(gate) * up) @ f64(w["w_down"]).T[::-1]'),
+    "inject_keep_on_audio": ('return rows * f64(keep)[:, None] + f64(audio_dense)',
+                             'return rows + f64(audio_dense) * f64(keep)[:, None]'),
+    "loop_context_off_by_one": ('cur + 1 <= n_ctx', 'cur + 1 < n_ctx'),
+    "loop_budget_excludes_first": ('len(tokens) < max_new', 'len(tokens) <= max_new'),
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
-def test_pins_catch_planted_mistake(name, tmp_path):
-    old, new = MUTATIONS[name]
+def run_pins_on_copy(tmp_path, old=None, new=None, name=""):
     shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
                     ignore=shutil.ignore_patterns("__pycache__"))
     (tmp_path / "tests").mkdir()
@@ -39,8 +41,22 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     shutil.copytree(os.path.join(ROOT, "tests", "golden"), tmp_path / "tests" / "golden")
     src = tmp_path / "oracle" / "decoder.py"
     text = src.read_text()
-    assert text.count(old) >= 1, name
-    src.write_text(text.replace(old, new))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "tests/test_oracle_pins.py"],
-                       cwd=tmp_path, capture_output=True, text=True, timeout=300)
+    if old is not None:
+        assert text.count(old) >= 1, name
+        src.write_text(text.replace(old, new))
+    return subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "tests/test_oracle_pins.py"],
+                          cwd=tmp_path, capture_output=True, text=True, timeout=300)
+
+
+def test_unmutated_copy_passes(tmp_path):
+    """Control: the copied pin suite passes on the unchanged oracle, so a failure
+    below comes from the planted mistake and not from the copy itself."""
+    r = run_pins_on_copy(tmp_path)
+    assert r.returncode == 0, r.stdout[-2000:]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTATIONS[name]
+    r = run_pins_on_copy(tmp_path, old, new, name)
     assert r.returncode == 1, f"planted mistake {name} was not caught:\n{r.stdout[-2000:]}"

@@ -369,20 +369,6 @@ def test_kv_bytes_per_token_matches_pages_figure():
     assert c.bytes_per_token(2) == 114688
 
 
-def test_0p6b_shape_meets_the_moss_pages_cache_figure():
-    """The MOSS page's ~14 GiB at 131072 tokens is a figure about its own
-    Qwen3-0.6B decoder: the supplied 0.6B sizes must reproduce it."""
-    from speech_text_decoder_amd.workloads import QWEN3_0P6B
-    vals = {}
-    with open(os.path.join(GOLDEN, "kv_bytes_per_token.txt")) as f:
-        for line in f:
-            line = line.split("#")[0].split()
-            if line:
-                vals[line[0]] = int(line[1])
-    assert QWEN3_0P6B.kv_bytes_per_token() * vals["tokens"] == vals["bytes"]
-    assert QWEN3_0P6B.q_dim == 2 * QWEN3_0P6B.hidden   # attention wider than the residual stream
-
-
 def test_injection_blend_equals_the_three_way_concat():
     """The pages give the audio injection in two forms: the single-sequence
     prefill graph concatenates prefix embeddings, the encoder rows and suffix
