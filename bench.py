@@ -363,7 +363,7 @@ def bench_packed_prefill(args, wl):
             r = slice(b * T, (b + 1) * T)
             sess.inject(ids_d[r], keep_d[r], dense_d[r], x[r], stream=stream)
             sess.prefill(x[r], seq=b, stream=stream)
-            sess.head(x[(b + 1) * T - 1:], out_ids[b:b + 1], stream=stream)
+            sess.head(x[(b + 1) * T - 1:(b + 1) * T], out_ids[b:b + 1], stream=stream)
 
     def timed(job):
         with torch.cuda.stream(stream):
