@@ -33,8 +33,8 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
 # 256 MiB copy (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0); valid only for the kernel
 # sources they were taken on (sha256 of the listed files).
 TRAFFIC = {
-    "gateup_gemv": {"rows": 1, "bytes": 50580078, "files": ["kernels_gemv.hip", "common.h"],
-                    "sha256": "c1aff14dabb0311f8b334ecb7edcfc9dd8736562c83456c29a2bc54b95ba2a45",
+    "gateup_gemv": {"rows": 1, "bytes": 50580036, "files": ["kernels_gemv.hip", "gemv_ops.h", "common.h"],
+                    "sha256": "716424a91ac18102635aa5b31b78e1a3669ec1120db258d2d5b2e095f18df6a6",
                     "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"},
 }
 
