@@ -44,6 +44,7 @@ struct sttd_workspace {
     int32_t* rowpos;               // [max_rows]: per-row positions of a packed batched prefill
     int32_t* rowseq;               // [max_rows]: per-row slabs of a packed batched prefill
     uint32_t* sync;                // [kStepSyncWords] hand-off counters of the fused step (zero between launches)
+    uint32_t* merge_ctr;           // [max_rows][n_kv] attention split counts (zero between launches)
     bool fused_step;               // STTD_OPT_FUSED_STEP
 };
 
@@ -301,7 +302,7 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
                 ProfScope ps(STTD_KERN_ATTN_ROWS, s);
                 TRY(launch_attn_rows((const float*)ws->qbuf + (size_t)r0 * qd, qd, Ti, nq, ri, kl, sp,
                                      (p0 + Ti + sp - 1) / sp, ws->part, mfma ? nullptr : ws->attn_o + (size_t)r0 * qd,
-                                     aoi, aoli, qd, ws->err, nullptr, wt, s));
+                                     aoi, aoli, qd, ws->err, nullptr, wt, s, ws->merge_ctr + (size_t)r0 * nkv));
             }
         }
     } else if (flash) {
@@ -318,7 +319,7 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
         const int span = ((prefill ? rm.pos0 + R : pos_bound) + splits - 1) / splits;
         TRY(launch_attn_rows(prefill ? (const float*)ws->qbuf : ws->qkv, prefill ? qd : qkv_cols, R, nq, rm, kl,
                              splits, span, ws->part, mfma || defer ? nullptr : ws->attn_o, mfma ? ao : nullptr,
-                             mfma ? ao_lo : nullptr, qd, ws->err, prefill ? nullptr : &qr, wt, s));
+                             mfma ? ao_lo : nullptr, qd, ws->err, prefill ? nullptr : &qr, wt, s, ws->merge_ctr));
     }
     // --- O projection + residual
     if (mfma) {
@@ -500,6 +501,7 @@ sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int m
     const size_t o_h = take((size_t)H * sizeof(float));
     const size_t o_rowpos = take(R * sizeof(int32_t));
     const size_t o_rowseq = take(R * sizeof(int32_t));
+    const size_t o_merge = take(R * nkv * sizeof(uint32_t));
     sttd_workspace* ws = new (std::nothrow) sttd_workspace();
     if (!ws) return STTD_ERR_OOM;
     ws->p = *p;
@@ -528,6 +530,7 @@ sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int m
     ws->hbuf = (float*)(b + o_h);
     ws->rowpos = (int32_t*)(b + o_rowpos);
     ws->rowseq = (int32_t*)(b + o_rowseq);
+    ws->merge_ctr = (uint32_t*)(b + o_merge);
     ws->fused_step = false;
     // RoPE table in fp64 on the host: pair i of position pos turns by pos * theta^(-2i/d)
     std::vector<float> table((size_t)max_pos * d);

@@ -46,6 +46,9 @@ struct RowsArgs {
     float eps;
     const float* rope;
     int max_pos;
+    // non-null with several splits and an output to write: [rows][n_kv] zeroed
+    // counts; the last split of a (row, KV head) to finish merges all of them
+    uint32_t* merge_ctr;
     uint64_t* clk;
 };
 
@@ -345,6 +348,55 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
                 MEM::st(pp + 1, L);
             }
             MEM::st(pp + 4 + e, O);
+        }
+    }
+    // 8. several splits and an output: the split of this (row, KV head) that
+    //    finishes last merges all partial records and writes o, so no combine
+    //    pass runs. The partials were published with device-scope stores, which
+    //    each wave waits for before the count; the merging split reads them with
+    //    device-scope loads (records of neighbouring pairs share cache lines,
+    //    which a plain load could find stale in this XCD's L2). It resets the
+    //    count for the next launch.
+    if (a.merge_ctr && a.n_splits > 1) {
+        __shared__ int is_last;
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have completed
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t* c = a.merge_ctr + (int64_t)r * a.kv.n_kv + j;
+            const uint32_t old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            is_last = old == (uint32_t)(a.n_splits - 1);
+            if (is_last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (is_last) {
+            for (int t = tid; t < G * D; t += NW * 64) {
+                const int g = t / D, e = t % D;
+                const float* pp = a.part + ((int64_t)r * a.n_heads + j * G + g) * a.n_splits * (D + 4);
+                float M = -INFINITY, L = 0.f, O = 0.f;
+#pragma unroll 8
+                for (int sp = 0; sp < a.n_splits; ++sp) {
+                    const float* q = pp + (int64_t)sp * (D + 4);
+                    const float ms = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const float ls = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const float os = __hip_atomic_load(q + 4 + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const float Mn = fmaxf(M, ms);
+                    const float fa = Mn == -INFINITY ? 0.f : exp2f(M - Mn);
+                    const float fb = Mn == -INFINITY ? 0.f : exp2f(ms - Mn);
+                    L = L * fa + ls * fb;
+                    O = O * fa + os * fb;
+                    M = Mn;
+                }
+                const float v = L > 0.f ? O / L : 0.f;
+                const int64_t idx = (int64_t)r * a.ldo + (j * G + g) * D + e;
+                if (a.out_f32) {
+                    a.out_f32[idx] = v;
+                } else {
+                    uint16_t hi, lo;
+                    split_bf16(v, hi, lo);
+                    a.out_bf16[idx] = hi;
+                    if (a.out_lo) a.out_lo[idx] = lo;
+                }
+            }
         }
     }
 }

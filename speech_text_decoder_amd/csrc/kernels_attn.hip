@@ -17,7 +17,9 @@ namespace sttd {
 template <class KT, class GT, int D, int G, int NW, bool FUSE>
 __global__ __launch_bounds__(NW * 64) void attn_rows_kernel(RowsArgs a) {
     clock_begin(a.clk);
-    attn_rows_item<KT, GT, D, G, NW, FUSE>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    // partials are published with device-scope stores: the last split of a
+    // (row, KV head) may merge them in this launch (RowsArgs::merge_ctr)
+    attn_rows_item<KT, GT, D, G, NW, FUSE, PubMem>(a, blockIdx.x, blockIdx.y, blockIdx.z);
     clock_end(a.clk);
 }
 
@@ -76,7 +78,7 @@ static hipError_t rows_dispatch(const RowsArgs& a, int R, bool wide, hipStream_t
         default: return hipErrorInvalidValue;
     }
 #undef ROWS_LAUNCH
-    if (a.n_splits > 1 && (a.out_f32 || a.out_bf16))
+    if (a.n_splits > 1 && (a.out_f32 || a.out_bf16) && !a.merge_ctr)
         attn_combine_kernel<D><<<dim3(R, a.n_heads), D, 0, s>>>(a.part, a.n_heads, a.n_splits, a.out_f32, a.out_bf16,
                                                                 a.out_lo, a.ldo, a.clk);
     return hipGetLastError();
@@ -95,12 +97,18 @@ static hipError_t rows_dispatch_kv(const RowsArgs& a, int R, bool wide, hipStrea
 
 hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, RowMap rm, KVLayer kv, int n_splits,
                             int span_bound, float* part, float* out_f32, uint16_t* out_bf16, uint16_t* out_bf16_lo,
-                            int64_t ldo, uint32_t* err, const QkRope* fuse, WType gt, hipStream_t s) {
+                            int64_t ldo, uint32_t* err, const QkRope* fuse, WType gt, hipStream_t s,
+                            uint32_t* merge_ctr) {
     if (R <= 0) return hipSuccess;
     if (n_splits < 1 || n_splits > 64 || (fuse && (!rm.pos || !rm.seq))) return hipErrorInvalidValue;
     RowsArgs a{};
     a.q = q; a.ldq = ldq; a.n_heads = n_heads; a.rm = rm; a.kv = kv; a.n_splits = n_splits; a.part = part;
     a.out_f32 = out_f32; a.out_bf16 = out_bf16; a.out_lo = out_bf16_lo; a.ldo = ldo; a.err = err;
+    // the last split merges up to kMergeMaxSplits splits itself (measured: 2 splits
+    // of 16 rows, 23.5 -> 22.2 us per block with the combine pass gone); beyond,
+    // the combine pass, which spreads the merge over a workgroup per head, is faster
+    // (32 splits of one 4200-row span: 11.6 us against 13.3 us merging in-kernel)
+    a.merge_ctr = n_splits > 1 && n_splits <= kMergeMaxSplits && (out_f32 || out_bf16) ? merge_ctr : nullptr;
     a.clk = clock_slot();
     if (fuse) {
         a.q_gain = fuse->q_gain; a.k_gain = fuse->k_gain; a.eps = fuse->eps; a.rope = fuse->rope;

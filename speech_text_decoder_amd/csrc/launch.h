@@ -168,9 +168,13 @@ hipError_t launch_gemm(const GemmArgs& g, GemmEpi epi, hipStream_t s);
 // value at each row's position (Q/K norm + RoPE + KV write fused); without
 // it q holds normed, rotated query rows and the cache holds every key.
 // span_bound: an upper bound on the cache rows one split of a row covers.
+// merge_ctr: [R][n_kv] zeroed counts; with it, 2..kMergeMaxSplits splits and an
+// output, the last split of each (row, KV head) merges the splits in the same
+// launch (and zeroes its count) instead of a combine pass.
 hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, RowMap rm, KVLayer kv, int n_splits,
                             int span_bound, float* part, float* out_f32, uint16_t* out_bf16, uint16_t* out_bf16_lo,
-                            int64_t ldo, uint32_t* err, const QkRope* fuse, WType gt, hipStream_t s);
+                            int64_t ldo, uint32_t* err, const QkRope* fuse, WType gt, hipStream_t s,
+                            uint32_t* merge_ctr = nullptr);
 // Causal flash attention (MFMA, f16 cache) of T rows of one slab at positions pos0..
 hipError_t launch_attn_prefill(const uint16_t* q16, int64_t ldq, int T, int pos0, int seq, int n_heads, KVLayer kv,
                                uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo, hipStream_t s);
