@@ -14,12 +14,14 @@ namespace sttd {
 
 // ------------------------------------------------------------------ rows attention (decode)
 // The item body (attn_rows.h) runs one (row, KV head, split) per workgroup.
-template <class KT, class GT, int D, int G, int NW, bool FUSE>
+// PUB: the partials are published with device-scope stores, for the last split
+// of a (row, KV head) to merge in this launch (RowsArgs::merge_ctr); otherwise
+// plain stores, read by the next launch.
+template <class KT, class GT, int D, int G, int NW, bool FUSE, bool PUB>
 __global__ __launch_bounds__(NW * 64) void attn_rows_kernel(RowsArgs a) {
     clock_begin(a.clk);
-    // partials are published with device-scope stores: the last split of a
-    // (row, KV head) may merge them in this launch (RowsArgs::merge_ctr)
-    attn_rows_item<KT, GT, D, G, NW, FUSE, PubMem>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    if (PUB) attn_rows_item<KT, GT, D, G, NW, FUSE, PubMem>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    else attn_rows_item<KT, GT, D, G, NW, FUSE, PlainMem>(a, blockIdx.x, blockIdx.y, blockIdx.z);
     clock_end(a.clk);
 }
 
@@ -63,12 +65,16 @@ static hipError_t rows_dispatch(const RowsArgs& a, int R, bool wide, hipStream_t
     const dim3 grid(R, a.kv.n_kv, a.n_splits);
     // 4 waves per workgroup for groups of up to 2 query heads (the shorter merge tail beats
     // the extra rows in flight) unless a split spans more than 128 cache rows; 8 for larger groups
+    const bool pub = a.merge_ctr != nullptr;
 #define ROWS_LAUNCH(G_)                                                                             \
     do {                                                                                            \
-        if (G_ <= 2 && !wide)                                                                       \
-            attn_rows_kernel<KT, GT, D, G_, 4, FUSE><<<grid, 4 * 64, 0, s>>>(a);                    \
-        else                                                                                        \
-            attn_rows_kernel<KT, GT, D, G_, 8, FUSE><<<grid, 8 * 64, 0, s>>>(a);                    \
+        if (G_ <= 2 && !wide) {                                                                     \
+            if (pub) attn_rows_kernel<KT, GT, D, G_, 4, FUSE, true><<<grid, 4 * 64, 0, s>>>(a);     \
+            else attn_rows_kernel<KT, GT, D, G_, 4, FUSE, false><<<grid, 4 * 64, 0, s>>>(a);        \
+        } else {                                                                                    \
+            if (pub) attn_rows_kernel<KT, GT, D, G_, 8, FUSE, true><<<grid, 8 * 64, 0, s>>>(a);     \
+            else attn_rows_kernel<KT, GT, D, G_, 8, FUSE, false><<<grid, 8 * 64, 0, s>>>(a);        \
+        }                                                                                           \
     } while (0)
     switch (G) {
         case 1: ROWS_LAUNCH(1); break;
