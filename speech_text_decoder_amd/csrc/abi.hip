@@ -252,6 +252,7 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
         }
     }
     // --- attention half: norm + QKV projection
+    bool qk_fused = false;  // the Q|K|V GEMM's epilogue does the Q/K norm, RoPE and cache write
     QkRope qr{};
     qr.q_gain = w->q_norm; qr.k_gain = w->k_norm; qr.eps = eps; qr.rope = ws->rope; qr.max_pos = ws->max_pos;
     qr.rm = rm; qr.kv = kl; qr.q_out = ws->qbuf; qr.q_f16 = flash; qr.ldq = qd; qr.err = ws->err;
@@ -266,8 +267,11 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
         g.w[0] = (const uint16_t*)w->wq; g.w[1] = (const uint16_t*)w->wk; g.w[2] = (const uint16_t*)w->wv;
         g.seg_end[0] = qd; g.seg_end[1] = qd + kvd; g.seg_end[2] = qkv_cols;
         g.N = qkv_cols; g.C = ws->qkv; g.ldc = qkv_cols;
+        // long prefills: per-head norm, RoPE and the cache write in the projection's epilogue
+        qk_fused = flash && !xn_lo && gemm_qkrope_fits(R, qkv_cols, H, d);
+        if (qk_fused) g.qk = qr;
         ProfScope ps(STTD_KERN_QKV_GEMM, s);
-        TRY(launch_gemm(g, GEMM_STORE, s));
+        TRY(launch_gemm(g, qk_fused ? GEMM_QKROPE : GEMM_STORE, s));
     } else {
         GemvArgs a{};
         a.w[0] = w->wq; a.w[1] = w->wk; a.w[2] = w->wv;
@@ -280,7 +284,7 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
     // --- per-head Q/K norm + RoPE + cache write, then attention. Prefill rows of
     // one sequence need every key written first (separate kernel); decode rows
     // (one per slab) do it inside the attention kernel.
-    if (prefill) {
+    if (prefill && !qk_fused) {
         ProfScope ps(STTD_KERN_QK_ROPE_KV, s);
         TRY(launch_qk_norm_rope_kv(ws->qkv, qkv_cols, R, wt, qr, s));
     }

@@ -366,6 +366,48 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
                     g.Cb[(int64_t)m * g.ldcb + c] = hi;
                     if (g.Cb_lo) g.Cb_lo[(int64_t)m * g.ldcb + c] = lo;
                 }
+            } else if (EPI == GEMM_QKROPE) {
+                // the wave's 128 columns are one head (query, key or value) of row m:
+                // lane l holds columns 16 j + l % 16, so the NeoX pair (c, c + 64) is
+                // fragments j and j + 4 of the same lane and the head's sum of squares
+                // is a sum over the 16 lanes of a DPP row (qk_head_item's arithmetic)
+                const QkRope& q = g.qk;
+                const int hi = (tile_n * BN + wn * (BN / 2)) / 128;
+                const int pos = row_pos(q.rm, m), seq = row_seq(q.rm, m);
+                if (pos < 0 || pos >= q.kv.n_ctx || pos >= q.max_pos || seq < 0 || seq >= q.kv.n_seq) {
+                    if (lane % 16 == 0 && wn == 0) record_error(q.err, pos < 0 || pos >= q.kv.n_ctx ? 1u : 2u);
+                    continue;
+                }
+                const int c0 = lane % 16;
+                float v[FN];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) v[j] = acc[i][j][rr];
+                if (hi >= q.n_heads + q.n_kv) {  // value head: copied as it is
+                    const int64_t off = ((int64_t)(seq * q.n_kv + hi - q.n_heads - q.n_kv) * q.kv.n_ctx + pos) * 128;
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) F16::st((uint16_t*)q.kv.v, off + j * 16 + c0, v[j]);
+                    continue;
+                }
+                const bool is_q = hi < q.n_heads;
+                const uint16_t* gain = (const uint16_t*)(is_q ? q.q_gain : q.k_gain);
+                float ss = 0.f;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) ss = fmaf(v[j], v[j], ss);
+                ss = row16_sum(ss);
+                const float rs = 1.0f / sqrtf(ss / 128.f + q.eps);
+                const float2* cs = reinterpret_cast<const float2*>(q.rope) + (int64_t)pos * 64;
+                const int64_t off = is_q ? (int64_t)m * q.ldq + hi * 128
+                                         : ((int64_t)(seq * q.n_kv + hi - q.n_heads) * q.kv.n_ctx + pos) * 128;
+                uint16_t* out = is_q ? (uint16_t*)q.q_out : (uint16_t*)q.kv.k;
+#pragma unroll
+                for (int j = 0; j < FN / 2; ++j) {
+                    const int c = j * 16 + c0;
+                    const float a = v[j] * rs * BF16::ld(gain, c);
+                    const float b = v[j + FN / 2] * rs * BF16::ld(gain, c + 64);
+                    const float2 t = cs[c];
+                    F16::st(out, off + c, a * t.x - b * t.y);
+                    F16::st(out, off + c + 64, a * t.y + b * t.x);
+                }
             } else {
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
@@ -383,7 +425,13 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
 }
 
 // Whether the large tiles apply: many rows, no split activations, shapes that tile.
+bool gemm_qkrope_fits(int M, int N, int K, int head_dim) {
+    return head_dim == 128 && M >= 1024 && K % BIG_BK == 0 && N % BIG_BN == 0 &&
+           ((M + BIG_BM - 1) / BIG_BM) * (N / BIG_BN) >= 256;
+}
+
 static bool big_tiles_fit(const GemmArgs& g, GemmEpi epi) {
+    if (epi == GEMM_QKROPE) return !g.A_lo && gemm_qkrope_fits(g.M, g.N, g.K, g.qk.d);
     if (g.A_lo || g.M < 1024 || g.K % BIG_BK) return false;
     return !(epi == GEMM_SWIGLU && g.N % 128);
 }
@@ -393,6 +441,11 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     if (epi == GEMM_SWIGLU) {
         const int tiles_n = g.N / 128;
         gemm_big_kernel<GEMM_SWIGLU, BIG_BN><<<tiles_m * tiles_n, 512, 0, s>>>(g, tiles_m, tiles_n);
+        return;
+    }
+    if (epi == GEMM_QKROPE) {
+        const int tiles_n = g.N / BIG_BN;
+        gemm_big_kernel<GEMM_QKROPE, BIG_BN><<<tiles_m * tiles_n, 512, 0, s>>>(g, tiles_m, tiles_n);
         return;
     }
     // residual outputs too narrow to fill the CUs even with 256 x 128 tiles: two
@@ -604,6 +657,7 @@ hipError_t launch_gemm(const GemmArgs& args, GemmEpi epi, hipStream_t s) {
     if (args.M <= 0) return hipSuccess;
     GemmArgs g = args;
     g.clk = clock_slot();
+    if (epi == GEMM_QKROPE && !big_tiles_fit(g, epi)) return hipErrorInvalidValue;
     if (g.M <= kSkinnyMaxRows && g.K % 32 == 0) launch_gemm_skinny(g, epi, s);
     else if (big_tiles_fit(g, epi)) launch_gemm_big(g, epi, s);
     else if (g.A_lo) {

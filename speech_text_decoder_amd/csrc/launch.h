@@ -138,7 +138,10 @@ struct HeadArgs {
 hipError_t launch_lm_head_argmax(const HeadArgs& a, WType wt, hipStream_t s);
 
 // ---- MFMA GEMM (kernels_gemm.hip): C = A W^T, A bf16 [M, K], W bf16 [N, K].
-enum GemmEpi { GEMM_STORE = 0, GEMM_RESID = 1, GEMM_SWIGLU = 2 };
+// GEMM_QKROPE: the Q|K|V projection of a prefill with the per-head Q/K RMSNorm,
+// NeoX RoPE, f16 query write and cache write done in the epilogue (GemmArgs::qk;
+// large-M tiles only, see gemm_qkrope_fits)
+enum GemmEpi { GEMM_STORE = 0, GEMM_RESID = 1, GEMM_SWIGLU = 2, GEMM_QKROPE = 3 };
 // A_lo (optional) holds bf16(a - bf16(a)) of every A element with the same
 // stride: the product then takes A + A_lo, an activation operand with about
 // 16 significant bits, at twice the MFMA work (used where HBM bounds the GEMM).
@@ -156,9 +159,13 @@ struct GemmArgs {
     uint16_t* Cb;        // SWIGLU output (bf16, ldcb)
     uint16_t* Cb_lo;     // optional low half of the SWIGLU output
     int64_t ldcb;
+    QkRope qk;           // GEMM_QKROPE: gains, table, row map, cache and q output (q_f16)
     uint64_t* clk;
 };
 hipError_t launch_gemm(const GemmArgs& g, GemmEpi epi, hipStream_t s);
+// Whether launch_gemm takes GEMM_QKROPE for this shape: at least 1024 rows,
+// head_dim 128, and enough 256 x 256 tiles to fill the CUs.
+bool gemm_qkrope_fits(int M, int N, int K, int head_dim);
 
 // ---- attention (kernels_attn.hip)
 // Split-K GQA attention of independent rows (decode, and prefill on f32 caches):
