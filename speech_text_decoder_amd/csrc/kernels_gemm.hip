@@ -348,6 +348,82 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
         __syncthreads();
     }
 
+    if (EPI == GEMM_QKROPE) {
+        // the wave's 128 columns are one head (query, key or value) of its 64 rows:
+        // lane l holds columns 16 j + l % 16, so the NeoX pair (c, c + 64) is
+        // fragments j and j + 4 of the same lane and a row's sum of squares over
+        // the head is a sum over the 16 lanes of a DPP row (qk_head_item's
+        // arithmetic). Gains are loaded once; the table rows of a fragment's 4
+        // rows are all requested before any is used.
+        const QkRope& q = g.qk;
+        const int hi = (tile_n * BN + wn * (BN / 2)) / 128;
+        const int c0 = lane % 16;
+        const bool is_v = hi >= q.n_heads + q.n_kv, is_q = hi < q.n_heads;
+        float gn[FN];
+        const uint16_t* gain = (const uint16_t*)(is_q ? q.q_gain : q.k_gain);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) gn[j] = is_v ? 1.f : BF16::ld(gain, j * 16 + c0);
+        const float2* table = reinterpret_cast<const float2*>(q.rope);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            int pos[4], seq[4];
+            bool ok[4];
+            float2 cs[4][FN / 2];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int m = m0 + wm * 64 + i * 16 + (lane / 16) * 4 + rr;
+                const int mc = m < g.M ? m : g.M - 1;
+                pos[rr] = row_pos(q.rm, mc);
+                seq[rr] = row_seq(q.rm, mc);
+                ok[rr] = m < g.M && pos[rr] >= 0 && pos[rr] < q.kv.n_ctx && pos[rr] < q.max_pos && seq[rr] >= 0 &&
+                         seq[rr] < q.kv.n_seq;
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                for (int j = 0; j < FN / 2; ++j)
+                    cs[rr][j] = is_v ? float2{1.f, 0.f} : table[(int64_t)(ok[rr] ? pos[rr] : 0) * 64 + j * 16 + c0];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int m = m0 + wm * 64 + i * 16 + (lane / 16) * 4 + rr;
+                if (!ok[rr]) {  // the same for the 16 lanes of a DPP row (one row m)
+                    if (m < g.M && c0 == 0 && wn == 0)
+                        record_error(q.err, pos[rr] < 0 || pos[rr] >= q.kv.n_ctx ? 1u : 2u);
+                    continue;
+                }
+                float v[FN];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) v[j] = acc[i][j][rr];
+                if (is_v) {  // value head: copied as it is
+                    const int64_t off =
+                        ((int64_t)(seq[rr] * q.n_kv + hi - q.n_heads - q.n_kv) * q.kv.n_ctx + pos[rr]) * 128;
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) F16::st((uint16_t*)q.kv.v, off + j * 16 + c0, v[j]);
+                    continue;
+                }
+                float ss = 0.f;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) ss = fmaf(v[j], v[j], ss);
+                ss = row16_sum(ss);
+                const float rs = 1.0f / sqrtf(ss / 128.f + q.eps);
+                const int64_t off =
+                    is_q ? (int64_t)m * q.ldq + hi * 128
+                         : ((int64_t)(seq[rr] * q.n_kv + hi - q.n_heads) * q.kv.n_ctx + pos[rr]) * 128;
+                uint16_t* out = is_q ? (uint16_t*)q.q_out : (uint16_t*)q.kv.k;
+#pragma unroll
+                for (int j = 0; j < FN / 2; ++j) {
+                    const int c = j * 16 + c0;
+                    const float a = v[j] * rs * gn[j];
+                    const float b = v[j + FN / 2] * rs * gn[j + FN / 2];
+                    F16::st(out, off + c, a * cs[rr][j].x - b * cs[rr][j].y);
+                    F16::st(out, off + c + 64, a * cs[rr][j].y + b * cs[rr][j].x);
+                }
+            }
+        }
+        clock_end(g.clk);
+        return;
+    }
+
     // epilogue
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -365,48 +441,6 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
                     split_bf16(a, hi, lo);
                     g.Cb[(int64_t)m * g.ldcb + c] = hi;
                     if (g.Cb_lo) g.Cb_lo[(int64_t)m * g.ldcb + c] = lo;
-                }
-            } else if (EPI == GEMM_QKROPE) {
-                // the wave's 128 columns are one head (query, key or value) of row m:
-                // lane l holds columns 16 j + l % 16, so the NeoX pair (c, c + 64) is
-                // fragments j and j + 4 of the same lane and the head's sum of squares
-                // is a sum over the 16 lanes of a DPP row (qk_head_item's arithmetic)
-                const QkRope& q = g.qk;
-                const int hi = (tile_n * BN + wn * (BN / 2)) / 128;
-                const int pos = row_pos(q.rm, m), seq = row_seq(q.rm, m);
-                if (pos < 0 || pos >= q.kv.n_ctx || pos >= q.max_pos || seq < 0 || seq >= q.kv.n_seq) {
-                    if (lane % 16 == 0 && wn == 0) record_error(q.err, pos < 0 || pos >= q.kv.n_ctx ? 1u : 2u);
-                    continue;
-                }
-                const int c0 = lane % 16;
-                float v[FN];
-#pragma unroll
-                for (int j = 0; j < FN; ++j) v[j] = acc[i][j][rr];
-                if (hi >= q.n_heads + q.n_kv) {  // value head: copied as it is
-                    const int64_t off = ((int64_t)(seq * q.n_kv + hi - q.n_heads - q.n_kv) * q.kv.n_ctx + pos) * 128;
-#pragma unroll
-                    for (int j = 0; j < FN; ++j) F16::st((uint16_t*)q.kv.v, off + j * 16 + c0, v[j]);
-                    continue;
-                }
-                const bool is_q = hi < q.n_heads;
-                const uint16_t* gain = (const uint16_t*)(is_q ? q.q_gain : q.k_gain);
-                float ss = 0.f;
-#pragma unroll
-                for (int j = 0; j < FN; ++j) ss = fmaf(v[j], v[j], ss);
-                ss = row16_sum(ss);
-                const float rs = 1.0f / sqrtf(ss / 128.f + q.eps);
-                const float2* cs = reinterpret_cast<const float2*>(q.rope) + (int64_t)pos * 64;
-                const int64_t off = is_q ? (int64_t)m * q.ldq + hi * 128
-                                         : ((int64_t)(seq * q.n_kv + hi - q.n_heads) * q.kv.n_ctx + pos) * 128;
-                uint16_t* out = is_q ? (uint16_t*)q.q_out : (uint16_t*)q.kv.k;
-#pragma unroll
-                for (int j = 0; j < FN / 2; ++j) {
-                    const int c = j * 16 + c0;
-                    const float a = v[j] * rs * BF16::ld(gain, c);
-                    const float b = v[j + FN / 2] * rs * BF16::ld(gain, c + 64);
-                    const float2 t = cs[c];
-                    F16::st(out, off + c, a * t.x - b * t.y);
-                    F16::st(out, off + c + 64, a * t.y + b * t.x);
                 }
             } else {
 #pragma unroll
