@@ -3,6 +3,8 @@
 // kernel and by the fused decode-step kernel.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -353,48 +355,58 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
     // 8. several splits and an output: the split of this (row, KV head) that
     //    finishes last merges all partial records and writes o, so no combine
     //    pass runs. The partials were published with device-scope stores, which
-    //    each wave waits for before the count; the merging split reads them with
-    //    device-scope loads (records of neighbouring pairs share cache lines,
-    //    which a plain load could find stale in this XCD's L2). It resets the
-    //    count for the next launch.
-    if (a.merge_ctr && a.n_splits > 1) {
-        __shared__ int is_last;
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have completed
-        __syncthreads();
-        if (tid == 0) {
-            uint32_t* c = a.merge_ctr + (int64_t)r * a.kv.n_kv + j;
-            const uint32_t old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            is_last = old == (uint32_t)(a.n_splits - 1);
-            if (is_last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-        if (is_last) {
-            for (int t = tid; t < G * D; t += NW * 64) {
-                const int g = t / D, e = t % D;
-                const float* pp = a.part + ((int64_t)r * a.n_heads + j * G + g) * a.n_splits * (D + 4);
-                float M = -INFINITY, L = 0.f, O = 0.f;
-#pragma unroll 8
-                for (int sp = 0; sp < a.n_splits; ++sp) {
-                    const float* q = pp + (int64_t)sp * (D + 4);
-                    const float ms = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    const float ls = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    const float os = __hip_atomic_load(q + 4 + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    const float Mn = fmaxf(M, ms);
-                    const float fa = Mn == -INFINITY ? 0.f : exp2f(M - Mn);
-                    const float fb = Mn == -INFINITY ? 0.f : exp2f(ms - Mn);
-                    L = L * fa + ls * fb;
-                    O = O * fa + os * fb;
-                    M = Mn;
-                }
-                const float v = L > 0.f ? O / L : 0.f;
-                const int64_t idx = (int64_t)r * a.ldo + (j * G + g) * D + e;
-                if (a.out_f32) {
-                    a.out_f32[idx] = v;
-                } else {
-                    uint16_t hi, lo;
-                    split_bf16(v, hi, lo);
-                    a.out_bf16[idx] = hi;
-                    if (a.out_lo) a.out_lo[idx] = lo;
+    //    each wave waits for before the count. The merging split copies the
+    //    G * n_splits records into LDS with device-scope loads, every thread's
+    //    loads in flight at once (records of neighbouring pairs share cache
+    //    lines, which a plain load could find stale in this XCD's L2), then
+    //    merges from LDS. It resets the count for the next launch. Only the
+    //    publishing instantiation carries this (and its LDS).
+    if constexpr (std::is_same<MEM, PubMem>::value) {
+        if (a.merge_ctr && a.n_splits > 1) {
+            constexpr int MREC = 64;  // records staged: G * n_splits <= MREC (checked on the host)
+            __shared__ __attribute__((aligned(16))) float mrg[MREC * (D + 4)];
+            __shared__ int is_last;
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have completed
+            __syncthreads();
+            if (tid == 0) {
+                uint32_t* c = a.merge_ctr + (int64_t)r * a.kv.n_kv + j;
+                const uint32_t old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                is_last = old == (uint32_t)(a.n_splits - 1);
+                if (is_last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+            if (is_last) {
+                // the G heads' records are contiguous: record (g, split) at (g * n_splits + split) * (D + 4)
+                const int nrec = G * a.n_splits;
+                const uint64_t* src = reinterpret_cast<const uint64_t*>(
+                    a.part + ((int64_t)r * a.n_heads + j * G) * a.n_splits * (D + 4));
+                uint64_t* dst = reinterpret_cast<uint64_t*>(mrg);
+                for (int i = tid; i < nrec * (D + 4) / 2; i += NW * 64)
+                    dst[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __syncthreads();
+                for (int t = tid; t < G * D; t += NW * 64) {
+                    const int g = t / D, e = t % D;
+                    const float* rec = mrg + g * a.n_splits * (D + 4);
+                    float M = -INFINITY;
+                    for (int sp = 0; sp < a.n_splits; ++sp) M = fmaxf(M, rec[sp * (D + 4)]);
+                    float L = 0.f, O = 0.f;
+                    if (M != -INFINITY) {
+                        for (int sp = 0; sp < a.n_splits; ++sp) {
+                            const float w = exp2f(rec[sp * (D + 4)] - M);
+                            L = fmaf(w, rec[sp * (D + 4) + 1], L);
+                            O = fmaf(w, rec[sp * (D + 4) + 4 + e], O);
+                        }
+                    }
+                    const float v = L > 0.f ? O / L : 0.f;
+                    const int64_t idx = (int64_t)r * a.ldo + (j * G + g) * D + e;
+                    if (a.out_f32) {
+                        a.out_f32[idx] = v;
+                    } else {
+                        uint16_t hi, lo;
+                        split_bf16(v, hi, lo);
+                        a.out_bf16[idx] = hi;
+                        if (a.out_lo) a.out_lo[idx] = lo;
+                    }
                 }
             }
         }

@@ -110,11 +110,15 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
     RowsArgs a{};
     a.q = q; a.ldq = ldq; a.n_heads = n_heads; a.rm = rm; a.kv = kv; a.n_splits = n_splits; a.part = part;
     a.out_f32 = out_f32; a.out_bf16 = out_bf16; a.out_lo = out_bf16_lo; a.ldo = ldo; a.err = err;
-    // the last split merges up to kMergeMaxSplits splits itself (measured: 2 splits
-    // of 16 rows, 23.5 -> 22.2 us per block with the combine pass gone); beyond,
-    // the combine pass, which spreads the merge over a workgroup per head, is faster
-    // (32 splits of one 4200-row span: 11.6 us against 13.3 us merging in-kernel)
-    a.merge_ctr = n_splits > 1 && n_splits <= kMergeMaxSplits && (out_f32 || out_bf16) ? merge_ctr : nullptr;
+    // the last split merges up to kMergeMaxSplits splits itself (their G * n_splits
+    // records staged in LDS), so no combine pass runs (measured: 2 splits of 16 rows,
+    // 23.5 -> 22 us per block). With many splits every split's wait for its
+    // write-through stores costs more than the combine launch (32 splits of one
+    // 4200-row span: 13.8 us in-kernel against 11.6 us with the combine pass).
+    const int group = n_heads / kv.n_kv;
+    a.merge_ctr = n_splits > 1 && n_splits <= kMergeMaxSplits && group * n_splits <= 64 && (out_f32 || out_bf16)
+                      ? merge_ctr
+                      : nullptr;
     a.clk = clock_slot();
     if (fuse) {
         a.q_gain = fuse->q_gain; a.k_gain = fuse->k_gain; a.eps = fuse->eps; a.rope = fuse->rope;
