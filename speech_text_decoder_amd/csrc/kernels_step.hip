@@ -356,22 +356,27 @@ hipError_t launch_step_fused(const StepFusedArgs& a, hipStream_t s) {
     // Every workgroup must be resident at once: at most what the occupancy
     // allows (two per CU suffice), and no more than 512, the items of the
     // 1.7B shape's Q, O and down stages.
+    struct GridOf {
+        StepKernel k;
+        int dev, grid;
+    };
     static std::mutex mu;
-    static std::vector<std::pair<StepKernel, int>> grids;
-    int grid = 0;
+    static std::vector<GridOf> grids;  // per (kernel, device)
+    int dev = 0, grid = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
     {
         std::lock_guard<std::mutex> lk(mu);
         for (const auto& g : grids)
-            if (g.first == k) grid = g.second;
+            if (g.k == k && g.dev == dev) grid = g.grid;
         if (!grid) {
-            int dev = 0, cus = 0, per_cu = 0;
-            hipError_t e = hipGetDevice(&dev);
-            if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            int cus = 0, per_cu = 0;
+            e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
             if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k, 256, 0);
             if (e != hipSuccess) return e;
             if (per_cu < 1 || cus < 1) return hipErrorInvalidValue;
             grid = min(cus * min(per_cu, 2), 512);
-            grids.emplace_back(k, grid);
+            grids.push_back({k, dev, grid});
         }
     }
     RowsArgs ra{};
