@@ -183,3 +183,31 @@ def test_injection_then_packed_stack_prefill_and_per_sequence_ids():
             assert got[b] == O.greedy_token(want[b])
     assert sess.error_bits() == 0
     sess.close()
+
+
+def test_packed_prefill_fp32_cache_rows_attention():
+    """bf16 weights on an f32 cache: the packed rows go through the rows-attention
+    kernel with per-row positions and slabs (no flash tiles)."""
+    sh = replace(SMALL128, kvdtype="f32")
+    e, _, _ = packed_case(sh, 59, [21, 9, 40], [1, 2, 0], pos0s=[0, 0, 0])
+    log(f"packed on an f32 cache: {e:.2e}")
+
+
+def test_packed_prefill_fp32_weights_tiny_block():
+    """The fp32 block (fp32 weights, f32 cache) packed: 1e-4 relative bound."""
+    sh = WORKLOADS["tiny_fp32_block"].shape
+    w = synth.block_weights(60, 0, sh)
+    ow = widen_layer(w)
+    Ts, slabs = [12, 20], [1, 0]
+    x = synth.prefill_rows(60, sum(Ts), sh.hidden)
+    sess = DecoderSession(sh, [w], n_ctx=64, n_seq=2, max_rows=sum(Ts))
+    cache = O.KVCache(1, 2, 64, sh.n_kv_heads, sh.head_dim)
+    positions = np.concatenate([np.arange(T) for T in Ts])
+    seqs = np.concatenate([np.full(T, s) for s, T in zip(slabs, Ts)])
+    want = O.block(x, positions, seqs, ow, sh, cache, 0)
+    xd = dev(x)
+    sess.prefill_batched(xd, Ts, slabs)
+    torch.cuda.synchronize()
+    check(xd.cpu().numpy(), want, True, "packed fp32 block")
+    assert sess.error_bits() == 0
+    sess.close()
