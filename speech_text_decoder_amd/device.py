@@ -113,7 +113,7 @@ class DecoderSession:
                 _wrap(v, n, dt, self.device).view(sh.n_kv_heads, self.n_ctx, sh.head_dim))
 
     def set_fused_step(self, enabled: bool):
-        """STTD_OPT_FUSED_STEP: single-row steps as one persistent launch per block (default on)."""
+        """STTD_OPT_FUSED_STEP: single-row steps as one persistent launch per block (default off)."""
         B.workspace_set_option(self.ws, B.OPT_FUSED_STEP, 1 if enabled else 0)
 
     def error_bits(self):
