@@ -486,7 +486,7 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     // K halves of each 256 x 256 tile, added into the residual with atomics
     // (measured at 1224 rows and 2048 columns: down 104 -> 89 us, O 46 -> 38 us;
     // at 4096 rows, where 256 x 128 tiles already make 256 workgroups, the split
-    // was slower: O 55 -> 68 us)
+    // was slower: O 55 -> 68 us, and down (K = 6144) 125 -> 137-144 us)
     const int tiles256 = tiles_m * ((g.N + BIG_BN - 1) / BIG_BN);
     const int tiles128 = tiles_m * ((g.N + 127) / 128);
     if (epi == GEMM_RESID && tiles128 < 256 && tiles256 % 8 == 0 && (g.K / BIG_BK) % 2 == 0 &&
