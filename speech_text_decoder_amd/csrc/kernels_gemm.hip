@@ -674,8 +674,9 @@ static hipError_t launch_gemm_t(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     }
     dim3 grid((g.N + BN - 1) / BN, gy, 1);
     // Few workgroups: split K over them (atomic adds into C, which a STORE zeroes first)
-    // while fewer than ~256 run and each keeps >= 4 K-steps
-    while (grid.x * grid.y * grid.z * 2 <= 256 && g.K / BK >= (int)grid.z * 2 * 4) grid.z *= 2;
+    // while fewer than ~512 run (two per CU hide each K-step's load latency) and each
+    // keeps >= 4 K-steps
+    while (grid.x * grid.y * grid.z * 2 <= 512 && g.K / BK >= (int)grid.z * 2 * 4) grid.z *= 2;
     if (epi == GEMM_STORE && grid.z > 1 && g.ldc != g.N) grid.z = 1;  // zeroing needs contiguous rows
     if (epi == GEMM_STORE && grid.z > 1) {
         const hipError_t e = launch_fill_zero(g.C, (size_t)g.M * g.N * sizeof(float), s);
