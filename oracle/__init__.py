@@ -6,7 +6,7 @@ cpu_baseline leg of bench.py may import it; the HIP path never does.
 Parity status of each function (what pins it is in tests/test_oracle_pins.py):
   rms_norm, rope_neox, silu, softmax, gqa_attention_row, block,
   block_rows_subset, final_logits, greedy_token, prefill_stack, step_stack,
-  greedy_generate, inject, greedy_loop: pinned by closed forms, library special cases,
+  greedy_generate, inject, greedy_loop, top2_margin: pinned by closed forms, library special cases,
   brute force, the causal / batching invariants, and (inject) the pages'
   second form of the same injection, the 3-way concat. The pages print no numeric worked
   example of any decoder output, so no value of the pages' own pins them;

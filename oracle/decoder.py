@@ -243,8 +243,19 @@ def greedy_token(logits):
 
 
 def top2_margin(logits):
-    l = np.sort(np.asarray(logits, dtype=np.float64))
-    return float(l[-1] - l[-2])
+    """Gap between the largest and the second-largest logit of one row: the
+    quantity the greedy-token check compares with its 1e-2 threshold. NaN counts
+    as -inf, as in greedy_token; equal top values give 0; a row with one finite
+    value gives +inf."""
+    l = np.asarray(logits, dtype=np.float64).copy()
+    l[np.isnan(l)] = -np.inf
+    i = int(np.argmax(l))
+    top = l[i]
+    l[i] = -np.inf
+    second = np.max(l)
+    if top == second:
+        return 0.0
+    return float(top - second)
 
 
 # ---------------------------------------------------------------- drivers

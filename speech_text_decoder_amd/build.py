@@ -7,6 +7,7 @@ import glob
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -41,12 +42,13 @@ def build_hip():
     if not srcs:
         return None
     out = os.path.join(HERE, "libsttd.so")
-    objs = []
-    for s in srcs:
-        o = os.path.join(CSRC, "_obj_" + os.path.basename(s) + ".o")
-        _run([HIPCC] + [f for f in HIP_FLAGS if f != "-shared"] + ["-I", os.path.join(ROOT, "include"),
-                                                                     "-c", s, "-o", o])
-        objs.append(o)
+    objs = [os.path.join(CSRC, "_obj_" + os.path.basename(s) + ".o") for s in srcs]
+    cmds = [[HIPCC] + [f for f in HIP_FLAGS if f != "-shared"] + ["-I", os.path.join(ROOT, "include"), "-c", s, "-o", o]
+            for s, o in zip(srcs, objs)]
+    # one compiler per source file, at most `jobs` at a time
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(jobs) as pool:
+        list(pool.map(_run, cmds))
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", out + ".tmp"])
     os.replace(out + ".tmp", out)
     for o in objs:

@@ -29,6 +29,9 @@ MUTATIONS = {
                              'return rows + f64(audio_dense) * f64(keep)[:, None]'),
     "loop_context_off_by_one": ('cur + 1 <= n_ctx', 'cur + 1 < n_ctx'),
     "loop_budget_excludes_first": ('len(tokens) < max_new', 'len(tokens) <= max_new'),
+    "margin_to_smallest": ('second = np.max(l)', 'second = np.min(np.where(np.isinf(l), np.inf, l))'),
+    "margin_keeps_nan": ('l[np.isnan(l)] = -np.inf\n    i = int(np.argmax(l))',
+                         'i = int(np.argmax(l))'),
 }
 
 

@@ -327,6 +327,25 @@ def test_argmax_planted_ties_nan_and_monotone():
     assert O.greedy_token(l3) == 0
 
 
+def test_top2_margin_closed_forms():
+    """The margin that gates every greedy-id check: largest minus second largest,
+    whatever the order of the row, with ties at the top giving 0 and NaN counted
+    as -inf (the same rule as the argmax)."""
+    assert O.top2_margin([3.0, 1.0, 2.0]) == 1.0                    # unsorted
+    assert O.top2_margin([-5.0, -2.0, -7.0]) == 3.0                 # all negative
+    assert O.top2_margin([1.0, 4.0, 4.0, 0.0]) == 0.0               # tie at the top
+    assert O.top2_margin([0.5, 4.0, 2.5, 4.0 - 2 ** -20]) == 2 ** -20
+    assert O.top2_margin([np.nan, 2.0, 1.0]) == 1.0                 # NaN never counts as the top
+    assert O.top2_margin([2.0, np.nan, 5.0, -1.0]) == 3.0
+    assert O.top2_margin([np.nan, 7.0, np.nan]) == np.inf           # one finite value
+    rng = np.random.default_rng(11)
+    row = rng.standard_normal(151936)
+    row[90000] = 9.0
+    row[123] = 8.75
+    assert O.top2_margin(row) == 0.25
+    assert O.top2_margin(row[::-1]) == 0.25
+
+
 def test_final_logits_tied_head_closed_form():
     rng = np.random.default_rng(20)
     E = rng.standard_normal((50, 16))
