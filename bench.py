@@ -65,6 +65,11 @@ def parse():
                     help="independent weight/KV replicas stacked for single-block workloads (MALL honesty)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-profile", action="store_true")
+    ap.add_argument("--act-split", type=int, default=None,
+                    help="STTD_OPT_ACT_SPLIT mask (GEMM inputs split into bf16 hi/lo above 512 rows); default: "
+                         "the library's (all four) for stacks, 0 for the single-block workloads")
+    ap.add_argument("--no-prefill-leg", action="store_true",
+                    help="skip the 4096-row single-block prefill figure carried on the default line")
     ap.add_argument("--fused-step", action="store_true",
                     help="single-row decode steps as one persistent launch per block (STTD_OPT_FUSED_STEP)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -114,6 +119,18 @@ def decode_step_bytes(sh, n_layers, rows, mean_keys, with_head):
 
 
 # ---------------------------------------------------------------- helpers
+def cpu_model():
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -170,29 +187,96 @@ def clock_profile(binding, torch, stream, eager=None, capture=None, reps=8):
     return totals
 
 
-def kernel_table(totals, sh, rows_of, keys_of):
-    """Attach algorithmic bytes/flops per launch and the achieved rates to the clock spans."""
+def event_profile(binding, torch, stream, fn):
+    """Per-kernel HIP-event durations: fn() launches eagerly on `stream` with every
+    kernel family bracketed by an event pair on that stream (sttd_profile_enable).
+    Event pairs cover the dispatch and the end-of-kernel release, as rocprofv3's
+    durations do. Returns {name: [launches, total_us]}."""
+    binding.profile_enable(ALL_KERNELS)
+    with torch.cuda.stream(stream):
+        fn()
+    torch.cuda.synchronize()
+    binding.profile_enable(0)
+    out = {}
+    for k, name in enumerate(KERNEL_NAMES):
+        n, ms = binding.profile_read(k)
+        if n:
+            out[name] = [n, ms * 1e3]
+    return out
+
+
+def kernel_table(totals, sh, rows_of, keys_of, events=None):
+    """Attach algorithmic bytes/flops per launch and the achieved rates to the
+    device-clock spans (and to the HIP-event durations, when given)."""
     out = {}
     for name, (n, us) in totals.items():
         avg_us = us / n
         b, f = kernel_cost(name, sh, rows_of(name), keys_of(name))
-        out[name] = {"launches": n, "avg_us": round(avg_us, 3), "bytes": int(b), "flops": f,
-                     "gbs": round(b / (avg_us * 1e-6) / 1e9, 1) if b else None,
-                     "tflops": round(f / (avg_us * 1e-6) / 1e12, 2) if f else None}
+        e = {"launches": n, "avg_us": round(avg_us, 3), "bytes": int(b), "flops": f,
+             "gbs": round(b / (avg_us * 1e-6) / 1e9, 1) if b else None,
+             "tflops": round(f / (avg_us * 1e-6) / 1e12, 2) if f else None}
+        if events and name in events:
+            ev_us = events[name][1] / events[name][0]
+            e["event_avg_us"] = round(ev_us, 3)
+            e["event_gbs"] = round(b / (ev_us * 1e-6) / 1e9, 1) if b else None
+            e["event_tflops"] = round(f / (ev_us * 1e-6) / 1e12, 2) if f else None
+        out[name] = e
     return out
 
 
+def job_roofline(phases):
+    """The roofline object of the kernel family that takes the most time over the
+    job. phases: [(phase, table, events, launches_per_job_scale, rows_of)], where
+    events[name] = [launches, total_us] of the profiled launches and the scale turns
+    those into per-job time (e.g. steps per job / steps profiled)."""
+    best = None
+    total = 0.0
+    for phase, table, events, scale, rows_of in phases:
+        for name, (n, us) in events.items():
+            t = us * scale
+            total += t
+            if name in table and (best is None or t > best[0]):
+                best = (t, phase, table, name, rows_of(name))
+    if best is None:
+        return None
+    t, phase, table, name, rows = best
+    r = roofline_entry(table, name, kernel_bound(name, rows), rows)
+    r["phase"] = phase
+    r["job_share"] = round(t / total, 4) if total else None
+    return r
+
+
 def roofline_entry(table, name, bound, rows=1):
+    """The roofline object of one kernel family. achieved = algorithmic bytes (flops)
+    per launch / the HIP-event average duration of its launches (the headline; it
+    covers what rocprofv3's kernel durations cover); the device-clock span figure
+    (first workgroup start to last workgroup end, shorter by the dispatch and the
+    end-of-kernel release) is reported beside it."""
     e = table.get(name)
     if not e:
         return None
+    ev_us = e.get("event_avg_us", e["avg_us"])
+    timing = "hip events" if "event_avg_us" in e else "device clock"
     if bound == "hbm":
-        return {"kernel": name, "bound": "hbm", "achieved": e["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(e["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(name, rows), "avg_us": e["avg_us"],
-                "bytes_per_launch": e["bytes"]}
-    return {"kernel": name, "bound": "mfma", "achieved": e["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(e["tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": None, "avg_us": e["avg_us"],
-            "flops_per_launch": e.get("flops")}
+        ach = e["bytes"] / (ev_us * 1e-6) / 1e9
+        return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(name, rows), "avg_us": round(ev_us, 3),
+                "timing": timing, "bytes_per_launch": e["bytes"], "device_span_avg_us": e["avg_us"],
+                "device_span_frac": round(e["gbs"] / HBM_PEAK_GBS, 4)}
+    ach = e["flops"] / (ev_us * 1e-6) / 1e12
+    return {"kernel": name, "bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None, "avg_us": round(ev_us, 3), "timing": timing,
+            "flops_per_launch": e.get("flops"), "device_span_avg_us": e["avg_us"],
+            "device_span_frac": round(e["tflops"] / BF16_PEAK_TFLOPS, 4)}
+
+
+def kernel_bound(name, rows):
+    """Which roof a kernel family is held to at this row count: MFMA for the many-row
+    GEMMs and the flash attention (arithmetic intensity above the ~315 FLOP/B ridge),
+    HBM for everything that streams weights or the cache."""
+    if name == "attn_prefill" or (name.endswith("gemm") and rows >= 1024):
+        return "mfma"
+    return "hbm"
 
 
 # ---------------------------------------------------------------- greedy stack (prefill + greedy decode)
@@ -209,6 +293,8 @@ def bench_greedy_stack(args, wl):
     x_host = synth.prefill_rows(wl.cfg_id, T, sh.hidden)
     sess = DecoderSession(sh, layers, embed=E, final_norm=g, n_ctx=wl.n_ctx, max_rows=T)
     sess.set_fused_step(args.fused_step)
+    if args.act_split is not None:
+        sess.set_act_split(args.act_split)
     x0 = torch.from_numpy(x_host).cuda()
     x = torch.empty_like(x0)
     xs = torch.zeros(1, sh.hidden, device="cuda")
@@ -279,20 +365,34 @@ def bench_greedy_stack(args, wl):
         "config": {"workload": wl.name, "layers": sh.n_layers, "hidden": sh.hidden, "heads": sh.n_heads,
                    "kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim, "ffn": sh.ffn, "vocab": sh.vocab,
                    "prefill_rows": T, "new_tokens": new_tokens, "batch": 1, "kv_dtype": sh.kvdtype,
-                   "n_ctx": wl.n_ctx, "parallelism": "none (1 GPU)", "fused_step": args.fused_step},
+                   "n_ctx": wl.n_ctx, "parallelism": "none (1 GPU)", "fused_step": args.fused_step,
+                   "act_split_above_512_rows": args.act_split if args.act_split is not None else 15},
     }
     if not args.no_kernel_profile:
-        # device-clock spans: the prefill part eagerly, the decode step+head as a replayed graph
+        # device-clock spans: the prefill part eagerly, the decode step+head as a replayed
+        # graph; HIP-event durations: the same launches eagerly. Each profile starts from a
+        # fresh prefill, so the decode steps run at positions T, T + 1, ...
         reps = 16
+
+        def dec_steps():
+            for _ in range(reps):
+                sess.step(xs, pos, pos_bound=wl.n_ctx)
+                sess.head(xs, ids, next_x=xs, pos=pos)
+
         pre = clock_profile(binding, torch, stream, eager=lambda: prefill_part(stream))
         dec = clock_profile(binding, torch, stream, reps=reps, capture=lambda: (
             sess.step(xs, pos, pos_bound=wl.n_ctx), sess.head(xs, ids, next_x=xs, pos=pos)))
+        pre_ev = event_profile(binding, torch, stream, lambda: prefill_part(stream))
+        dec_ev = event_profile(binding, torch, stream, dec_steps)
         torch.cuda.synchronize()
         rows = lambda n: T if n.endswith("gemm") or n in ("rmsnorm", "attn_prefill") else 1
-        res["kernels"] = {"prefill": kernel_table(pre, sh, rows, lambda n: T),
-                          "decode": kernel_table(dec, sh, lambda n: 1, lambda n: T + 1 + reps / 2.0)}
-        res["kernel_timing"] = "device clock (s_memrealtime, 100 MHz): first-workgroup start to last-workgroup end"
-        res["roofline"] = roofline_entry(res["kernels"]["decode"], "gateup_gemv", "hbm")
+        res["kernels"] = {"prefill": kernel_table(pre, sh, rows, lambda n: T, pre_ev),
+                          "decode": kernel_table(dec, sh, lambda n: 1, lambda n: T + 1 + reps / 2.0, dec_ev)}
+        res["kernel_timing"] = ("avg_us: device clock (s_memrealtime, 100 MHz), first-workgroup start to "
+                                "last-workgroup end; event_avg_us: HIP event pair around each eager launch")
+        res["roofline"] = job_roofline([("prefill", res["kernels"]["prefill"], pre_ev, 1.0, rows),
+                                        ("decode", res["kernels"]["decode"], dec_ev, n_steps / reps,
+                                         lambda n: 1)])
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_greedy(wl, layers, E, g, x_host, new_tokens)
     sess.close()
@@ -322,6 +422,7 @@ def cpu_baseline_greedy(wl, layers, E, g, x_host, new_tokens):
     step_s = (t2 - t1) / n
     job_s = (t1 - t0) + (new_tokens - 1) * step_s
     return {"value": round(new_tokens / job_s, 4), "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"fp64 oracle: {T}-row prefill of the 28-block stack + head ({t1 - t0:.1f} s), then {n} greedy "
                       f"steps ({step_s:.2f} s each); job time extrapolated to {new_tokens} new tokens",
             "prefill_tok_s": round(T / (t1 - t0), 2), "decode_tok_s": round(1.0 / step_s, 4)}
@@ -346,17 +447,21 @@ def bench_packed_prefill(args, wl):
     g = synth.final_norm(wl.cfg_id, sh)
     ids_h, keep_h, dense_h = synth.injected_prompts(wl.cfg_id, Bn, wl.prompt_split, sh.hidden, sh.vocab)
     sess = DecoderSession(sh, layers, embed=E, final_norm=g, n_ctx=wl.n_ctx, n_seq=Bn, max_rows=Bn * T)
+    if args.act_split is not None:
+        sess.set_act_split(args.act_split)
     ids_d = torch.from_numpy(ids_h).cuda()
     keep_d = torch.from_numpy(keep_h).cuda()
     dense_d = torch.from_numpy(dense_h).cuda()
     x = torch.empty(Bn * T, sh.hidden, device="cuda")
     out_ids = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    last_rows = torch.arange(1, Bn + 1, dtype=torch.int32, device="cuda") * T - 1
     stream = torch.cuda.Stream()
 
     def packed_job():
         sess.inject(ids_d, keep_d, dense_d, x, stream=stream)
         sess.prefill_batched(x, [T] * Bn, list(range(Bn)), stream=stream)
-        sess.head(x[T - 1:], out_ids, row_stride=T * sh.hidden, rows=Bn, stream=stream)
+        # each prompt's last row, picked on the device by row index
+        sess.head(x, out_ids, x_rows=last_rows, stream=stream)
 
     def separate_job():
         for b in range(Bn):
@@ -397,16 +502,19 @@ def bench_packed_prefill(args, wl):
         "config": {"workload": wl.name, "layers": sh.n_layers, "hidden": sh.hidden, "heads": sh.n_heads,
                    "kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim, "ffn": sh.ffn, "vocab": sh.vocab,
                    "prompts": Bn, "prompt_rows": T, "prompt_split": list(wl.prompt_split), "kv_dtype": sh.kvdtype,
-                   "n_ctx": wl.n_ctx, "parallelism": "none (1 GPU)"},
+                   "n_ctx": wl.n_ctx, "parallelism": "none (1 GPU)",
+                   "act_split_above_512_rows": args.act_split if args.act_split is not None else 15},
     }
     if not args.no_kernel_profile:
         prof = clock_profile(binding, torch, stream, eager=packed_job)
+        ev = event_profile(binding, torch, stream, packed_job)
         torch.cuda.synchronize()
         rws = lambda n: rows if n.endswith("gemm") or n in ("rmsnorm", "qk_rope_kv") else (
             T if n == "attn_prefill" else Bn)
-        res["kernels"] = {"prefill": kernel_table(prof, sh, rws, lambda n: T)}
-        res["kernel_timing"] = "device clock (s_memrealtime, 100 MHz): first-workgroup start to last-workgroup end"
-        res["roofline"] = roofline_entry(res["kernels"]["prefill"], "gateup_gemm", "mfma")
+        res["kernels"] = {"prefill": kernel_table(prof, sh, rws, lambda n: T, ev)}
+        res["kernel_timing"] = ("avg_us: device clock (s_memrealtime, 100 MHz), first-workgroup start to "
+                                "last-workgroup end; event_avg_us: HIP event pair around each eager launch")
+        res["roofline"] = job_roofline([("prefill", res["kernels"]["prefill"], ev, 1.0, rws)])
     if not args.no_cpu_baseline:
         import oracle as O
         ol = [{k: synth.widen(v).astype(np.float64) for k, v in w.items()} for w in layers]
@@ -418,7 +526,8 @@ def bench_packed_prefill(args, wl):
         O.greedy_token(O.final_logits(last, synth.widen(g), Ef, sh.rms_eps)[0])
         dt = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": round(T / dt, 2), "unit": "tokens/s", "cores": cpu_threads(),
-                               "kind": "oracle", "sample": f"fp64 oracle: one of the {Bn} prompts ({T} rows: "
+                               "kind": "oracle", "cpu_model": cpu_model(),
+                               "sample": f"fp64 oracle: one of the {Bn} prompts ({T} rows: "
                                f"injection, 28 blocks, head) in {dt:.1f} s"}
     sess.close()
     return res
@@ -441,6 +550,9 @@ def bench_block(args, wl):
     rows_host = np.stack([synth.step_rows(wl.cfg_id, k, 1, sh.hidden)[0] for k in range(n_steps)])
     sess = DecoderSession(sh, layers, n_ctx=wl.n_ctx, max_rows=T)
     sess.set_fused_step(args.fused_step)
+    # one block (the replicas are independent single blocks): plain bf16 activations
+    # above 512 rows stay within the parity bound for a single block
+    sess.set_act_split(args.act_split if args.act_split is not None else 0)
     x0 = torch.from_numpy(x_host).cuda()
     x = torch.empty_like(x0)
     r0 = torch.from_numpy(rows_host).cuda()
@@ -501,7 +613,8 @@ def bench_block(args, wl):
         "config": {"workload": wl.name, "replicas": R, "hidden": sh.hidden, "heads": sh.n_heads,
                    "kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim, "ffn": sh.ffn, "prefill_rows": T,
                    "decode_steps": n_steps, "batch": 1, "kv_dtype": sh.kvdtype, "wdtype": sh.wdtype,
-                   "parallelism": "none (1 GPU)", "fused_step": args.fused_step},
+                   "parallelism": "none (1 GPU)", "fused_step": args.fused_step,
+                   "act_split_above_512_rows": args.act_split if args.act_split is not None else 0},
     }
     if R > 1:
         # the same job on one replica: its 100.7 MB of weights then stay in the 256 MB MALL
@@ -546,14 +659,18 @@ def bench_block(args, wl):
 
         pre = clock_profile(binding, torch, stream, eager=pre_eager)
         dec = clock_profile(binding, torch, stream, capture=dec_capture, reps=4)
+        pre_ev = event_profile(binding, torch, stream, pre_eager)
+        dec_ev = event_profile(binding, torch, stream, dec_capture)
         rw = lambda n: T if n.endswith("gemm") or n in ("rmsnorm", "attn_prefill") else 1
-        res["kernels"] = {"prefill": kernel_table(pre, sh, rw, lambda n: T),
-                          "decode": kernel_table(dec, sh, lambda n: 1, lambda n: T + (n_prof + 1) / 2.0)}
-        res["kernel_timing"] = "device clock (s_memrealtime, 100 MHz): first-workgroup start to last-workgroup end"
-        if T >= 1024 and sh.wdtype == "bf16":
-            res["roofline"] = roofline_entry(res["kernels"]["prefill"], "gateup_gemm", "mfma")
-        else:
-            res["roofline"] = roofline_entry(res["kernels"]["decode"], "gateup_gemv", "hbm")
+        res["kernels"] = {"prefill": kernel_table(pre, sh, rw, lambda n: T, pre_ev),
+                          "decode": kernel_table(dec, sh, lambda n: 1, lambda n: T + (n_prof + 1) / 2.0, dec_ev)}
+        res["kernel_timing"] = ("avg_us: device clock (s_memrealtime, 100 MHz), first-workgroup start to "
+                                "last-workgroup end; event_avg_us: HIP event pair around each eager launch")
+        res["roofline"] = job_roofline([("prefill", res["kernels"]["prefill"], pre_ev, 1.0, rw),
+                                        ("decode", res["kernels"]["decode"], dec_ev, n_steps / n_prof,
+                                         lambda n: 1)])
+        # the prefill's own dominant kernel (the MFMA roof for long prefills)
+        res["prefill_roofline"] = job_roofline([("prefill", res["kernels"]["prefill"], pre_ev, 1.0, rw)])
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_block(wl, layers[0], x_host, rows_host)
     sess.close()
@@ -577,6 +694,7 @@ def cpu_baseline_block(wl, w, x_host, rows_host):
         O.block(rows_host[k:k + 1], [Ts + k], [0], ow, sh, cache, 0)
     t2 = time.perf_counter()
     return {"value": round((Ts + n) / (t2 - t0), 3), "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"fp64 oracle, one block: {Ts}-row prefill ({t1 - t0:.2f} s) + {n} decode steps "
                       f"({(t2 - t1) / n:.3f} s each)",
             "prefill_tok_s": round(Ts / (t1 - t0), 2), "decode_tok_s": round(n / (t2 - t1), 3)}
@@ -653,15 +771,118 @@ def bench_batched(args, wl):
             x.copy_(x0)
             pos.copy_(pos0)
         reps = 8
+
+        def eager_steps():
+            x.copy_(x0)
+            pos.copy_(pos0)
+            for _ in range(reps):
+                sess.step(x, pos, pos_bound=bound)
+                sess.head(x, ids, next_x=x, pos=pos)
+
         dec = clock_profile(binding, torch, stream, reps=reps, capture=lambda: (
             sess.step(x, pos, pos_bound=bound), sess.head(x, ids, next_x=x, pos=pos)))
-        table = kernel_table(dec, sh, lambda n: Bn, lambda n: float(lens.mean()) + (reps + 1) / 2.0)
+        ev = event_profile(binding, torch, stream, eager_steps)
+        table = kernel_table(dec, sh, lambda n: Bn, lambda n: float(lens.mean()) + (reps + 1) / 2.0, ev)
         res["kernels"] = {"decode": table}
-        res["kernel_timing"] = "device clock (s_memrealtime, 100 MHz): first-workgroup start to last-workgroup end"
-        res["roofline"] = roofline_entry(table, "gateup_gemm" if "gateup_gemm" in table else "gateup_gemv", "hbm",
-                                         rows=Bn)
+        res["kernel_timing"] = ("avg_us: device clock (s_memrealtime, 100 MHz), first-workgroup start to "
+                                "last-workgroup end; event_avg_us: HIP event pair around each eager launch")
+        res["roofline"] = job_roofline([("decode", table, ev, n_steps / reps, lambda n: Bn)])
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_batched(wl, layers, E, g, lens)
     sess.close()
     return res
+
+
+def cpu_baseline_batched(wl, layers, E, g, lens):
+    """The oracle on the host: one decode step of two of the batch's sequences (the
+    shortest and the longest context) through the 28 blocks + head, with their
+    caches filled as on the GPU; rows per second of that sample."""
+    import oracle as O
+    from speech_text_decoder_amd import synth
+
+    sh = wl.shape
+    sample = [int(np.argmin(lens)), int(np.argmax(lens))]
+    ol = [{k: synth.widen(v).astype(np.float64) for k, v in w.items()} for w in layers]
+    Ef = synth.widen(E).astype(np.float64)
+    gf = synth.widen(g)
+    cache = O.KVCache(sh.n_layers, len(sample), int(lens.max()) + 2, sh.n_kv_heads, sh.head_dim)
+    for l in range(sh.n_layers):
+        for i, b in enumerate(sample):
+            k, v = synth.kv_fill(wl.cfg_id, l, b, int(lens[b]), sh, wl.n_ctx)
+            cache.k[l, i, :lens[b]] = synth.kv_widen(synth.kv_stored(k, sh.kvdtype))
+            cache.v[l, i, :lens[b]] = synth.kv_widen(synth.kv_stored(v, sh.kvdtype))
+    x = synth.step_rows(wl.cfg_id, 0, wl.batch, sh.hidden)[sample].astype(np.float64)
+    t0 = time.perf_counter()
+    xo = O.step_stack(x, lens[sample], list(range(len(sample))), ol, sh, cache)
+    [O.greedy_token(r) for r in O.final_logits(xo, gf, Ef, sh.rms_eps)]
+    dt = time.perf_counter() - t0
+    return {"value": round(len(sample) / dt, 4), "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"fp64 oracle: one decode step of 2 of the {wl.batch} sequences (contexts "
+                      f"{int(lens[sample[0]])} and {int(lens[sample[1]])}) through 28 blocks + head in {dt:.2f} s"}
+
+
+def prefill_leg(args, name="qwen3_1p7b_block_long4096", replicas=8):
+    """The long-prefill figure carried on the default line: the causal prefill of one
+    1.7B-shaped block over 4096 rows, timed as `replicas` independent replicas chained
+    (weights and KV stream from HBM, not the 256 MB MALL), per block = total / replicas;
+    bf16 MFMA fraction of the whole prefill and the roofline of its dominant kernel."""
+    import torch
+    from speech_text_decoder_amd import binding, synth
+    from speech_text_decoder_amd.device import DecoderSession
+    from speech_text_decoder_amd.workloads import WORKLOADS
+
+    wl = WORKLOADS[name]
+    sh = wl.shape
+    T = wl.prefill_rows
+    layers = [synth.block_weights(wl.cfg_id, r, sh) for r in range(replicas)]
+    x_host = synth.prefill_rows(wl.cfg_id, T, sh.hidden)
+    sess = DecoderSession(sh, layers, n_ctx=wl.n_ctx, max_rows=T)
+    x0 = torch.from_numpy(x_host).cuda()
+    x = torch.empty_like(x0)
+    stream = torch.cuda.Stream()
+
+    def run():
+        x.copy_(x0)
+        sess.prefill(x)
+
+    def timed_ms():
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                run()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for i in range(args.steps):
+                x.copy_(x0)
+                evs[i][0].record(stream)
+                sess.prefill(x)
+                evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e[0].elapsed_time(e[1]) for e in evs])) / replicas
+
+    H, I, qd, kvd = sh.hidden, sh.ffn, sh.q_dim, sh.kv_dim
+    flops = 2.0 * T * H * (qd + 2 * kvd + I * 2) + 2.0 * T * (qd * H + I * H) + 4.0 * qd * T * (T + 1) / 2
+    sess.set_act_split(binding.SPLIT_ALL)
+    ms_split = timed_ms()
+    # the headline: one block with plain bf16 GEMM activations (within the parity
+    # bound for a single block; its 4096-row parity test runs the same mode)
+    sess.set_act_split(0)
+    ms = timed_ms()
+    out = {"workload": name, "rows": T, "replicas": replicas, "act_split": 0, "prefill_ms_per_block": round(ms, 5),
+           "prefill_tok_s_per_block": round(T / (ms * 1e-3), 1),
+           "prefill_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+           "prefill_mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "split_activations": {"act_split": binding.SPLIT_ALL, "prefill_ms_per_block": round(ms_split, 5),
+                                 "prefill_mfma_frac": round(flops / (ms_split * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}}
+    if not args.no_kernel_profile:
+        pre = clock_profile(binding, torch, stream, eager=run)
+        ev = event_profile(binding, torch, stream, run)
+        rw = lambda n: T if n.endswith("gemm") or n in ("rmsnorm", "attn_prefill") else 1
+        out["kernels"] = kernel_table(pre, sh, rw, lambda n: T, ev)
+        out["roofline"] = job_roofline([("prefill", out["kernels"], ev, 1.0, rw)])
+    sess.close()
+    return out
 
 
 def main():
@@ -694,6 +915,8 @@ def main():
     elif wl.greedy and wl.prefill_rows > 0:
         res = bench_greedy_stack(args, wl)
         unit = "tokens/s"
+        if args.workload == "qwen3_1p7b_stack28_greedy256" and not args.no_prefill_leg:
+            res["long_prefill"] = prefill_leg(args)
     elif wl.batch > 1:
         res = bench_batched(args, wl)
         unit = "tokens/s"

@@ -87,6 +87,7 @@ typedef struct sttd_workspace sttd_workspace; /* opaque */
 #define STTD_DEVERR_SLAB 2u     /* a slab id was < 0 or >= the cache's n_seq */
 #define STTD_DEVERR_TOKEN 4u    /* a token id was < 0 or >= vocab */
 #define STTD_DEVERR_SYNC 8u     /* a fused decode step's stage hand-off timed out (200 ms); its outputs are invalid */
+#define STTD_DEVERR_ROW 16u     /* a head row index was < 0 or >= n_x_rows */
 
 /* block_prefill flag: the FFN (and so the block output) is computed for the
  * last row only; rows 0..T-2 of x are left holding the attention residual
@@ -147,6 +148,27 @@ sttd_status sttd_workspace_free(sttd_workspace *ws);
  * order). Calls that share a workspace must not run concurrently: the
  * counters are per workspace. */
 #define STTD_OPT_FUSED_STEP 1
+/* STTD_OPT_ACT_SPLIT, default 15: precision of the activations that feed the
+ * bf16-weight MFMA projections. A split activation is carried as two bf16
+ * parts, hi = bf16(v) and lo = bf16(v - hi), so the product sees about 16
+ * significant bits of it at twice the MFMA work. Up to 512 rows per call all
+ * four are split whatever the value (those GEMMs are bound by weight bytes
+ * there, so the second MFMA pass is free). Above 512 rows an activation is
+ * split when its bit is set in `value` and rounded to plain bf16 otherwise:
+ * STTD_SPLIT_QKV (the attention RMSNorm output), STTD_SPLIT_O (the attention
+ * output), STTD_SPLIT_GATE_UP (the FFN RMSNorm output), STTD_SPLIT_DOWN (the
+ * SwiGLU output). Measured on the 28-block 1.7B-shaped stack (8 packed
+ * prompts of 153 rows, 1224 rows per call) against the fp64 oracle: with all
+ * four plain the final logits move by 11% of their RMS, beyond the 3e-2
+ * bound on hidden states; all four split, 1.2%; any one plain, 4% or more.
+ * One block stays within the bound with all four plain (its 4096-row parity
+ * test), so a caller running a single block or a shallow stack may set 0 to
+ * halve the MFMA work of long prefills. */
+#define STTD_OPT_ACT_SPLIT 2
+#define STTD_SPLIT_QKV 1
+#define STTD_SPLIT_O 2
+#define STTD_SPLIT_GATE_UP 4
+#define STTD_SPLIT_DOWN 8
 /* Sets `option` to `value`. Unknown option or value: STTD_ERR_INVALID_ARG. */
 sttd_status sttd_workspace_set_option(sttd_workspace *ws, int option, int value);
 
@@ -225,15 +247,25 @@ sttd_status sttd_block_step(const sttd_block_params *p, const sttd_block_weights
 /* Final RMSNorm, tied lm_head and greedy argmax over B rows (the tail of
  * build_step_graph; the host argmax in run() on the Qwen3-ASR model page
  * keeps the lowest index on ties, and so does this call; a NaN logit never
- * wins). x rows are read at x + b * x_row_stride (floats), so the last
- * prefill row can be passed directly. final_norm [hidden], embed
- * [vocab, hidden] (storage wtype). Outputs: ids [B] int32; optional logits
+ * wins: it ranks below every number, -inf included, so a row of NaN logits
+ * gives id 0). final_norm [hidden], embed [vocab, hidden] (storage wtype).
+ * Input rows: with x_rows NULL, row b is read at x + b * x_row_stride
+ * (floats), so the last prefill row can be passed directly. With x_rows
+ * (device int32 [B]), row b is read at x + x_rows[b] * x_row_stride: the
+ * per-sequence last-row gather of the batched prefill graph
+ * (build_prefill_graph_batched on the Qwen3-ASR decoder page gathers each
+ * utterance's last position before the final norm and head; run_batch on the
+ * model page fills those positions), so ragged packed prompts take one head
+ * call. n_x_rows (host) is the number of rows x holds and must be >= 1 then;
+ * an index outside [0, n_x_rows) reads row 0 and records STTD_DEVERR_ROW (that
+ * row's outputs are then meaningless). Outputs: ids [B] int32; optional logits
  * [B, vocab] fp32 (NULL: not written); optional next_x [B, hidden] fp32 =
  * embed[ids[b]] (the next step's input rows); optional pos [B] int32
  * incremented by one after the step (device-resident step counter). */
 sttd_status sttd_lm_head_argmax(const void *final_norm, const void *embed, sttd_dtype wtype, int vocab, int hidden,
                                 float rms_eps, sttd_workspace *ws, int B, const float *x, int64_t x_row_stride,
-                                int32_t *ids, float *logits, float *next_x, int32_t *pos, void *stream);
+                                const int32_t *x_rows, int n_x_rows, int32_t *ids, float *logits, float *next_x,
+                                int32_t *pos, void *stream);
 
 /* Greedy stopping rules on the device, per row (the step loop of run() on
  * the Qwen3-ASR model page, and per row in its batched step loop): a row goes

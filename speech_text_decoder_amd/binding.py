@@ -15,8 +15,10 @@ LIB_PATH = os.path.join(_HERE, "libsttd.so")
 OK, ERR_INVALID_ARG, ERR_OOM, ERR_BACKEND, ERR_CONTEXT_FULL, ERR_UNSUPPORTED = range(6)
 F32, BF16, F16 = 0, 1, 2
 LAST_ROW_FFN_ONLY = 1
-DEVERR_POSITION, DEVERR_SLAB, DEVERR_TOKEN, DEVERR_SYNC = 1, 2, 4, 8
-OPT_FUSED_STEP = 1
+DEVERR_POSITION, DEVERR_SLAB, DEVERR_TOKEN, DEVERR_SYNC, DEVERR_ROW = 1, 2, 4, 8, 16
+OPT_FUSED_STEP, OPT_ACT_SPLIT = 1, 2
+SPLIT_QKV, SPLIT_O, SPLIT_GATE_UP, SPLIT_DOWN = 1, 2, 4, 8
+SPLIT_ALL = 15
 
 EXPORTS = [
     "sttd_status_string", "sttd_kv_context_for", "sttd_kv_cache_alloc", "sttd_kv_cache_free", "sttd_kv_cache_clear", "sttd_kv_cache_view",
@@ -82,7 +84,7 @@ def lib():
             "sttd_block_prefill_batched": [P(BlockParams), P(BlockWeights), vp, vp, i32, i32, P(i32), P(i32), P(i32),
                                            vp, vp],
             "sttd_block_step": [P(BlockParams), P(BlockWeights), vp, vp, i32, i32, vp, vp, i32, vp, vp],
-            "sttd_lm_head_argmax": [vp, vp, i32, i32, i32, f32, vp, i32, vp, i64, vp, vp, vp, vp, vp],
+            "sttd_lm_head_argmax": [vp, vp, i32, i32, i32, f32, vp, i32, vp, i64, vp, i32, vp, vp, vp, vp, vp],
             "sttd_greedy_stop": [P(StopRules), i32, vp, i32, vp, vp, vp, vp, vp, vp, vp],
             "sttd_profile_enable": [ctypes.c_uint32],
             "sttd_profile_read": [i32, P(i64), P(ctypes.c_double)],
@@ -238,6 +240,8 @@ def clock_spans(max_slots):
 
 
 def lm_head_argmax(final_norm, embed, wtype, vocab, hidden, rms_eps, ws, B, x, x_row_stride, ids, logits=0,
-                   next_x=0, pos=0, stream=0):
-    _check(lib().sttd_lm_head_argmax(final_norm, embed, wtype, vocab, hidden, rms_eps, ws, B, x, x_row_stride, ids,
-                                     logits, next_x, pos, stream), "sttd_lm_head_argmax")
+                   next_x=0, pos=0, stream=0, x_rows=0, n_x_rows=0):
+    """x_rows: device int32 [B] row indices into x (0: row b at x + b * x_row_stride)."""
+    _check(lib().sttd_lm_head_argmax(final_norm, embed, wtype, vocab, hidden, rms_eps, ws, B, x, x_row_stride,
+                                     x_rows, n_x_rows, ids, logits, next_x, pos, stream), "sttd_lm_head_argmax")
+

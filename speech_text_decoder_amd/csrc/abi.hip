@@ -46,6 +46,7 @@ struct sttd_workspace {
     uint32_t* sync;                // [kStepSyncWords] hand-off counters of the fused step (zero between launches)
     uint32_t* merge_ctr;           // [max_rows][n_kv] attention split counts (zero between launches)
     bool fused_step;               // STTD_OPT_FUSED_STEP
+    uint32_t split_mask;           // STTD_OPT_ACT_SPLIT: GEMM inputs kept as bf16 high + low parts at any row count
 };
 
 namespace {
@@ -223,12 +224,20 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
     bool flash = mfma && prefill && kl.type == KV_F16;
     if (flash && segs)  // every packed sequence must be long enough for the flash tiles' query layout
         for (int i = 0; i < segs->n; ++i) flash = flash && segs->len[i] > kGemvMaxRows;
-    const bool split = R <= kSplitMaxRows;
-    uint16_t* xn_lo = split ? ws->xn + (size_t)ws->max_rows * H : nullptr;
+    // which GEMM inputs are split into bf16 high + low parts: all of them up to
+    // kSplitMaxRows rows (HBM-bound there, so the doubled MFMA work is free), and
+    // beyond that the ones the workspace's STTD_OPT_ACT_SPLIT mask names (all four
+    // by default: on the 28-block stack plain bf16 ones drift the logits past the
+    // parity bound)
+    const bool split_all = R <= kSplitMaxRows;
+    const uint32_t sm = ws->split_mask;
+    uint16_t* xn_lo_base = ws->xn + (size_t)ws->max_rows * H;
+    uint16_t* xn_lo = split_all || (sm & STTD_SPLIT_QKV) ? xn_lo_base : nullptr;
+    uint16_t* ffn_lo = split_all || (sm & STTD_SPLIT_GATE_UP) ? xn_lo_base : nullptr;
     uint16_t* ao = (uint16_t*)ws->attn_o;
-    uint16_t* ao_lo = split ? ao + (size_t)ws->max_rows * qd : nullptr;
+    uint16_t* ao_lo = split_all || (sm & STTD_SPLIT_O) ? ao + (size_t)ws->max_rows * qd : nullptr;
     uint16_t* act = (uint16_t*)ws->act;
-    uint16_t* act_lo = split ? act + (size_t)ws->max_rows * I : nullptr;
+    uint16_t* act_lo = split_all || (sm & STTD_SPLIT_DOWN) ? act + (size_t)ws->max_rows * I : nullptr;
 
     // --- a single decode row: the whole block as one persistent launch
     if (!prefill && R == 1 && ws->fused_step) {
@@ -350,10 +359,10 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
     if (mfma && nr > kGemvMaxRows) {
         {
             ProfScope ps(STTD_KERN_RMSNORM, s);
-            TRY(launch_rmsnorm_rows_bf16(xf, H, w->ffn_norm, wt, ws->xn, xn_lo, H, nr, H, eps, s));
+            TRY(launch_rmsnorm_rows_bf16(xf, H, w->ffn_norm, wt, ws->xn, ffn_lo, H, nr, H, eps, s));
         }
         GemmArgs g{};
-        g.A = ws->xn; g.A_lo = xn_lo; g.lda = H; g.M = nr; g.K = H;
+        g.A = ws->xn; g.A_lo = ffn_lo; g.lda = H; g.M = nr; g.K = H;
         g.w[0] = (const uint16_t*)w->w_gate_up; g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = 2 * I;
         g.N = I; g.Cb = act; g.Cb_lo = act_lo; g.ldcb = I;
         {
@@ -536,6 +545,7 @@ sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int m
     ws->rowseq = (int32_t*)(b + o_rowseq);
     ws->merge_ctr = (uint32_t*)(b + o_merge);
     ws->fused_step = false;
+    ws->split_mask = STTD_SPLIT_QKV | STTD_SPLIT_O | STTD_SPLIT_GATE_UP | STTD_SPLIT_DOWN;
     // RoPE table in fp64 on the host: pair i of position pos turns by pos * theta^(-2i/d)
     std::vector<float> table((size_t)max_pos * d);
     const int half = d / 2;
@@ -571,6 +581,10 @@ sttd_status sttd_workspace_set_option(sttd_workspace* ws, int option, int value)
     if (!ws) return STTD_ERR_INVALID_ARG;
     if (option == STTD_OPT_FUSED_STEP && (value == 0 || value == 1)) {
         ws->fused_step = value == 1;
+        return STTD_OK;
+    }
+    if (option == STTD_OPT_ACT_SPLIT && value >= 0 && value <= 15) {
+        ws->split_mask = (uint32_t)value;
         return STTD_OK;
     }
     return STTD_ERR_INVALID_ARG;
@@ -675,14 +689,17 @@ sttd_status sttd_block_step(const sttd_block_params* p, const sttd_block_weights
 
 sttd_status sttd_lm_head_argmax(const void* final_norm, const void* embed, sttd_dtype wtype, int vocab, int hidden,
                                 float rms_eps, sttd_workspace* ws, int B, const float* x, int64_t x_row_stride,
-                                int32_t* ids, float* logits, float* next_x, int32_t* pos, void* stream) {
+                                const int32_t* x_rows, int n_x_rows, int32_t* ids, float* logits, float* next_x,
+                                int32_t* pos, void* stream) {
     if (!final_norm || !embed || !ws || !x || !ids || vocab <= 0 || hidden <= 0 || B <= 0) return STTD_ERR_INVALID_ARG;
     if (wtype != STTD_BF16 && wtype != STTD_F32) return STTD_ERR_UNSUPPORTED;
     if (hidden % 64 || hidden > 8192) return STTD_ERR_UNSUPPORTED;
     if (B > ws->max_rows || vocab > ws->vocab || x_row_stride < hidden) return STTD_ERR_INVALID_ARG;
+    if (x_rows && n_x_rows < 1) return STTD_ERR_INVALID_ARG;
     HeadArgs a{};
     a.gain = final_norm; a.embed = embed; a.vocab = vocab; a.hidden = hidden; a.eps = rms_eps;
     a.x = x; a.ldx = x_row_stride; a.rows = B; a.ids = ids; a.logits = logits; a.next_x = next_x; a.pos = pos;
+    a.xrow = x_rows; a.n_xrows = n_x_rows;
     a.partials = ws->partials; a.max_partials = kHeadPartials; a.err = ws->err;
     a.zbuf = hidden <= ws->p.hidden ? ws->xn : nullptr;  // 2 * B * hidden bf16 fit in the normed-row planes
     ProfScope ps(STTD_KERN_LM_HEAD, (hipStream_t)stream);

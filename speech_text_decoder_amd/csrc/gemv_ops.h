@@ -108,12 +108,14 @@ __device__ __forceinline__ float wave_reduce_multi(float (&v)[V]) {
     return v[0];
 }
 
-// This wave's activation chunks: xv[c][b][i] = x[b][k_c + i] (* gain when NORM),
-// zero where k_c + i >= K or b >= nb; ss[b] += sum of x^2 over those elements.
+// This wave's activation chunks from per-row pointers: xv[c][b][i] = xr[b][k_c + i]
+// (* gain when NORM), zero where k_c + i >= K or b >= nb; ss[b] += sum of x^2
+// over those elements. xr[b] must be readable for every b (rows past nb repeat a
+// valid one).
 template <class WT, int KCH, int BT, bool NORM, class MEM = PlainMem>
-__device__ __forceinline__ void load_activations(const float* __restrict__ x, int64_t ldx, int nb, int K,
-                                                 const typename WT::T* __restrict__ gain, const int (&kk)[KCH],
-                                                 float (&xv)[KCH][BT][8], float (&ss)[BT]) {
+__device__ __forceinline__ void load_activation_rows(const float* const (&xr)[BT], int nb, int K,
+                                                     const typename WT::T* __restrict__ gain, const int (&kk)[KCH],
+                                                     float (&xv)[KCH][BT][8], float (&ss)[BT]) {
 #pragma unroll
     for (int b = 0; b < BT; ++b) ss[b] = 0.f;
 #pragma unroll
@@ -125,7 +127,7 @@ __device__ __forceinline__ void load_activations(const float* __restrict__ x, in
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
             float v[8];
-            MEM::ld8(x + (int64_t)(b < nb ? b : 0) * ldx + k, v);
+            MEM::ld8(xr[b] + k, v);
             const bool use = in && b < nb;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -135,6 +137,17 @@ __device__ __forceinline__ void load_activations(const float* __restrict__ x, in
             }
         }
     }
+}
+
+// The same for rows x + b * ldx, b < nb.
+template <class WT, int KCH, int BT, bool NORM, class MEM = PlainMem>
+__device__ __forceinline__ void load_activations(const float* __restrict__ x, int64_t ldx, int nb, int K,
+                                                 const typename WT::T* __restrict__ gain, const int (&kk)[KCH],
+                                                 float (&xv)[KCH][BT][8], float (&ss)[BT]) {
+    const float* xr[BT];
+#pragma unroll
+    for (int b = 0; b < BT; ++b) xr[b] = x + (int64_t)(b < nb ? b : 0) * ldx;
+    load_activation_rows<WT, KCH, BT, NORM, MEM>(xr, nb, K, gain, kk, xv, ss);
 }
 
 // Activation chunks merged from attention split partials (see GemvArgs::xpart):

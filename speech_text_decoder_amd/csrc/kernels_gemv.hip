@@ -178,7 +178,20 @@ __global__ __launch_bounds__(256) void lm_head_kernel(HeadArgs a) {
     const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE, t = threadIdx.x;
     const int b0 = blockIdx.y * BT;
     const int nb = min(BT, a.rows - b0);
-    const float* x = a.x + (int64_t)b0 * a.ldx;
+    // activation row of each of this workgroup's rows (the caller's row index, if any)
+    const float* xr[BT];
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+        int src = b0 + (b < nb ? b : 0);
+        if (a.xrow) {
+            src = a.xrow[src];
+            if (src < 0 || src >= a.n_xrows) {
+                if (b < nb && blockIdx.x == 0 && t == 0) record_error(a.err, kDevErrRow);
+                src = 0;
+            }
+        }
+        xr[b] = a.x + (int64_t)src * a.ldx;
+    }
     const T* E = (const T*)a.embed;
     const int n_blocks = (a.vocab + NR - 1) / NR;
 
@@ -197,7 +210,7 @@ __global__ __launch_bounds__(256) void lm_head_kernel(HeadArgs a) {
     int blk = blockIdx.x;
     if (blk < n_blocks) fetch(blk, wc);
     float xv[KCH][BT][8], ss[BT];
-    load_activations<WT, KCH, BT, true>(x, a.ldx, nb, a.hidden, (const T*)a.gain, kk, xv, ss);
+    load_activation_rows<WT, KCH, BT, true>(xr, nb, a.hidden, (const T*)a.gain, kk, xv, ss);
     float rs[BT];
     {
         // row scales once per workgroup
@@ -411,7 +424,8 @@ __global__ __launch_bounds__(256) void head_mfma_kernel(HeadArgs a, const uint16
 static hipError_t launch_head_mfma(const HeadArgs& a, hipStream_t s) {
     uint16_t* zh = a.zbuf;
     uint16_t* zl = a.zbuf + (size_t)a.rows * a.hidden;
-    hipError_t e = launch_rmsnorm_rows_bf16(a.x, a.ldx, a.gain, W_BF16, zh, zl, a.hidden, a.rows, a.hidden, a.eps, s);
+    hipError_t e = launch_rmsnorm_rows_bf16(a.x, a.ldx, a.gain, W_BF16, zh, zl, a.hidden, a.rows, a.hidden, a.eps, s,
+                                            a.xrow, a.n_xrows, a.err);
     if (e != hipSuccess) return e;
     const int n_tiles = (a.vocab + 31) / 32;
     const int grid = n_tiles < a.max_partials ? n_tiles : a.max_partials;

@@ -15,10 +15,19 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_bf16_kernel(const float* __r
                                                                 const typename GT::T* __restrict__ g,
                                                                 uint16_t* __restrict__ out,
                                                                 uint16_t* __restrict__ out_lo, int64_t ldo, int H,
-                                                                float eps, uint64_t* clk) {
+                                                                float eps, const int32_t* __restrict__ xrow,
+                                                                int n_xrows, uint32_t* err, uint64_t* clk) {
     __shared__ float red[4];
     clock_begin(clk);
-    const float* xr = x + (int64_t)blockIdx.x * ldx;
+    int src = blockIdx.x;
+    if (xrow) {
+        src = xrow[blockIdx.x];
+        if (src < 0 || src >= n_xrows) {
+            if (threadIdx.x == 0) record_error(err, kDevErrRow);
+            src = 0;
+        }
+    }
+    const float* xr = x + (int64_t)src * ldx;
     uint16_t* o = out + (int64_t)blockIdx.x * ldo;
     float ss = 0.f;
     for (int i = threadIdx.x * 4; i < H; i += 1024) {
@@ -50,12 +59,15 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_bf16_kernel(const float* __r
 }
 
 hipError_t launch_rmsnorm_rows_bf16(const float* x, int64_t ldx, const void* gain, WType gt, uint16_t* out,
-                                    uint16_t* out_lo, int64_t ldo, int R, int H, float eps, hipStream_t s) {
+                                    uint16_t* out_lo, int64_t ldo, int R, int H, float eps, hipStream_t s,
+                                    const int32_t* xrow, int n_xrows, uint32_t* err) {
     if (R <= 0) return hipSuccess;
     if (gt == W_BF16)
-        rmsnorm_rows_bf16_kernel<BF16><<<R, 256, 0, s>>>(x, ldx, (const uint16_t*)gain, out, out_lo, ldo, H, eps, clock_slot());
+        rmsnorm_rows_bf16_kernel<BF16><<<R, 256, 0, s>>>(x, ldx, (const uint16_t*)gain, out, out_lo, ldo, H, eps,
+                                                         xrow, n_xrows, err, clock_slot());
     else
-        rmsnorm_rows_bf16_kernel<F32><<<R, 256, 0, s>>>(x, ldx, (const float*)gain, out, out_lo, ldo, H, eps, clock_slot());
+        rmsnorm_rows_bf16_kernel<F32><<<R, 256, 0, s>>>(x, ldx, (const float*)gain, out, out_lo, ldo, H, eps, xrow,
+                                                        n_xrows, err, clock_slot());
     return hipGetLastError();
 }
 

@@ -75,8 +75,12 @@ struct QkRope {
 // ---- norms, rotary, gathers (kernels_misc.hip)
 // out[r, :] = x[r, :] / sqrt(mean(x[r]^2) + eps) * gain, rows r < R; out bf16.
 // With out_lo, the value is also split: out = bf16(v), out_lo = bf16(v - out).
+// With xrow, output row r normalises input row xrow[r] (an index outside
+// [0, n_xrows) reads row 0 and records kDevErrRow in err).
+constexpr uint32_t kDevErrRow = 16u;  // STTD_DEVERR_ROW
 hipError_t launch_rmsnorm_rows_bf16(const float* x, int64_t ldx, const void* gain, WType gt, uint16_t* out,
-                                    uint16_t* out_lo, int64_t ldo, int R, int H, float eps, hipStream_t s);
+                                    uint16_t* out_lo, int64_t ldo, int R, int H, float eps, hipStream_t s,
+                                    const int32_t* xrow = nullptr, int n_xrows = 0, uint32_t* err = nullptr);
 // Per-head Q/K RMSNorm + NeoX RoPE (table) + K/V cache write; q written to q_out
 // as fp32 (q_f16 false) or f16 (q_f16 true) with row stride ldq.
 hipError_t launch_qk_norm_rope_kv(const float* qkv, int64_t ldqkv, int R, WType gt, const QkRope& q, hipStream_t s);
@@ -125,6 +129,8 @@ struct HeadArgs {
     const float* x;
     int64_t ldx;
     int rows;
+    const int32_t* xrow; // optional [rows]: row b reads x + xrow[b] * ldx (else x + b * ldx)
+    int n_xrows;         // with xrow: rows x holds; an index outside [0, n_xrows) reads row 0 and flags kDevErrRow
     int32_t* ids;
     float* logits;       // optional [rows, vocab]
     float* next_x;       // optional [rows, hidden]

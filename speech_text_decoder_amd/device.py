@@ -89,14 +89,20 @@ class DecoderSession:
                          0 if seq is None else seq.data_ptr(), pos.data_ptr(), pb, x.data_ptr(), s)
         return x
 
-    def head(self, x, ids, logits=None, next_x=None, pos=None, row_stride=None, rows=None, stream=None):
+    def head(self, x, ids, logits=None, next_x=None, pos=None, row_stride=None, rows=None, x_rows=None, stream=None):
+        """x_rows: optional cuda int32 [B] row indices into x (e.g. each packed prompt's last row)."""
         s = stream_handle(stream)
-        Bn = x.shape[0] if rows is None else rows
+        if x_rows is not None:
+            Bn = x_rows.shape[0]
+        else:
+            Bn = x.shape[0] if rows is None else rows
         B.lm_head_argmax(self.final_norm.data_ptr(), self.embed.data_ptr(), WT_CODE[self.shape.wdtype], self.vocab,
                          self.shape.hidden, self.shape.rms_eps, self.ws, Bn, x.data_ptr(),
                          self.shape.hidden if row_stride is None else row_stride, ids.data_ptr(),
                          0 if logits is None else logits.data_ptr(), 0 if next_x is None else next_x.data_ptr(),
-                         0 if pos is None else pos.data_ptr(), s)
+                         0 if pos is None else pos.data_ptr(), s,
+                         x_rows=0 if x_rows is None else x_rows.data_ptr(),
+                         n_x_rows=0 if x_rows is None else x.shape[0])
 
     def gather(self, ids, x, stream=None):
         B.embed_gather(self.embed.data_ptr(), WT_CODE[self.shape.wdtype], self.vocab, self.shape.hidden,
@@ -115,6 +121,10 @@ class DecoderSession:
     def set_fused_step(self, enabled: bool):
         """STTD_OPT_FUSED_STEP: single-row steps as one persistent launch per block (default off)."""
         B.workspace_set_option(self.ws, B.OPT_FUSED_STEP, 1 if enabled else 0)
+
+    def set_act_split(self, mask: int):
+        """STTD_OPT_ACT_SPLIT: GEMM inputs (B.SPLIT_* bits) kept as bf16 high + low parts above 512 rows."""
+        B.workspace_set_option(self.ws, B.OPT_ACT_SPLIT, int(mask))
 
     def error_bits(self):
         return B.workspace_error(self.ws)

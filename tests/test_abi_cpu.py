@@ -42,8 +42,8 @@ def test_null_and_bad_arguments_rejected_on_host():
         == B.ERR_INVALID_ARG
     assert L.sttd_block_step(ctypes.byref(p), ctypes.byref(w), None, None, 0, 1, None, None, 1, None, None) \
         == B.ERR_INVALID_ARG
-    assert L.sttd_lm_head_argmax(None, None, B.BF16, 10, 256, 1e-6, None, 1, None, 256, None, None, None, None,
-                                 None) == B.ERR_INVALID_ARG
+    assert L.sttd_lm_head_argmax(None, None, B.BF16, 10, 256, 1e-6, None, 1, None, 256, None, 0, None, None, None,
+                                 None, None) == B.ERR_INVALID_ARG
     assert L.sttd_embed_gather(None, B.BF16, 10, 256, 1, None, None, None, None) == B.ERR_INVALID_ARG
     assert L.sttd_kv_cache_free(None) == B.ERR_INVALID_ARG
     assert L.sttd_workspace_free(None) == B.ERR_INVALID_ARG

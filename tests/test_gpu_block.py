@@ -38,13 +38,16 @@ def gpu_kv_rows(sess, layer, seq, positions):
     return k, v
 
 
-def run_block_case(shape, cfg_id, T, steps, n_ctx, chunks=None, seed_layer=0):
-    """Prefill T rows (optionally in chunks) then `steps` single-row decode steps; compare every output."""
+def run_block_case(shape, cfg_id, T, steps, n_ctx, chunks=None, seed_layer=0, act_split=None):
+    """Prefill T rows (optionally in chunks) then `steps` single-row decode steps; compare every output.
+    act_split: STTD_OPT_ACT_SPLIT mask for calls above 512 rows (None: the library default, all split)."""
     fp32 = shape.wdtype == "f32"
     w = synth.block_weights(cfg_id, seed_layer, shape)
     ow = widen_layer(w)
     x = synth.prefill_rows(cfg_id, T, shape.hidden)
     sess = DecoderSession(shape, [w], n_ctx=n_ctx, max_rows=max(T, 1))
+    if act_split is not None:
+        sess.set_act_split(act_split)
     cache = O.KVCache(1, 1, n_ctx, shape.n_kv_heads, shape.head_dim)
     want = O.block(x, np.arange(T), np.zeros(T, int), ow, shape, cache, 0)
     xd = dev(x)
@@ -92,27 +95,33 @@ def test_small_bf16_head128_group8(T):
     log(f"SMALL128 T={T}: {max(errs):.2e}")
 
 
-def test_many_rows_large_tiles_with_row_and_column_tails():
-    """1100 rows take the 256 x 256 MFMA tiles: 4 full row tiles and a ragged one; the
-    hidden size 320 leaves a partial column tile in the O and down projections."""
+@pytest.mark.parametrize("act_split", [0, B.SPLIT_ALL, B.SPLIT_O | B.SPLIT_DOWN])
+def test_many_rows_large_tiles_with_row_and_column_tails(act_split):
+    """1100 rows: with plain bf16 activations the 256 x 256 MFMA tiles (4 full row tiles
+    and a ragged one; the hidden size 320 leaves a partial column tile in the O and down
+    projections); with split ones (the default) the 64 x 128 tiles on hi/lo planes; and
+    a mixed mask."""
     sh = DecoderShape(hidden=320, n_heads=4, n_kv_heads=2, head_dim=64, ffn=768)
-    errs = run_block_case(sh, 15, 1100, 1, 1200)
-    log(f"T=1100 H=320: {max(errs):.2e}")
+    errs = run_block_case(sh, 15, 1100, 1, 1200, act_split=act_split)
+    log(f"T=1100 H=320 split {act_split}: {max(errs):.2e}")
 
 
 @pytest.mark.parametrize("T", [513, 700])
-def test_mid_size_prefill_plain_bf16_rows_with_split_k(T):
-    """513-1023 rows: the 64x128-tile GEMMs without the split activations, with K split
+@pytest.mark.parametrize("act_split", [0, B.SPLIT_ALL])
+def test_mid_size_prefill_rows_with_split_k(T, act_split):
+    """513-1023 rows: the 64x128-tile GEMMs with plain or split activations, with K split
     over workgroups (atomic adds) where few of them run."""
-    errs = run_block_case(SMALL128, 18, T, 1, 768)
-    log(f"SMALL128 T={T}: {max(errs):.2e}")
+    errs = run_block_case(SMALL128, 18, T, 1, 768, act_split=act_split)
+    log(f"SMALL128 T={T} split {act_split}: {max(errs):.2e}")
 
 
-def test_chunked_prefill_with_a_large_tile_chunk():
-    """A 1030-row chunk (256x256 MFMA tiles, flash attention at pos0 = 70) after a 70-row one."""
+@pytest.mark.parametrize("act_split", [0, B.SPLIT_ALL])
+def test_chunked_prefill_with_a_large_tile_chunk(act_split):
+    """A 1030-row chunk (256x256 MFMA tiles with plain activations, flash attention at
+    pos0 = 70) after a 70-row one."""
     sh = DecoderShape(hidden=320, n_heads=4, n_kv_heads=2, head_dim=64, ffn=768)
-    errs = run_block_case(sh, 19, 1100, 1, 1200, chunks=[70, 1030])
-    log(f"chunks [70, 1030] H=320: {max(errs):.2e}")
+    errs = run_block_case(sh, 19, 1100, 1, 1200, chunks=[70, 1030], act_split=act_split)
+    log(f"chunks [70, 1030] H=320 split {act_split}: {max(errs):.2e}")
 
 
 def test_small_fp32_kv_cache_bf16_weights():
@@ -164,8 +173,11 @@ def test_qwen3_1p7b_block_t153_prefill_then_64_steps():
 
 
 @pytest.mark.parametrize("n_rows", [3, 21])
-def test_lm_head_argmax_planted_ties_and_feedback(n_rows):
-    """3 rows take the GEMV head; 21 rows the MFMA head (norm planes, a 16-row and a 5-row chunk)."""
+def test_lm_head_argmax_planted_ties_nan_and_feedback(n_rows):
+    """3 rows take the GEMV head; 21 rows the MFMA head (norm planes, a 16-row and a 5-row chunk).
+    Planted: a tie (lowest index wins), a maximum at the last vocabulary row, a NaN
+    embedding row (a NaN logit in every row, never chosen), and a row of x holding a
+    NaN (every logit NaN: id 0, as the oracle's scan with NaN read as -inf)."""
     sh = replace(SMALL64, vocab=5000)
     rng = np.random.default_rng(3)
     E = synth.to_bf16_bits(rng.standard_normal((sh.vocab, sh.hidden)).astype(np.float32) * 0.02)
@@ -178,6 +190,12 @@ def test_lm_head_argmax_planted_ties_and_feedback(n_rows):
     # row 1: a single planted maximum at the last vocabulary row
     z1 = x[1] / np.sqrt(np.mean(x[1] ** 2) + 1e-6)
     E[4999] = synth.to_bf16_bits(z1 * 0.5)
+    # every row: vocabulary row 2500 is NaN, so is its logit
+    nan_col = 2500
+    E[nan_col] = 0x7FC0
+    E[nan_col, 1:] = 0
+    # the last row: a NaN activation makes every logit of that row NaN
+    x[n_rows - 1, 7] = np.nan
     sess = DecoderSession(sh, [synth.block_weights(16, 0, sh)], embed=E, final_norm=g, n_ctx=16, max_rows=n_rows)
     xd = dev(x)
     ids = torch.zeros(n_rows, dtype=torch.int32, device="cuda")
@@ -185,18 +203,67 @@ def test_lm_head_argmax_planted_ties_and_feedback(n_rows):
     nx = torch.zeros(n_rows, sh.hidden, dtype=torch.float32, device="cuda")
     pos0 = np.arange(5, 5 + n_rows, dtype=np.int32)
     pos = dev(pos0)
-    want_logits = O.final_logits(x, synth.widen(g), synth.widen(E), sh.rms_eps)
+    with np.errstate(invalid="ignore"):
+        want_logits = O.final_logits(x, synth.widen(g), synth.widen(E), sh.rms_eps)
+    finite_rows = n_rows - 1
+    keep_cols = np.arange(sh.vocab) != nan_col
     for rep in range(3):        # slots and counters must re-arm themselves between calls
         sess.head(xd, ids, logits=logits, next_x=nx, pos=pos)
         torch.cuda.synchronize()
         got = ids.cpu().numpy()
-        check(logits.cpu().numpy(), want_logits, False, "logits")
+        gl = logits.cpu().numpy()
+        check(gl[:finite_rows][:, keep_cols], want_logits[:finite_rows][:, keep_cols], False, "logits")
+        assert np.all(np.isnan(gl[:, nan_col])) and np.all(np.isnan(gl[n_rows - 1]))
         assert got[0] == 17, got
         assert got[1] == 4999, got
-        for b in range(2, n_rows):
-            assert got[b] == O.greedy_token(want_logits[b]) or O.top2_margin(want_logits[b]) <= MARGIN, b
+        assert got[n_rows - 1] == 0 == O.greedy_token(want_logits[n_rows - 1]), got
+        assert nan_col not in got.tolist()
+        for b in range(2, finite_rows):
+            if O.top2_margin(want_logits[b]) > MARGIN:
+                assert got[b] == O.greedy_token(want_logits[b]), b
+            else:   # near-tie: the GPU's pick is one of the near-maximal logits
+                assert want_logits[b][got[b]] >= np.nanmax(want_logits[b]) - MARGIN, b
         np.testing.assert_array_equal(nx.cpu().numpy(), synth.widen(E)[got])
         assert pos.cpu().numpy().tolist() == (pos0 + 1 + rep).tolist()
+    sess.close()
+
+
+@pytest.mark.parametrize("n_rows", [3, 13])
+def test_lm_head_device_row_index(n_rows):
+    """Head rows picked by a device index array (the per-sequence last-row gather
+    of a packed prefill): equal to passing the gathered rows, for the GEMV (3) and
+    the MFMA (13) head; an index outside the rows reads row 0 and is flagged."""
+    sh = replace(SMALL64, vocab=3000)
+    rng = np.random.default_rng(5)
+    E = synth.to_bf16_bits(rng.standard_normal((sh.vocab, sh.hidden)).astype(np.float32) * 0.02)
+    g = synth.to_bf16_bits(1 + 0.02 * rng.standard_normal(sh.hidden).astype(np.float32))
+    n_x = 40
+    x = rng.standard_normal((n_x, sh.hidden)).astype(np.float32)
+    rows = rng.choice(n_x, n_rows, replace=False).astype(np.int32)
+    sess = DecoderSession(sh, [synth.block_weights(21, 0, sh)], embed=E, final_norm=g, n_ctx=16, max_rows=n_x)
+    xd = dev(x)
+    ids = torch.zeros(n_rows, dtype=torch.int32, device="cuda")
+    logits = torch.zeros(n_rows, sh.vocab, device="cuda")
+    sess.head(xd, ids, logits=logits, x_rows=dev(rows))
+    ids2 = torch.zeros(n_rows, dtype=torch.int32, device="cuda")
+    logits2 = torch.zeros(n_rows, sh.vocab, device="cuda")
+    sess.head(dev(x[rows]), ids2, logits=logits2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids2.cpu().numpy())
+    np.testing.assert_array_equal(logits.cpu().numpy(), logits2.cpu().numpy())
+    want = O.final_logits(x[rows], synth.widen(g), synth.widen(E), sh.rms_eps)
+    check(logits.cpu().numpy(), want, False, "indexed-row logits")
+    assert sess.error_bits() == 0
+    bad = rows.copy()
+    bad[1] = n_x
+    sess.head(xd, ids, logits=logits, x_rows=dev(bad))
+    torch.cuda.synchronize()
+    assert sess.error_bits() == B.DEVERR_ROW
+    clamped = rows.copy()
+    clamped[1] = 0                    # what the flagged row reads instead
+    sess.head(dev(x[clamped]), ids2, logits=logits2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(logits.cpu().numpy(), logits2.cpu().numpy())
     sess.close()
 
 

@@ -161,7 +161,10 @@ def test_batched_decode_b16_sampled_rows():
     sess.close()
 
 
-def test_long4096_block_sampled_prefill_rows_and_16_steps():
+@pytest.mark.parametrize("act_split", [0, 15])
+def test_long4096_block_sampled_prefill_rows_and_16_steps(act_split):
+    """act_split 0: plain bf16 activations (the single-block long-prefill figure);
+    15: every activation split (the library default)."""
     wl = WORKLOADS["qwen3_1p7b_block_long4096"]
     sh = wl.shape
     T = wl.prefill_rows
@@ -169,6 +172,7 @@ def test_long4096_block_sampled_prefill_rows_and_16_steps():
     ow = widen_layer_f64(w)
     x = synth.prefill_rows(wl.cfg_id, T, sh.hidden)
     sess = DecoderSession(sh, [w], n_ctx=wl.n_ctx, max_rows=T)
+    sess.set_act_split(act_split)
     xd = dev(x)
     sess.prefill(xd)
     torch.cuda.synchronize()
