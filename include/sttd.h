@@ -267,6 +267,27 @@ sttd_status sttd_lm_head_argmax(const void *final_norm, const void *embed, sttd_
                                 const int32_t *x_rows, int n_x_rows, int32_t *ids, float *logits, float *next_x,
                                 int32_t *pos, void *stream);
 
+/* The same head for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument; the call allocates nothing and calls no allocating
+ * routine. Its scratch (the argmax keys of at most
+ * STTD_STATIC_HEAD_MAX_ROWS rows and their normed bf16 planes, 256 KiB) is
+ * a static device array the library holds on each GPU it runs on until the
+ * process ends; its address is looked up once per device on the first call.
+ * Arguments and results are those of sttd_lm_head_argmax, with the same
+ * kernels, except: B > STTD_STATIC_HEAD_MAX_ROWS returns
+ * STTD_ERR_INVALID_ARG; device-side error bits (STTD_DEVERR_ROW,
+ * STTD_DEVERR_TOKEN) are OR'd into the optional device word `err` (NULL: not
+ * recorded). Nothing in the scratch needs to start at zero. Every call on one
+ * GPU shares that GPU's scratch: two calls that overlap in time on one GPU
+ * (different streams, or different host threads without ordering) race and
+ * give undefined results. */
+#define STTD_STATIC_HEAD_MAX_ROWS 16
+sttd_status sttd_lm_head_argmax_static(const void *final_norm, const void *embed, sttd_dtype wtype, int vocab,
+                                       int hidden, float rms_eps, int B, const float *x, int64_t x_row_stride,
+                                       const int32_t *x_rows, int n_x_rows, int32_t *ids, float *logits,
+                                       float *next_x, int32_t *pos, uint32_t *err, void *stream);
+
 /* Greedy stopping rules on the device, per row (the step loop of run() on
  * the Qwen3-ASR model page, and per row in its batched step loop): a row goes
  * on while its newest token is not eos_id, it has fewer than max_new tokens

@@ -25,6 +25,7 @@ EXPORTS = [
     "sttd_workspace_alloc", "sttd_workspace_free", "sttd_workspace_error", "sttd_workspace_set_option",
     "sttd_embed_gather", "sttd_embed_inject",
     "sttd_block_prefill", "sttd_block_prefill_batched", "sttd_block_step", "sttd_lm_head_argmax",
+    "sttd_lm_head_argmax_static",
     "sttd_greedy_stop", "sttd_profile_enable", "sttd_profile_read",
     "sttd_clock_enable", "sttd_clock_disable", "sttd_clock_reset", "sttd_clock_read", "sttd_clock_spans",
 ]
@@ -85,6 +86,8 @@ def lib():
                                            vp, vp],
             "sttd_block_step": [P(BlockParams), P(BlockWeights), vp, vp, i32, i32, vp, vp, i32, vp, vp],
             "sttd_lm_head_argmax": [vp, vp, i32, i32, i32, f32, vp, i32, vp, i64, vp, i32, vp, vp, vp, vp, vp],
+            "sttd_lm_head_argmax_static": [vp, vp, i32, i32, i32, f32, i32, vp, i64, vp, i32, vp, vp, vp, vp, vp,
+                                           vp],
             "sttd_greedy_stop": [P(StopRules), i32, vp, i32, vp, vp, vp, vp, vp, vp, vp],
             "sttd_profile_enable": [ctypes.c_uint32],
             "sttd_profile_read": [i32, P(i64), P(ctypes.c_double)],
@@ -245,3 +248,13 @@ def lm_head_argmax(final_norm, embed, wtype, vocab, hidden, rms_eps, ws, B, x, x
     _check(lib().sttd_lm_head_argmax(final_norm, embed, wtype, vocab, hidden, rms_eps, ws, B, x, x_row_stride,
                                      x_rows, n_x_rows, ids, logits, next_x, pos, stream), "sttd_lm_head_argmax")
 
+
+STATIC_HEAD_MAX_ROWS = 16
+
+
+def lm_head_argmax_static(final_norm, embed, wtype, vocab, hidden, rms_eps, B, x, x_row_stride, ids, logits=0,
+                          next_x=0, pos=0, err=0, stream=0, x_rows=0, n_x_rows=0):
+    """The allocation-free head (no workspace; at most STATIC_HEAD_MAX_ROWS rows)."""
+    _check(lib().sttd_lm_head_argmax_static(final_norm, embed, wtype, vocab, hidden, rms_eps, B, x, x_row_stride,
+                                            x_rows, n_x_rows, ids, logits, next_x, pos, err, stream),
+           "sttd_lm_head_argmax_static")

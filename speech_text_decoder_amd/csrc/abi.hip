@@ -707,6 +707,67 @@ sttd_status sttd_lm_head_argmax(const void* final_norm, const void* embed, sttd_
     return STTD_OK;
 }
 
+}  // extern "C"
+
+// ------------------------------------------------------------ allocation-free head
+// Scratch of sttd_lm_head_argmax_static: per row the persistent head's 1024
+// workgroup keys, then (hidden <= 2048) the normed rows as bf16 high and low
+// planes for the MFMA head. One copy per device for the process's lifetime;
+// host code reaches it only through the address hipGetSymbolAddress returns.
+namespace {
+constexpr int kStaticHeadHidden = 2048;  // widest row the MFMA head's planes hold
+constexpr size_t kStaticPartialBytes = (size_t)STTD_STATIC_HEAD_MAX_ROWS * kHeadPartials * sizeof(unsigned long long);
+constexpr size_t kStaticPlaneBytes = (size_t)2 * STTD_STATIC_HEAD_MAX_ROWS * kStaticHeadHidden * sizeof(uint16_t);
+constexpr size_t kStaticScratchBytes = kStaticPartialBytes + kStaticPlaneBytes;
+constexpr int kMaxDevices = 64;
+
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// The device address of this device's scratch copy, looked up once per device.
+static sttd_status static_scratch(void** out) {
+    int dev = -1;
+    TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return STTD_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    if (!g_static_ptr[dev]) {
+        void* p = nullptr;
+        TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p) return STTD_ERR_BACKEND;
+        g_static_ptr[dev] = p;
+    }
+    *out = g_static_ptr[dev];
+    return STTD_OK;
+}
+
+extern "C" {
+
+sttd_status sttd_lm_head_argmax_static(const void* final_norm, const void* embed, sttd_dtype wtype, int vocab,
+                                       int hidden, float rms_eps, int B, const float* x, int64_t x_row_stride,
+                                       const int32_t* x_rows, int n_x_rows, int32_t* ids, float* logits,
+                                       float* next_x, int32_t* pos, uint32_t* err, void* stream) {
+    if (!final_norm || !embed || !x || !ids || vocab <= 0 || hidden <= 0 || B <= 0) return STTD_ERR_INVALID_ARG;
+    if (wtype != STTD_BF16 && wtype != STTD_F32) return STTD_ERR_UNSUPPORTED;
+    if (hidden % 64 || hidden > 8192) return STTD_ERR_UNSUPPORTED;
+    if (B > STTD_STATIC_HEAD_MAX_ROWS || x_row_stride < hidden) return STTD_ERR_INVALID_ARG;
+    if (x_rows && n_x_rows < 1) return STTD_ERR_INVALID_ARG;
+    void* base = nullptr;
+    const sttd_status st = static_scratch(&base);
+    if (st != STTD_OK) return st;
+    HeadArgs a{};
+    a.gain = final_norm; a.embed = embed; a.vocab = vocab; a.hidden = hidden; a.eps = rms_eps;
+    a.x = x; a.ldx = x_row_stride; a.rows = B; a.ids = ids; a.logits = logits; a.next_x = next_x; a.pos = pos;
+    a.xrow = x_rows; a.n_xrows = n_x_rows;
+    a.partials = (unsigned long long*)base; a.max_partials = kHeadPartials; a.err = err;
+    a.zbuf = hidden <= kStaticHeadHidden ? (uint16_t*)((char*)base + kStaticPartialBytes) : nullptr;
+    ProfScope ps(STTD_KERN_LM_HEAD, (hipStream_t)stream);
+    TRY(launch_lm_head_argmax(a, wtype == STTD_BF16 ? W_BF16 : W_F32, (hipStream_t)stream));
+    return STTD_OK;
+}
+
 sttd_status sttd_greedy_stop(const sttd_stop_rules* r, int B, const int32_t* ids, int advance, int32_t* pos,
                              int32_t* active, int32_t* n_gen, int32_t* tokens, int32_t* truncated, int32_t* n_active,
                              void* stream) {
