@@ -317,12 +317,16 @@ sttd_status sttd_greedy_stop(const sttd_stop_rules *r /* host */, int B, const i
 /* ---------------------------------------------------------------- per-kernel timing
  * The per-op profiler of the MOSS-Transcribe-Diarize page (src/arch/moss/
  * model.cpp, run() and its OpProf table: wall time per graph node), as HIP
- * event pairs: while a kernel family's bit (1 << kind) is set in the mask,
- * each of its launches is bracketed by two events on the launch stream.
- * Launches on a capturing stream are not timed. sttd_profile_read
- * synchronises on the recorded events and returns the number of timed
- * launches and their summed milliseconds, then clears that family. The
- * attention-rows family spans the split kernel and its combine. */
+ * events: while a kernel family's bit (1 << kind) is set in the mask, every
+ * kernel an eager call of that family launches carries a start/stop event pair
+ * bound to its dispatch (hipExtLaunchKernel), so each pair times one kernel
+ * from dispatch to completion, as rocprofv3's kernel trace does, without the
+ * gaps between kernels. Launches on a capturing stream are not timed.
+ * sttd_profile_read synchronises on the recorded events and returns the number
+ * of timed calls of the family and the summed milliseconds of their kernels,
+ * then clears that family. A call may launch several kernels: the attention-
+ * rows family spans the split kernel and its combine, the head its finalize
+ * pass. */
 typedef enum {
     STTD_KERN_RMSNORM = 0,      /* RMSNorm rows to bf16 (prefill) */
     STTD_KERN_QKV_GEMV = 1,     /* fused RMSNorm + Q|K|V projection, decode rows */

@@ -55,7 +55,8 @@ namespace {
 struct Profiler {
     std::mutex mu;
     uint32_t mask = 0;
-    std::vector<std::pair<hipEvent_t, hipEvent_t>> timed[STTD_KERN_COUNT];
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> timed[STTD_KERN_COUNT];  // one pair per kernel launch
+    int64_t calls[STTD_KERN_COUNT] = {};                                    // timed calls of each family
     std::vector<hipEvent_t> pool;
 
     hipEvent_t get() {
@@ -70,6 +71,8 @@ struct Profiler {
     }
 };
 Profiler g_prof;
+// Event pairs of the launches of the call being issued on this thread (nullptr: not timed).
+thread_local std::vector<std::pair<hipEvent_t, hipEvent_t>>* t_pairs = nullptr;
 
 // Device-clock timing: one slot of kClockEntries (start, end) pairs per timed launch.
 struct ClockProf {
@@ -99,11 +102,12 @@ hipError_t clock_collect(std::vector<uint64_t>& h) {
     return e;
 }
 
-// Times the launches of one kernel family: event pairs (eager launches) and/or
-// a device-clock slot (eager or captured launches), as enabled.
+// Times the launches of one kernel family: an event pair bound to each kernel's
+// dispatch (eager launches) and/or a device-clock slot (eager or captured
+// launches), as enabled.
 class ProfScope {
   public:
-    ProfScope(int kind, hipStream_t s) : kind_(kind), s_(s) {
+    ProfScope(int kind, hipStream_t s) : kind_(kind) {
         if (g_clk.mask & (1u << kind)) {
             std::lock_guard<std::mutex> lk(g_clk.mu);
             if (g_clk.used < g_clk.cap) {
@@ -114,23 +118,22 @@ class ProfScope {
         if (!(g_prof.mask & (1u << kind))) return;
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
-        std::lock_guard<std::mutex> lk(g_prof.mu);
-        b_ = g_prof.get();
-        e_ = g_prof.get();
-        if (b_ && e_ && hipEventRecord(b_, s) != hipSuccess) b_ = nullptr;
+        timed_ = true;
+        t_pairs = &pairs_;
     }
     ~ProfScope() {
         g_clk.current = nullptr;
-        if (!b_ || !e_) return;
-        if (hipEventRecord(e_, s_) != hipSuccess) return;
+        if (!timed_) return;
+        t_pairs = nullptr;
         std::lock_guard<std::mutex> lk(g_prof.mu);
-        g_prof.timed[kind_].emplace_back(b_, e_);
+        for (auto& pr : pairs_) g_prof.timed[kind_].push_back(pr);
+        g_prof.calls[kind_] += 1;
     }
 
   private:
     int kind_;
-    hipStream_t s_;
-    hipEvent_t b_ = nullptr, e_ = nullptr;
+    bool timed_ = false;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> pairs_;
 };
 
 constexpr int kGemvMaxRows = 4;    // rows beyond this take the MFMA GEMMs (bf16 weights)
@@ -198,7 +201,10 @@ KVLayer kv_layer(const sttd_kv_cache* kv, int layer) {
 // Splits of each row's cache span over workgroups: about 128 positions each,
 // but for batches of rows no more than about one 8-wave workgroup per CU
 // (256), so each workgroup streams a longer run of rows (measured on 16 rows of
-// 150-1500 positions: 256 workgroups of 8 waves beat 512 of 4 and any larger grid).
+// 150-1500 positions: 256 workgroups of 8 waves beat 512 of 4 and any larger grid;
+// 256 workgroups dealt to the rows by length (22.8 us per block) and one split per
+// row (27.8 us) both lost to two equal splits per row (21.0 us): the split merge
+// costs a write-through, an atomic and a reload, not the streaming).
 int choose_splits(int rows, int n_kv, int pos_bound, int part_cap) {
     int s = (pos_bound + 127) / 128;
     if (s > 32) s = 32;  // long single rows: fewer, longer splits (8-wave workgroups) and one combine
@@ -396,6 +402,17 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
 }  // namespace
 
 uint64_t* sttd::clock_slot() { return g_clk.current; }
+
+bool sttd::next_launch_events(hipEvent_t* start, hipEvent_t* stop) {
+    if (!t_pairs) return false;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    hipEvent_t b = g_prof.get(), e = g_prof.get();
+    if (!b || !e) return false;
+    t_pairs->emplace_back(b, e);
+    *start = b;
+    *stop = e;
+    return true;
+}
 
 extern "C" {
 
@@ -856,9 +873,12 @@ sttd_status sttd_clock_spans(int max, int* kinds, uint64_t* start_end, int* n) {
 sttd_status sttd_profile_read(int kernel, int64_t* launches, double* total_ms) {
     if (kernel < 0 || kernel >= STTD_KERN_COUNT || !launches || !total_ms) return STTD_ERR_INVALID_ARG;
     std::vector<std::pair<hipEvent_t, hipEvent_t>> pairs;
+    int64_t calls = 0;
     {
         std::lock_guard<std::mutex> lk(g_prof.mu);
         pairs.swap(g_prof.timed[kernel]);
+        calls = g_prof.calls[kernel];
+        g_prof.calls[kernel] = 0;
     }
     double sum = 0.0;
     sttd_status st = STTD_OK;
@@ -875,7 +895,7 @@ sttd_status sttd_profile_read(int kernel, int64_t* launches, double* total_ms) {
             g_prof.pool.push_back(pr.second);
         }
     }
-    *launches = (int64_t)pairs.size();
+    *launches = calls;
     *total_ms = sum;
     return st;
 }

@@ -54,23 +54,35 @@ struct RowsArgs {
     uint64_t* clk;
 };
 
-// One head vector of D values: RMSNorm with `gain`, NeoX rotation at `pos`,
-// times `scale`, into dst (LDS); one wave. Lane i < D/2 owns the pair (i, i + D/2).
-template <class GT, int D>
-__device__ __forceinline__ void norm_rope_head(const float* __restrict__ src, const typename GT::T* gain, float eps,
-                                               const float* __restrict__ rope, int pos, float scale, float* dst) {
-    constexpr int HALF = D / 2;
-    const int lane = threadIdx.x % WAVE;
-    const bool act = lane < HALF;
-    const float u0 = act ? src[lane] : 0.f, u1 = act ? src[lane + HALF] : 0.f;
-    const float rs = 1.0f / sqrtf(wave_sum(u0 * u0 + u1 * u1) / (float)D + eps);
-    if (act) {
-        const float a = u0 * rs * GT::ld(gain, lane), b = u1 * rs * GT::ld(gain, lane + HALF);
-        const float2 cs = reinterpret_cast<const float2*>(rope)[(int64_t)pos * HALF + lane];
-        dst[lane] = (a * cs.x - b * cs.y) * scale;
-        dst[lane + HALF] = (a * cs.y + b * cs.x) * scale;
+// Eight cache elements as loaded (16 bytes of f16, or 32 of fp32), widened at use,
+// so a wave holds twice the rows in flight for the registers of fp32 copies.
+template <class KT>
+struct KvRaw;
+template <>
+struct KvRaw<F16> {
+    u32x4 v;
+    __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const u32x4*>(p); }
+    __device__ __forceinline__ void widen(float* o) const {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = f16_bits_to_f32((uint16_t)(w[i] & 0xFFFFu));
+            o[2 * i + 1] = f16_bits_to_f32((uint16_t)(w[i] >> 16));
+        }
     }
-}
+};
+template <>
+struct KvRaw<F32> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const f32x4*>(p);
+        b = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    __device__ __forceinline__ void widen(float* o) const {
+        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+        o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    }
+};
 
 // Fold another (m, l, o) running state into this one (base-2 exponents).
 template <int G>
@@ -166,7 +178,8 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
     float2 cs = make_float2(1.f, 0.f);
     if (FUSE) cs = reinterpret_cast<const float2*>(a.rope)[(int64_t)(ok ? pos : 0) * HALF + lc];
     const int n_keys = ok ? pos + 1 : 0;
-    const int chunk = (n_keys + a.n_splits - 1) / a.n_splits;
+    const int ns = a.n_splits;
+    const int chunk = (n_keys + ns - 1) / ns;
     const int c0 = split * chunk;
     const int c1 = min(c0 + chunk, n_keys);
     const bool owner = FUSE && ok && c0 <= pos && pos < c1;  // this split holds the new key
@@ -175,15 +188,17 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
     const T* Vp = (const T*)a.kv.v + slab + sub * 8;
     const int cend = owner ? pos : c1;  // the new key (owner) is folded in from LDS below
     // RIF rows per group in flight: row c + q * NG for q < RIF (clamped to row 0 past the end)
+    // (8 per group for G <= 2 with f16 rows kept packed measured slower for one
+    // decode row: 5.4 -> 6.3 us per launch)
     constexpr int RIF = G <= 2 ? 4 : (G == 4 ? 2 : 1);
     constexpr int STEP = RIF * NG;
     int c = c0 + grp;
-    float kr[RIF][8], vr[RIF][8];
+    KvRaw<KT> kr[RIF], vr[RIF];
 #pragma unroll
     for (int q = 0; q < RIF; ++q) {
         const int cq = c + q * NG < cend ? c + q * NG : 0;
-        load8(Kp + (int64_t)cq * D, kr[q], KT());
-        load8(Vp + (int64_t)cq * D, vr[q], KT());
+        kr[q].load(Kp + (int64_t)cq * D);
+        vr[q].load(Vp + (int64_t)cq * D);
     }
     __builtin_amdgcn_sched_barrier(0);
     // 3. finish the head items: RMSNorm + rotation (queries, key); the owner
@@ -240,31 +255,35 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
         float sc[RIF][G];
 #pragma unroll
         for (int q = 0; q < RIF; ++q) {
+            float kf[8];
+            kr[q].widen(kf);
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 float t = 0.f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) t = fmaf(qv[g][i], kr[q][i], t);
+                for (int i = 0; i < 8; ++i) t = fmaf(qv[g][i], kf[i], t);
                 sc[q][g] = group_sum<LPK>(t);
             }
         }
-        float vcur[RIF][8];
+        KvRaw<KT> vcur[RIF];
 #pragma unroll
-        for (int q = 0; q < RIF; ++q)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) vcur[q][i] = vr[q][i];
+        for (int q = 0; q < RIF; ++q) vcur[q] = vr[q];
         const int cn = c + STEP;
         if (cn < cend) {
 #pragma unroll
             for (int q = 0; q < RIF; ++q) {
                 const int cq = cn + q * NG < cend ? cn + q * NG : cn;
-                load8(Kp + (int64_t)cq * D, kr[q], KT());
-                load8(Vp + (int64_t)cq * D, vr[q], KT());
+                kr[q].load(Kp + (int64_t)cq * D);
+                vr[q].load(Vp + (int64_t)cq * D);
             }
         }
 #pragma unroll
         for (int q = 0; q < RIF; ++q)
-            if (c + q * NG < cend) step_state<G>(m, l, o, sc[q], vcur[q]);
+            if (c + q * NG < cend) {
+                float vf[8];
+                vcur[q].widen(vf);
+                step_state<G>(m, l, o, sc[q], vf);
+            }
     }
     // 5. the new key (held in LDS by the owner), folded in by group 0
     if (owner && grp == 0) {
@@ -332,7 +351,7 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
                 O += f * wo_lds[w][g][e];
             }
         }
-        if (a.n_splits == 1) {
+        if (ns == 1) {
             const float v = L > 0.f ? O / L : 0.f;
             const int64_t idx = (int64_t)r * a.ldo + (j * G + g) * D + e;
             if (a.out_f32) {
@@ -362,7 +381,7 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
     //    merges from LDS. It resets the count for the next launch. Only the
     //    publishing instantiation carries this (and its LDS).
     if constexpr (std::is_same<MEM, PubMem>::value) {
-        if (a.merge_ctr && a.n_splits > 1) {
+        if (a.merge_ctr && ns > 1) {
             constexpr int MREC = 64;  // records staged: G * n_splits <= MREC (checked on the host)
             __shared__ __attribute__((aligned(16))) float mrg[MREC * (D + 4)];
             __shared__ int is_last;
@@ -371,12 +390,13 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
             if (tid == 0) {
                 uint32_t* c = a.merge_ctr + (int64_t)r * a.kv.n_kv + j;
                 const uint32_t old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                is_last = old == (uint32_t)(a.n_splits - 1);
+                is_last = old == (uint32_t)(ns - 1);
                 if (is_last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             __syncthreads();
             if (is_last) {
-                // the G heads' records are contiguous: record (g, split) at (g * n_splits + split) * (D + 4)
+                // the G heads' records are contiguous: record (g, split) at (g * n_splits + split) * (D + 4);
+                // this row's are splits [0, ns) of each head
                 const int nrec = G * a.n_splits;
                 const uint64_t* src = reinterpret_cast<const uint64_t*>(
                     a.part + ((int64_t)r * a.n_heads + j * G) * a.n_splits * (D + 4));
@@ -388,10 +408,10 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
                     const int g = t / D, e = t % D;
                     const float* rec = mrg + g * a.n_splits * (D + 4);
                     float M = -INFINITY;
-                    for (int sp = 0; sp < a.n_splits; ++sp) M = fmaxf(M, rec[sp * (D + 4)]);
+                    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, rec[sp * (D + 4)]);
                     float L = 0.f, O = 0.f;
                     if (M != -INFINITY) {
-                        for (int sp = 0; sp < a.n_splits; ++sp) {
+                        for (int sp = 0; sp < ns; ++sp) {
                             const float w = exp2f(rec[sp * (D + 4)] - M);
                             L = fmaf(w, rec[sp * (D + 4) + 1], L);
                             O = fmaf(w, rec[sp * (D + 4) + 4 + e], O);

@@ -69,11 +69,11 @@ static hipError_t rows_dispatch(const RowsArgs& a, int R, bool wide, hipStream_t
 #define ROWS_LAUNCH(G_)                                                                             \
     do {                                                                                            \
         if (G_ <= 2 && !wide) {                                                                     \
-            if (pub) attn_rows_kernel<KT, GT, D, G_, 4, FUSE, true><<<grid, 4 * 64, 0, s>>>(a);     \
-            else attn_rows_kernel<KT, GT, D, G_, 4, FUSE, false><<<grid, 4 * 64, 0, s>>>(a);        \
+            if (pub) launch_kernel(attn_rows_kernel<KT, GT, D, G_, 4, FUSE, true>, grid, 4 * 64, 0, s, a);     \
+            else launch_kernel(attn_rows_kernel<KT, GT, D, G_, 4, FUSE, false>, grid, 4 * 64, 0, s, a);        \
         } else {                                                                                    \
-            if (pub) attn_rows_kernel<KT, GT, D, G_, 8, FUSE, true><<<grid, 8 * 64, 0, s>>>(a);     \
-            else attn_rows_kernel<KT, GT, D, G_, 8, FUSE, false><<<grid, 8 * 64, 0, s>>>(a);        \
+            if (pub) launch_kernel(attn_rows_kernel<KT, GT, D, G_, 8, FUSE, true>, grid, 8 * 64, 0, s, a);     \
+            else launch_kernel(attn_rows_kernel<KT, GT, D, G_, 8, FUSE, false>, grid, 8 * 64, 0, s, a);        \
         }                                                                                           \
     } while (0)
     switch (G) {
@@ -85,7 +85,7 @@ static hipError_t rows_dispatch(const RowsArgs& a, int R, bool wide, hipStream_t
     }
 #undef ROWS_LAUNCH
     if (a.n_splits > 1 && (a.out_f32 || a.out_bf16) && !a.merge_ctr)
-        attn_combine_kernel<D><<<dim3(R, a.n_heads), D, 0, s>>>(a.part, a.n_heads, a.n_splits, a.out_f32, a.out_bf16,
+        launch_kernel(attn_combine_kernel<D>, dim3(R, a.n_heads), D, 0, s, a.part, a.n_heads, a.n_splits, a.out_f32, a.out_bf16,
                                                                 a.out_lo, a.ldo, a.clk);
     return hipGetLastError();
 }
@@ -159,15 +159,13 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
     constexpr int NT = 512;                // 8 waves: 4 row groups x 2 key groups
     constexpr int RF = 2;                  // 16-row fragments per wave
     constexpr int KB = 64, TQ = 4 * 16 * RF;
-    constexpr int KS = D, VS = KB;  // unpadded rows; 16-byte chunks XOR-swizzled by the row (swz below)
+    constexpr int KS = D;  // K and V rows unpadded; 16-byte chunks XOR-swizzled by the row (swz below)
     constexpr int KSTEPS = D / 32, DF = D / 16;
-    constexpr int KVECS = KB * D / 8 / NT;                  // 16-byte K pieces per thread per block
-    constexpr int VITEMS = (KB / 2) * (D / 8);              // (key pair, 8-dim chunk) items of V per block
-    constexpr int VPAIRS = (VITEMS + NT - 1) / NT;          // per thread
+    constexpr int KVECS = KB * D / 8 / NT;                  // 16-byte K (and V) pieces per thread per block
     constexpr int HO = DF / 2 * RF * 4;                     // O values per lane in each half of the hand-over
-    static_assert(HO * 256 * 4 <= 2 * KB * KS * 2 && HO * 256 * 4 <= 2 * D * VS * 2, "hand-over fits the buffers");
+    static_assert(HO * 256 * 4 <= 2 * KB * KS * 2, "hand-over fits the buffers");
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KB * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VS];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KB * KS];
     __shared__ float ml[2][RF][256];
     // element offset of 16-byte chunk c of an LDS row r of `stride` elements
     auto swz = [](int r, int c, int stride) { return r * stride + ((c ^ (r & 7)) * 8); };
@@ -228,49 +226,47 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
         const int n_keys = pos0 + tile_last + 1;  // keys any row of the tile can see
         const int n_blocks = (n_keys + KB - 1) / KB;
 
-        // staging: K as 16-byte row pieces; V as pairs of keys (2c, 2c + 1) over one
-        // 8-dim chunk, written to V^T as 32-bit words (the permutation keeps the
-        // pair adjacent). Rows past the tile's last key are clamped to it: they are
-        // real, finite cache rows whose scores the diagonal mask sets to -inf, so
-        // they add 0 to O
-        u32x4 kreg[KVECS], vreg[2 * VPAIRS];
+        // staging: K and V rows alike, as 16-byte row pieces (V is read transposed
+        // later). Rows past the tile's last key are clamped to it: they are real,
+        // finite cache rows whose scores the diagonal mask sets to -inf, so they add
+        // 0 to O
+        u32x4 kreg[KVECS], vreg[KVECS];
         auto fetch = [&](int kb) {
 #pragma unroll
             for (int i = 0; i < KVECS; ++i) {
                 const int v = tid + i * NT;
-                const int ck = min(kb * KB + v / (D / 8), n_keys - 1), ek = (v % (D / 8)) * 8;
-                kreg[i] = *reinterpret_cast<const u32x4*>(Kg + (int64_t)ck * D + ek);
-            }
-#pragma unroll
-            for (int i = 0; i < VPAIRS; ++i) {
-                const int v0 = tid + i * NT, v = v0 < VITEMS ? v0 : 0;
-                const int cv = kb * KB + 2 * (v % (KB / 2)), ev = (v / (KB / 2)) * 8;
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-                    vreg[2 * i + u] = *reinterpret_cast<const u32x4*>(Vg + (int64_t)min(cv + u, n_keys - 1) * D + ev);
+                const int64_t off = (int64_t)min(kb * KB + v / (D / 8), n_keys - 1) * D + (v % (D / 8)) * 8;
+                kreg[i] = *reinterpret_cast<const u32x4*>(Kg + off);
+                vreg[i] = *reinterpret_cast<const u32x4*>(Vg + off);
             }
         };
         auto stash = [&](int buf) {
 #pragma unroll
             for (int i = 0; i < KVECS; ++i) {
                 const int v = tid + i * NT;
-                *reinterpret_cast<u32x4*>(&Ks[buf][swz(v / (D / 8), v % (D / 8), KS)]) = kreg[i];
+                const int o = swz(v / (D / 8), v % (D / 8), KS);
+                *reinterpret_cast<u32x4*>(&Ks[buf][o]) = kreg[i];
+                *reinterpret_cast<u32x4*>(&Vs[buf][o]) = vreg[i];
             }
-#pragma unroll
-            for (int i = 0; i < VPAIRS; ++i) {
-                const int v = tid + i * NT;
-                if (v >= VITEMS) continue;
-                const int c = 2 * (v % (KB / 2)), e = (v / (KB / 2)) * 8, kk = c % 32;
-                const int pp = kk < 16 ? 8 * (kk / 4) + kk % 4 : 8 * ((kk - 16) / 4) + 4 + (kk - 16) % 4;
-                const int pos = (c / 32) * 32 + pp;  // even: the pair shares one 32-bit word
-                const u32x4 a = vreg[2 * i], b = vreg[2 * i + 1];
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    // dim e + jj of keys c (low half) and c + 1 (high half): one byte permute
-                    const uint32_t w = __builtin_amdgcn_perm(b[jj / 2], a[jj / 2], jj % 2 ? 0x07060302u : 0x05040100u);
-                    *reinterpret_cast<uint32_t*>(&Vt[buf][swz(e + jj, pos / 8, VS) + pos % 8]) = w;
-                }
-            }
+        };
+        // V^T fragment (A operand) of dims 16 df .. 16 df + 15 over the key group's 32
+        // keys by two LDS transpose reads (ds_read_b64_tr_b16). Within each 16-lane
+        // group the lanes hand in 16 rows of four 16-bit values and lane i receives
+        // element i % 4 of rows i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12 (checked on
+        // the device). Lane (g4, r16) hands in key row 4 g4 + r16 / 4 (then + 16) at
+        // dims 16 df + 4 (r16 % 4) .. + 3, so it receives dim 16 df + r16 of keys
+        // 4 g4 .. 4 g4 + 3 and 16 + 4 g4 .. 16 + 4 g4 + 3: the keys the S^T fragment
+        // gives the same lane in the P^T B operand.
+        auto vt_frag = [&](int buf, int df) {
+            const int row = kg * 32 + 4 * g4 + r16 / 4, dim = df * 16 + 4 * (r16 % 4);
+            const int o0 = swz(row, dim / 8, KS) + dim % 8, o1 = swz(row + 16, dim / 8, KS) + dim % 8;
+            typedef short s16x4 __attribute__((ext_vector_type(4)));
+            typedef short s16x8 __attribute__((ext_vector_type(8)));
+            const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(&Vs[buf][o0]));
+            const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(&Vs[buf][o1]));
+            return __builtin_bit_cast(f16x8, (s16x8)__builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
         };
         fetch(0);
         stash(0);
@@ -345,7 +341,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
             for (int rf = 0; rf < RF; ++rf) lacc[rf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[rf], lacc[rf], 0, 0, 0);
 #pragma unroll
             for (int df = 0; df < DF; ++df) {
-                const f16x8 vfr = *reinterpret_cast<const f16x8*>(&Vt[buf][swz(df * 16 + r16, kg * 4 + g4, VS)]);
+                const f16x8 vfr = vt_frag(buf, df);
 #pragma unroll
                 for (int rf = 0; rf < RF; ++rf)
                     o[df][rf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vfr, pb[rf], o[df][rf], 0, 0, 0);
@@ -360,7 +356,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
         // buffers are free after the loop's last barrier), lane-minor so that a
         // wave's 64 stores hit 64 consecutive words
         float* xo0 = reinterpret_cast<float*>(&Ks[0][0]);  // O values of df < DF / 2
-        float* xo1 = reinterpret_cast<float*>(&Vt[0][0]);  // and of the rest
+        float* xo1 = reinterpret_cast<float*>(&Vs[0][0]);  // and of the rest
         const int slot = wr * WAVE + lane;
         if (kg == 1) {
 #pragma unroll
@@ -414,9 +410,9 @@ hipError_t launch_attn_prefill(const uint16_t* q16, int64_t ldq, int T, int pos0
     const int paired = n_tiles * n_heads >= 512;
     dim3 grid(paired ? (n_tiles + 1) / 2 : n_tiles, n_heads);
     if (kv.d == 128)
-        attn_prefill_kernel<128><<<grid, 512, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, paired, clock_slot());
+        launch_kernel(attn_prefill_kernel<128>, grid, 512, 0, s, q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, paired, clock_slot());
     else if (kv.d == 64)
-        attn_prefill_kernel<64><<<grid, 512, 0, s>>>(q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, paired, clock_slot());
+        launch_kernel(attn_prefill_kernel<64>, grid, 512, 0, s, q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, paired, clock_slot());
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -474,12 +474,12 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     const int tiles_m = (g.M + BIG_BM - 1) / BIG_BM;
     if (epi == GEMM_SWIGLU) {
         const int tiles_n = g.N / 128;
-        gemm_big_kernel<GEMM_SWIGLU, BIG_BN><<<tiles_m * tiles_n, 512, 0, s>>>(g, tiles_m, tiles_n);
+        launch_kernel(gemm_big_kernel<GEMM_SWIGLU, BIG_BN>, tiles_m * tiles_n, 512, 0, s, g, tiles_m, tiles_n);
         return;
     }
     if (epi == GEMM_QKROPE) {
         const int tiles_n = g.N / BIG_BN;
-        gemm_big_kernel<GEMM_QKROPE, BIG_BN><<<tiles_m * tiles_n, 512, 0, s>>>(g, tiles_m, tiles_n);
+        launch_kernel(gemm_big_kernel<GEMM_QKROPE, BIG_BN>, tiles_m * tiles_n, 512, 0, s, g, tiles_m, tiles_n);
         return;
     }
     // residual outputs too narrow to fill the CUs even with 256 x 128 tiles: two
@@ -491,7 +491,7 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     const int tiles128 = tiles_m * ((g.N + 127) / 128);
     if (epi == GEMM_RESID && tiles128 < 256 && tiles256 % 8 == 0 && (g.K / BIG_BK) % 2 == 0 &&
         g.K / BIG_BK >= 16) {
-        gemm_big_kernel<GEMM_RESID, BIG_BN, 2><<<tiles256 * 2, 512, 0, s>>>(g, tiles_m, (g.N + BIG_BN - 1) / BIG_BN);
+        launch_kernel(gemm_big_kernel<GEMM_RESID, BIG_BN, 2>, tiles256 * 2, 512, 0, s, g, tiles_m, (g.N + BIG_BN - 1) / BIG_BN);
         return;
     }
     // narrow outputs: 128-column tiles so that about a full wave of workgroups runs
@@ -500,11 +500,11 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     const int tiles_n = (g.N + bn - 1) / bn;
     const int grid = tiles_m * tiles_n;
     if (epi == GEMM_RESID) {
-        if (narrow) gemm_big_kernel<GEMM_RESID, 128><<<grid, 512, 0, s>>>(g, tiles_m, tiles_n);
-        else gemm_big_kernel<GEMM_RESID, BIG_BN><<<grid, 512, 0, s>>>(g, tiles_m, tiles_n);
+        if (narrow) launch_kernel(gemm_big_kernel<GEMM_RESID, 128>, grid, 512, 0, s, g, tiles_m, tiles_n);
+        else launch_kernel(gemm_big_kernel<GEMM_RESID, BIG_BN>, grid, 512, 0, s, g, tiles_m, tiles_n);
     } else {
-        if (narrow) gemm_big_kernel<GEMM_STORE, 128><<<grid, 512, 0, s>>>(g, tiles_m, tiles_n);
-        else gemm_big_kernel<GEMM_STORE, BIG_BN><<<grid, 512, 0, s>>>(g, tiles_m, tiles_n);
+        if (narrow) launch_kernel(gemm_big_kernel<GEMM_STORE, 128>, grid, 512, 0, s, g, tiles_m, tiles_n);
+        else launch_kernel(gemm_big_kernel<GEMM_STORE, BIG_BN>, grid, 512, 0, s, g, tiles_m, tiles_n);
     }
 }
 
@@ -520,7 +520,9 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
 template <int EPI, int RF, int CF>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     // K-steps of 32 per load batch (8, in flight twice the bytes, measured slower
-    // at 16 rows: gate_up 17.4 -> 18.0 us, down 10.8 -> 11.7 us)
+    // at 16 rows: gate_up 17.4 -> 18.0 us, down 10.8 -> 11.7 us; two alternating
+    // batches of 4, loading one while the other feeds the MFMAs, measured slower too:
+    // QKV 7.6 -> 9.0 us, down 10.8 -> 13.0 us, from the higher register count)
     constexpr int PD = 4;
     __shared__ float red[4][RF * 16][CF * 16 + 1];
     clock_begin(g.clk);
@@ -637,13 +639,17 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 }
 
 // Rows a skinny launch takes (16 per row fragment, up to 4 fragments).
+#ifndef STTD_SKINNY_MAX_ROWS
 constexpr int kSkinnyMaxRows = 64;
+#else
+constexpr int kSkinnyMaxRows = STTD_SKINNY_MAX_ROWS;
+#endif
 
 template <int EPI, int CF>
 static void launch_skinny_rf(const GemmArgs& g, dim3 grid, hipStream_t s) {
-    if (g.M <= 16) gemm_skinny_kernel<EPI, 1, CF><<<grid, 256, 0, s>>>(g);
-    else if (g.M <= 32) gemm_skinny_kernel<EPI, 2, CF><<<grid, 256, 0, s>>>(g);
-    else gemm_skinny_kernel<EPI, 4, CF><<<grid, 256, 0, s>>>(g);
+    if (g.M <= 16) launch_kernel(gemm_skinny_kernel<EPI, 1, CF>, grid, 256, 0, s, g);
+    else if (g.M <= 32) launch_kernel(gemm_skinny_kernel<EPI, 2, CF>, grid, 256, 0, s, g);
+    else launch_kernel(gemm_skinny_kernel<EPI, 4, CF>, grid, 256, 0, s, g);
 }
 
 static void launch_gemm_skinny(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
@@ -660,16 +666,16 @@ static void launch_gemm_skinny(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     else launch_skinny_rf<GEMM_STORE, 1>(g, dim3(tiles, 1), s);
 }
 
-template <bool SPLIT>
-static hipError_t launch_gemm_t(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
-    constexpr int BM = 64, BN = 128;
+template <int BM, bool SPLIT>
+static hipError_t launch_gemm_bm(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
+    constexpr int BN = 128;
     const unsigned gy = (g.M + BM - 1) / BM;
     if (epi == GEMM_SWIGLU) {
         // 64-column tiles (32 act columns) when 128-column ones would leave CUs idle
         if ((unsigned)(g.N / (BN / 2)) * gy < 512 && g.N % 32 == 0)
-            gemm_bf16_kernel<BM, 64, GEMM_SWIGLU, SPLIT><<<dim3(g.N / 32, gy, 1), 256, 0, s>>>(g);
+            launch_kernel(gemm_bf16_kernel<BM, 64, GEMM_SWIGLU, SPLIT>, dim3(g.N / 32, gy, 1), 256, 0, s, g);
         else
-            gemm_bf16_kernel<BM, BN, GEMM_SWIGLU, SPLIT><<<dim3(g.N / (BN / 2), gy, 1), 256, 0, s>>>(g);
+            launch_kernel(gemm_bf16_kernel<BM, BN, GEMM_SWIGLU, SPLIT>, dim3(g.N / (BN / 2), gy, 1), 256, 0, s, g);
         return hipSuccess;
     }
     dim3 grid((g.N + BN - 1) / BN, gy, 1);
@@ -681,13 +687,22 @@ static hipError_t launch_gemm_t(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     if (epi == GEMM_STORE && grid.z > 1) {
         const hipError_t e = launch_fill_zero(g.C, (size_t)g.M * g.N * sizeof(float), s);
         if (e != hipSuccess) return e;
-        gemm_bf16_kernel<BM, BN, GEMM_RESID, SPLIT><<<grid, 256, 0, s>>>(g);
+        launch_kernel(gemm_bf16_kernel<BM, BN, GEMM_RESID, SPLIT>, grid, 256, 0, s, g);
     } else if (epi == GEMM_RESID) {
-        gemm_bf16_kernel<BM, BN, GEMM_RESID, SPLIT><<<grid, 256, 0, s>>>(g);
+        launch_kernel(gemm_bf16_kernel<BM, BN, GEMM_RESID, SPLIT>, grid, 256, 0, s, g);
     } else {
-        gemm_bf16_kernel<BM, BN, GEMM_STORE, SPLIT><<<grid, 256, 0, s>>>(g);
+        launch_kernel(gemm_bf16_kernel<BM, BN, GEMM_STORE, SPLIT>, grid, 256, 0, s, g);
     }
     return hipSuccess;
+}
+
+// 64-row tiles. One 160-row tile per workgroup (every row of a 153-row prefill, so
+// each weight tile streams once) measured slower at 153 rows: gate_up 42.8 -> 59.4 us,
+// QKV 19.3 -> 26.2, O 14.3 -> 18.2, down 24.7 -> 31.5 (fewer, larger workgroups at
+// one or two waves per SIMD hide less of each K-step's load latency).
+template <bool SPLIT>
+static hipError_t launch_gemm_t(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
+    return launch_gemm_bm<64, SPLIT>(g, epi, s);
 }
 
 hipError_t launch_gemm(const GemmArgs& args, GemmEpi epi, hipStream_t s) {

@@ -111,12 +111,12 @@ static void launch_bt(const GemvArgs& a, hipStream_t s) {
     const int per_wg = EPI == GEMV_SWIGLU ? NR / 2 : NR;
     dim3 grid((a.N + per_wg - 1) / per_wg, 1);
     if (a.rows == 1) {
-        gemv_kernel<WT, EPI, 1, NR, KCH, NORM, XPART><<<grid, 256, 0, s>>>(a);
+        launch_kernel(gemv_kernel<WT, EPI, 1, NR, KCH, NORM, XPART>, grid, 256, 0, s, a);
     } else if (a.rows == 2) {
-        gemv_kernel<WT, EPI, 2, NR, KCH, NORM, XPART><<<grid, 256, 0, s>>>(a);
+        launch_kernel(gemv_kernel<WT, EPI, 2, NR, KCH, NORM, XPART>, grid, 256, 0, s, a);
     } else {
         grid.y = (a.rows + 3) / 4;
-        gemv_kernel<WT, EPI, 4, NR, KCH, NORM, XPART><<<grid, 256, 0, s>>>(a);
+        launch_kernel(gemv_kernel<WT, EPI, 4, NR, KCH, NORM, XPART>, grid, 256, 0, s, a);
     }
 }
 
@@ -305,11 +305,11 @@ __global__ __launch_bounds__(256) void lm_head_finalize_kernel(HeadArgs a, int n
 template <class WT, int KCH>
 static void launch_head_k(const HeadArgs& a, dim3 grid, hipStream_t s) {
     constexpr int NR = 8;
-    if (a.rows == 1) lm_head_kernel<WT, 1, NR, KCH><<<grid, 256, 0, s>>>(a);
-    else if (a.rows == 2) lm_head_kernel<WT, 2, NR, KCH><<<grid, 256, 0, s>>>(a);
+    if (a.rows == 1) launch_kernel(lm_head_kernel<WT, 1, NR, KCH>, grid, 256, 0, s, a);
+    else if (a.rows == 2) launch_kernel(lm_head_kernel<WT, 2, NR, KCH>, grid, 256, 0, s, a);
     else {
         grid.y = (a.rows + 3) / 4;
-        lm_head_kernel<WT, 4, NR, KCH><<<grid, 256, 0, s>>>(a);
+        launch_kernel(lm_head_kernel<WT, 4, NR, KCH>, grid, 256, 0, s, a);
     }
 }
 
@@ -326,7 +326,7 @@ static hipError_t launch_head_wt(const HeadArgs& a, hipStream_t s) {
         case 4: launch_head_k<WT, 4>(a, grid, s); break;
         default: return hipErrorInvalidValue;
     }
-    lm_head_finalize_kernel<WT><<<a.rows, 256, 0, s>>>(a, grid_x);
+    launch_kernel(lm_head_finalize_kernel<WT>, a.rows, 256, 0, s, a, grid_x);
     return hipGetLastError();
 }
 
@@ -434,11 +434,11 @@ static hipError_t launch_head_mfma(const HeadArgs& a, hipStream_t s) {
         const int nb = a.rows - b0 < 16 ? a.rows - b0 : 16;
         const uint16_t* h = zh + (size_t)b0 * a.hidden;
         const uint16_t* l = zl + (size_t)b0 * a.hidden;
-        if (ksw <= 4) head_mfma_kernel<4><<<grid, 256, 0, s>>>(a, h, l, b0, nb);
-        else if (ksw <= 8) head_mfma_kernel<8><<<grid, 256, 0, s>>>(a, h, l, b0, nb);
-        else head_mfma_kernel<16><<<grid, 256, 0, s>>>(a, h, l, b0, nb);
+        if (ksw <= 4) launch_kernel(head_mfma_kernel<4>, grid, 256, 0, s, a, h, l, b0, nb);
+        else if (ksw <= 8) launch_kernel(head_mfma_kernel<8>, grid, 256, 0, s, a, h, l, b0, nb);
+        else launch_kernel(head_mfma_kernel<16>, grid, 256, 0, s, a, h, l, b0, nb);
     }
-    lm_head_finalize_kernel<BF16><<<a.rows, 256, 0, s>>>(a, grid);
+    launch_kernel(lm_head_finalize_kernel<BF16>, a.rows, 256, 0, s, a, grid);
     return hipGetLastError();
 }
 

@@ -63,10 +63,10 @@ hipError_t launch_rmsnorm_rows_bf16(const float* x, int64_t ldx, const void* gai
                                     const int32_t* xrow, int n_xrows, uint32_t* err) {
     if (R <= 0) return hipSuccess;
     if (gt == W_BF16)
-        rmsnorm_rows_bf16_kernel<BF16><<<R, 256, 0, s>>>(x, ldx, (const uint16_t*)gain, out, out_lo, ldo, H, eps,
+        launch_kernel(rmsnorm_rows_bf16_kernel<BF16>, R, 256, 0, s, x, ldx, (const uint16_t*)gain, out, out_lo, ldo, H, eps,
                                                          xrow, n_xrows, err, clock_slot());
     else
-        rmsnorm_rows_bf16_kernel<F32><<<R, 256, 0, s>>>(x, ldx, (const float*)gain, out, out_lo, ldo, H, eps, xrow,
+        launch_kernel(rmsnorm_rows_bf16_kernel<F32>, R, 256, 0, s, x, ldx, (const float*)gain, out, out_lo, ldo, H, eps, xrow,
                                                         n_xrows, err, clock_slot());
     return hipGetLastError();
 }
@@ -90,11 +90,11 @@ hipError_t launch_qk_norm_rope_kv(const float* qkv, int64_t ldqkv, int R, WType 
     const int items = R * (q.n_heads + 2 * q.n_kv);
     const int grid = (items + 3) / 4;
     if (gt == W_BF16) {
-        if (q.kv.type == KV_F16) qk_norm_rope_kv_kernel<BF16, F16><<<grid, 256, 0, s>>>(qkv, ldqkv, R, q);
-        else qk_norm_rope_kv_kernel<BF16, F32><<<grid, 256, 0, s>>>(qkv, ldqkv, R, q);
+        if (q.kv.type == KV_F16) launch_kernel(qk_norm_rope_kv_kernel<BF16, F16>, grid, 256, 0, s, qkv, ldqkv, R, q);
+        else launch_kernel(qk_norm_rope_kv_kernel<BF16, F32>, grid, 256, 0, s, qkv, ldqkv, R, q);
     } else {
-        if (q.kv.type == KV_F16) qk_norm_rope_kv_kernel<F32, F16><<<grid, 256, 0, s>>>(qkv, ldqkv, R, q);
-        else qk_norm_rope_kv_kernel<F32, F32><<<grid, 256, 0, s>>>(qkv, ldqkv, R, q);
+        if (q.kv.type == KV_F16) launch_kernel(qk_norm_rope_kv_kernel<F32, F16>, grid, 256, 0, s, qkv, ldqkv, R, q);
+        else launch_kernel(qk_norm_rope_kv_kernel<F32, F32>, grid, 256, 0, s, qkv, ldqkv, R, q);
     }
     return hipGetLastError();
 }
@@ -128,9 +128,9 @@ hipError_t launch_embed_gather(const void* embed, WType wt, int vocab, int hidde
                                const float* keep, const float* dense, float* x, uint32_t* err, hipStream_t s) {
     if (B <= 0) return hipSuccess;
     if (wt == W_BF16)
-        embed_gather_kernel<BF16><<<B, 256, 0, s>>>((const uint16_t*)embed, vocab, hidden, ids, keep, dense, x, err);
+        launch_kernel(embed_gather_kernel<BF16>, B, 256, 0, s, (const uint16_t*)embed, vocab, hidden, ids, keep, dense, x, err);
     else
-        embed_gather_kernel<F32><<<B, 256, 0, s>>>((const float*)embed, vocab, hidden, ids, keep, dense, x, err);
+        launch_kernel(embed_gather_kernel<F32>, B, 256, 0, s, (const float*)embed, vocab, hidden, ids, keep, dense, x, err);
     return hipGetLastError();
 }
 
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void expand_segments_kernel(Segments sg, int R
 
 hipError_t launch_expand_segments(const Segments& sg, int R, int32_t* pos, int32_t* seq, hipStream_t s) {
     if (R <= 0) return hipSuccess;
-    expand_segments_kernel<<<(R + 255) / 256, 256, 0, s>>>(sg, R, pos, seq);
+    launch_kernel(expand_segments_kernel, (R + 255) / 256, 256, 0, s, sg, R, pos, seq);
     return hipGetLastError();
 }
 
@@ -196,7 +196,7 @@ hipError_t launch_greedy_stop(int B, const int32_t* ids, int eos_id, int max_new
                               int32_t* pos, int32_t* active, int32_t* n_gen, int32_t* tokens, int32_t* truncated,
                               int32_t* n_active, hipStream_t s) {
     if (B <= 0) return hipSuccess;
-    greedy_stop_kernel<<<1, 256, 0, s>>>(B, ids, eos_id, max_new, n_ctx, advance, pos, active, n_gen, tokens,
+    launch_kernel(greedy_stop_kernel, 1, 256, 0, s, B, ids, eos_id, max_new, n_ctx, advance, pos, active, n_gen, tokens,
                                           truncated, n_active);
     return hipGetLastError();
 }
@@ -215,7 +215,7 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
     size_t grid = (n16 + 255) / 256;
     if (grid > 8192) grid = 8192;
     if (grid == 0) grid = 1;
-    fill_zero_kernel<<<(unsigned)grid, 256, 0, s>>>((uint4*)p, n16, (uint8_t*)p + n16 * 16, bytes - n16 * 16);
+    launch_kernel(fill_zero_kernel, (unsigned)grid, 256, 0, s, (uint4*)p, n16, (uint8_t*)p + n16 * 16, bytes - n16 * 16);
     return hipGetLastError();
 }
 
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256) void clock_reduce_kernel(const uint64_t* __res
 
 hipError_t launch_clock_reduce(const uint64_t* slots, int n, uint64_t* out, hipStream_t s) {
     if (n <= 0) return hipSuccess;
-    clock_reduce_kernel<<<n, 256, 0, s>>>(slots, out);
+    launch_kernel(clock_reduce_kernel, n, 256, 0, s, slots, out);
     return hipGetLastError();
 }
 

@@ -384,7 +384,7 @@ hipError_t launch_step_fused(const StepFusedArgs& a, hipStream_t s) {
     ra.n_splits = a.n_splits; ra.part = a.part; ra.out_f32 = a.n_splits > 1 ? nullptr : a.attn_o;
     ra.ldo = a.n_heads * a.d; ra.err = a.err; ra.q_gain = a.q_norm; ra.k_gain = a.k_norm; ra.eps = a.eps;
     ra.rope = a.rope; ra.max_pos = a.max_pos;
-    k<<<grid, 256, 0, s>>>(a, ra, clock_slot());
+    launch_kernel(k, grid, 256, 0, s, a, ra, clock_slot());
     return hipGetLastError();
 }
 

@@ -1,10 +1,40 @@
 // launch.h - host-side launchers of the gfx950 kernels (internal to libsttd).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace sttd {
+
+// Per-kernel event timing (sttd_profile_enable): while a timed kernel family's
+// eager call is being issued, each of its launches takes a start/stop event pair
+// (true) that hipExtLaunchKernel binds to the dispatch itself, so the pair times
+// that kernel alone (dispatch to completion), not the gaps around it.
+bool next_launch_events(hipEvent_t* start, hipEvent_t* stop);
+
+template <typename Tup, size_t... I>
+inline void tuple_addresses(Tup& t, void** out, std::index_sequence<I...>) {
+    ((out[I] = (void*)&std::get<I>(t)), ...);
+}
+
+// kernel<<<grid, block, shmem, s>>>(args...), with the event pair above when timed.
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+                          Args&&... args) {
+    hipEvent_t start = nullptr, stop = nullptr;
+    if (next_launch_events(&start, &stop)) {
+        std::tuple<KArgs...> t(std::forward<Args>(args)...);
+        void* argv[sizeof...(KArgs)];
+        tuple_addresses(t, argv, std::index_sequence_for<KArgs...>{});
+        (void)hipExtLaunchKernel((const void*)kernel, grid, block, argv, shmem, s, start, stop, 0);
+        return;
+    }
+    kernel<<<grid, block, shmem, s>>>(std::forward<Args>(args)...);
+}
 
 // Device-clock slot: kClockEntries (start, end) pairs, one per workgroup id;
 // ids from kClockBank1 up belong to a second kernel launched under the slot.
