@@ -235,19 +235,28 @@ __device__ __forceinline__ int big_lds_off(int r, int c) { return r * BIG_BK + (
 // grid, copy s taking the s-th part of K and adding its partial sums into C
 // (which already holds the residual) with fp32 atomics. Copies follow one
 // another in the grid, so each keeps the XCD-aware tile order.
-template <int EPI, int BN, int KSPLIT = 1>
-__global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+#ifndef STTD_BIG_WM
+#define STTD_BIG_WM 4
+#endif
+// WM: waves along M (4: 8 waves of 64 x BN/2; 2: 4 waves of 128 x BN/2, one per
+// SIMD, with the accumulators in AGPRs). One wave per SIMD reads a third less LDS
+// per MFMA but measured much slower at 4096 rows (gate_up 189 -> 284 us, down
+// 113 -> 175 us): a single wave cannot hide its LDS and global latency.
+template <int EPI, int BN, int KSPLIT = 1, int WM = STTD_BIG_WM>
+__global__ __launch_bounds__(WM * 128) void gemm_big_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     static_assert(EPI != GEMM_SWIGLU || BN == BIG_BN, "SwiGLU pairs gate and up inside 256-row weight tiles");
     static_assert(KSPLIT == 1 || EPI == GEMM_RESID, "split K adds into a residual");
-    constexpr int FM = 4, FN = BN / 32;
-    constexpr int VECS = BIG_BM * BIG_BK / 8 / 512;  // 16-byte vectors per thread and step: A
-    constexpr int BVECS = BN * BIG_BK / 8 / 512;     // and B
+    constexpr int NT = WM * 128;                     // threads
+    constexpr int WR = BIG_BM / WM;                  // rows per wave
+    constexpr int FM = WR / 16, FN = BN / 32;
+    constexpr int VECS = BIG_BM * BIG_BK / 8 / NT;   // 16-byte vectors per thread and step: A
+    constexpr int BVECS = BN * BIG_BK / 8 / NT;      // and B
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BIG_BM * BIG_STR];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BIG_STR];
 
     clock_begin(g.clk);
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
-    const int wm = wave / 2, wn = wave % 2;  // 4 x 2 waves, each 64 x 128
+    const int wm = wave / 2, wn = wave % 2;  // WM x 2 waves, each WR x BN / 2
     // XCD-aware tile order when the tile count splits evenly over the 8 XCDs
     const int n_tiles = tiles_m * tiles_n;
     const int id = KSPLIT > 1 ? (int)blockIdx.x % n_tiles : (int)blockIdx.x;
@@ -262,14 +271,14 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
     bool bok[BVECS];
 #pragma unroll
     for (int i = 0; i < VECS; ++i) {
-        const int v = tid + i * 512;
+        const int v = tid + i * NT;
         const int r = v / (BIG_BK / 8), ck = (v % (BIG_BK / 8)) * 8;
         const int am = m0 + r < g.M ? m0 + r : 0;
         aptr[i] = g.A + (int64_t)am * g.lda + k_begin + ck;
     }
 #pragma unroll
     for (int i = 0; i < BVECS; ++i) {
-        const int v = tid + i * 512;
+        const int v = tid + i * NT;
         const int r = v / (BIG_BK / 8), ck = (v % (BIG_BK / 8)) * 8;
         int grow;
         const uint16_t* W;
@@ -300,7 +309,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
     auto stash = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < VECS; ++i) {
-            const int v = tid + i * 512;
+            const int v = tid + i * NT;
             const int o = big_lds_off(v / (BIG_BK / 8), v % (BIG_BK / 8));
             *reinterpret_cast<u32x4*>(&As[buf][o]) = areg[i];
             if (i < BVECS) *reinterpret_cast<u32x4*>(&Bs[buf][o]) = breg[i < BVECS ? i : 0];
@@ -328,7 +337,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
             bf16x8 af[FM], bfr[FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(&Ab[big_lds_off(wm * 64 + i * 16 + lane % 16, kc / 8)]);
+                af[i] = *reinterpret_cast<const bf16x8*>(&Ab[big_lds_off(wm * WR + i * 16 + lane % 16, kc / 8)]);
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 bfr[j] = *reinterpret_cast<const bf16x8*>(&Bb[big_lds_off(wn * (BN / 2) + j * 16 + lane % 16, kc / 8)]);
@@ -371,7 +380,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
             float2 cs[4][FN / 2];
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const int m = m0 + wm * 64 + i * 16 + (lane / 16) * 4 + rr;
+                const int m = m0 + wm * WR + i * 16 + (lane / 16) * 4 + rr;
                 const int mc = m < g.M ? m : g.M - 1;
                 pos[rr] = row_pos(q.rm, mc);
                 seq[rr] = row_seq(q.rm, mc);
@@ -385,7 +394,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
                     cs[rr][j] = is_v ? float2{1.f, 0.f} : table[(int64_t)(ok[rr] ? pos[rr] : 0) * 64 + j * 16 + c0];
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const int m = m0 + wm * 64 + i * 16 + (lane / 16) * 4 + rr;
+                const int m = m0 + wm * WR + i * 16 + (lane / 16) * 4 + rr;
                 if (!ok[rr]) {  // the same for the 16 lanes of a DPP row (one row m)
                     if (m < g.M && c0 == 0 && wn == 0)
                         record_error(q.err, pos[rr] < 0 || pos[rr] >= q.kv.n_ctx ? 1u : 2u);
@@ -429,7 +438,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_m, 
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-            const int m = m0 + wm * 64 + i * 16 + (lane / 16) * 4 + rr;
+            const int m = m0 + wm * WR + i * 16 + (lane / 16) * 4 + rr;
             if (m >= g.M) continue;
             if (EPI == GEMM_SWIGLU) {
 #pragma unroll
@@ -474,12 +483,12 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     const int tiles_m = (g.M + BIG_BM - 1) / BIG_BM;
     if (epi == GEMM_SWIGLU) {
         const int tiles_n = g.N / 128;
-        launch_kernel(gemm_big_kernel<GEMM_SWIGLU, BIG_BN>, tiles_m * tiles_n, 512, 0, s, g, tiles_m, tiles_n);
+        launch_kernel(gemm_big_kernel<GEMM_SWIGLU, BIG_BN>, tiles_m * tiles_n, STTD_BIG_WM * 128, 0, s, g, tiles_m, tiles_n);
         return;
     }
     if (epi == GEMM_QKROPE) {
         const int tiles_n = g.N / BIG_BN;
-        launch_kernel(gemm_big_kernel<GEMM_QKROPE, BIG_BN>, tiles_m * tiles_n, 512, 0, s, g, tiles_m, tiles_n);
+        launch_kernel(gemm_big_kernel<GEMM_QKROPE, BIG_BN>, tiles_m * tiles_n, STTD_BIG_WM * 128, 0, s, g, tiles_m, tiles_n);
         return;
     }
     // residual outputs too narrow to fill the CUs even with 256 x 128 tiles: two
@@ -491,7 +500,7 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     const int tiles128 = tiles_m * ((g.N + 127) / 128);
     if (epi == GEMM_RESID && tiles128 < 256 && tiles256 % 8 == 0 && (g.K / BIG_BK) % 2 == 0 &&
         g.K / BIG_BK >= 16) {
-        launch_kernel(gemm_big_kernel<GEMM_RESID, BIG_BN, 2>, tiles256 * 2, 512, 0, s, g, tiles_m, (g.N + BIG_BN - 1) / BIG_BN);
+        launch_kernel(gemm_big_kernel<GEMM_RESID, BIG_BN, 2>, tiles256 * 2, STTD_BIG_WM * 128, 0, s, g, tiles_m, (g.N + BIG_BN - 1) / BIG_BN);
         return;
     }
     // narrow outputs: 128-column tiles so that about a full wave of workgroups runs
@@ -500,11 +509,11 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     const int tiles_n = (g.N + bn - 1) / bn;
     const int grid = tiles_m * tiles_n;
     if (epi == GEMM_RESID) {
-        if (narrow) launch_kernel(gemm_big_kernel<GEMM_RESID, 128>, grid, 512, 0, s, g, tiles_m, tiles_n);
-        else launch_kernel(gemm_big_kernel<GEMM_RESID, BIG_BN>, grid, 512, 0, s, g, tiles_m, tiles_n);
+        if (narrow) launch_kernel(gemm_big_kernel<GEMM_RESID, 128>, grid, STTD_BIG_WM * 128, 0, s, g, tiles_m, tiles_n);
+        else launch_kernel(gemm_big_kernel<GEMM_RESID, BIG_BN>, grid, STTD_BIG_WM * 128, 0, s, g, tiles_m, tiles_n);
     } else {
-        if (narrow) launch_kernel(gemm_big_kernel<GEMM_STORE, 128>, grid, 512, 0, s, g, tiles_m, tiles_n);
-        else launch_kernel(gemm_big_kernel<GEMM_STORE, BIG_BN>, grid, 512, 0, s, g, tiles_m, tiles_n);
+        if (narrow) launch_kernel(gemm_big_kernel<GEMM_STORE, 128>, grid, STTD_BIG_WM * 128, 0, s, g, tiles_m, tiles_n);
+        else launch_kernel(gemm_big_kernel<GEMM_STORE, BIG_BN>, grid, STTD_BIG_WM * 128, 0, s, g, tiles_m, tiles_n);
     }
 }
 
