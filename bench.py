@@ -32,10 +32,14 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by a plain
 # 256 MiB copy (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0); valid only for the kernel
 # sources they were taken on (sha256 of the listed files).
+_GEMV_SRC = {"files": ["kernels_gemv.hip", "gemv_ops.h", "common.h"],
+             "sha256": "5c3f3a0eb495645108d3801ab9343f144ba3e5351713a47653d76b1f5ddb349c",
+             "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
 TRAFFIC = {
-    "gateup_gemv": {"rows": 1, "bytes": 50580036, "files": ["kernels_gemv.hip", "gemv_ops.h", "common.h"],
-                    "sha256": "716424a91ac18102635aa5b31b78e1a3669ec1120db258d2d5b2e095f18df6a6",
-                    "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"},
+    "qkv_gemv": dict(_GEMV_SRC, rows=1, bytes=16958604),
+    "o_gemv": dict(_GEMV_SRC, rows=1, bytes=8676391),
+    "gateup_gemv": dict(_GEMV_SRC, rows=1, bytes=50579421),
+    "down_gemv": dict(_GEMV_SRC, rows=1, bytes=25509195),
 }
 
 
@@ -389,7 +393,7 @@ def bench_greedy_stack(args, wl):
         res["kernels"] = {"prefill": kernel_table(pre, sh, rows, lambda n: T, pre_ev),
                           "decode": kernel_table(dec, sh, lambda n: 1, lambda n: T + 1 + reps / 2.0, dec_ev)}
         res["kernel_timing"] = ("avg_us: device clock (s_memrealtime, 100 MHz), first-workgroup start to "
-                                "last-workgroup end; event_avg_us: HIP event pair around each eager launch")
+                                "last-workgroup end; event_avg_us: HIP event pair bound to each eager dispatch (hipExtLaunchKernel)")
         res["roofline"] = job_roofline([("prefill", res["kernels"]["prefill"], pre_ev, 1.0, rows),
                                         ("decode", res["kernels"]["decode"], dec_ev, n_steps / reps,
                                          lambda n: 1)])
@@ -513,7 +517,7 @@ def bench_packed_prefill(args, wl):
             T if n == "attn_prefill" else Bn)
         res["kernels"] = {"prefill": kernel_table(prof, sh, rws, lambda n: T, ev)}
         res["kernel_timing"] = ("avg_us: device clock (s_memrealtime, 100 MHz), first-workgroup start to "
-                                "last-workgroup end; event_avg_us: HIP event pair around each eager launch")
+                                "last-workgroup end; event_avg_us: HIP event pair bound to each eager dispatch (hipExtLaunchKernel)")
         res["roofline"] = job_roofline([("prefill", res["kernels"]["prefill"], ev, 1.0, rws)])
     if not args.no_cpu_baseline:
         import oracle as O
@@ -665,7 +669,7 @@ def bench_block(args, wl):
         res["kernels"] = {"prefill": kernel_table(pre, sh, rw, lambda n: T, pre_ev),
                           "decode": kernel_table(dec, sh, lambda n: 1, lambda n: T + (n_prof + 1) / 2.0, dec_ev)}
         res["kernel_timing"] = ("avg_us: device clock (s_memrealtime, 100 MHz), first-workgroup start to "
-                                "last-workgroup end; event_avg_us: HIP event pair around each eager launch")
+                                "last-workgroup end; event_avg_us: HIP event pair bound to each eager dispatch (hipExtLaunchKernel)")
         res["roofline"] = job_roofline([("prefill", res["kernels"]["prefill"], pre_ev, 1.0, rw),
                                         ("decode", res["kernels"]["decode"], dec_ev, n_steps / n_prof,
                                          lambda n: 1)])
@@ -785,7 +789,7 @@ def bench_batched(args, wl):
         table = kernel_table(dec, sh, lambda n: Bn, lambda n: float(lens.mean()) + (reps + 1) / 2.0, ev)
         res["kernels"] = {"decode": table}
         res["kernel_timing"] = ("avg_us: device clock (s_memrealtime, 100 MHz), first-workgroup start to "
-                                "last-workgroup end; event_avg_us: HIP event pair around each eager launch")
+                                "last-workgroup end; event_avg_us: HIP event pair bound to each eager dispatch (hipExtLaunchKernel)")
         res["roofline"] = job_roofline([("decode", table, ev, n_steps / reps, lambda n: Bn)])
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_batched(wl, layers, E, g, lens)
