@@ -273,11 +273,13 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
     qr.rm = rm; qr.kv = kl; qr.q_out = ws->qbuf; qr.q_f16 = flash; qr.ldq = qd; qr.err = ws->err;
     qr.n_heads = nq; qr.n_kv = nkv; qr.d = d;
     if (mfma) {
-        {
+        GemmArgs g{};
+        if (gemm_fuses_norm(R, H)) {  // few rows: the projection norms them itself
+            g.X = x; g.ldx = H; g.gain = (const uint16_t*)w->attn_norm; g.eps = eps; g.x_lo = xn_lo != nullptr;
+        } else {
             ProfScope ps(STTD_KERN_RMSNORM, s);
             TRY(launch_rmsnorm_rows_bf16(x, H, w->attn_norm, wt, ws->xn, xn_lo, H, R, H, eps, s));
         }
-        GemmArgs g{};
         g.A = ws->xn; g.A_lo = xn_lo; g.lda = H; g.M = R; g.K = H;
         g.w[0] = (const uint16_t*)w->wq; g.w[1] = (const uint16_t*)w->wk; g.w[2] = (const uint16_t*)w->wv;
         g.seg_end[0] = qd; g.seg_end[1] = qd + kvd; g.seg_end[2] = qkv_cols;
@@ -363,11 +365,13 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
     const int nr = last_row_only ? 1 : R;
     float* xf = x + (int64_t)r0 * H;
     if (mfma && nr > kGemvMaxRows) {
-        {
+        GemmArgs g{};
+        if (gemm_fuses_norm(nr, H)) {
+            g.X = xf; g.ldx = H; g.gain = (const uint16_t*)w->ffn_norm; g.eps = eps; g.x_lo = ffn_lo != nullptr;
+        } else {
             ProfScope ps(STTD_KERN_RMSNORM, s);
             TRY(launch_rmsnorm_rows_bf16(xf, H, w->ffn_norm, wt, ws->xn, ffn_lo, H, nr, H, eps, s));
         }
-        GemmArgs g{};
         g.A = ws->xn; g.A_lo = ffn_lo; g.lda = H; g.M = nr; g.K = H;
         g.w[0] = (const uint16_t*)w->w_gate_up; g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = 2 * I;
         g.N = I; g.Cb = act; g.Cb_lo = act_lo; g.ldcb = I;

@@ -149,6 +149,9 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
 // 8g + j holds key 4g + j (j < 4) or 16 + 4g + j - 4 (j >= 4). K and V^T are
 // double-buffered in LDS; the next block's rows load while the current one
 // computes. Exponentials in base 2 on scores scaled by log2(e) / sqrt(d).
+#ifndef STTD_FLASH_VSWZ
+#define STTD_FLASH_VSWZ 0
+#endif
 constexpr float kLazy = 8.f;  // lazy-rescale threshold of the flash kernel (base-2 exponent)
 
 template <int D>
@@ -169,6 +172,13 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
     __shared__ float ml[2][RF][256];
     // element offset of 16-byte chunk c of an LDS row r of `stride` elements
     auto swz = [](int r, int c, int stride) { return r * stride + ((c ^ (r & 7)) * 8); };
+    // V rows: a transpose read takes two chunks from each of 4 consecutive rows per
+    // 16 lanes; with STTD_FLASH_VSWZ rows are XOR-ed by 2r, which in a 32- or 64-bank
+    // model of LDS sends those 8 chunks (and the other 16-lane groups' rows) to
+    // distinct banks for 256-byte rows
+    auto swzv = [](int r, int c, int stride) {
+        return r * stride + ((c ^ (STTD_FLASH_VSWZ && D >= 128 ? (2 * r) & (D / 8 - 1) : r & 7)) * 8);
+    };
 
     clock_begin(clk);
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
@@ -244,9 +254,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
 #pragma unroll
             for (int i = 0; i < KVECS; ++i) {
                 const int v = tid + i * NT;
-                const int o = swz(v / (D / 8), v % (D / 8), KS);
-                *reinterpret_cast<u32x4*>(&Ks[buf][o]) = kreg[i];
-                *reinterpret_cast<u32x4*>(&Vs[buf][o]) = vreg[i];
+                *reinterpret_cast<u32x4*>(&Ks[buf][swz(v / (D / 8), v % (D / 8), KS)]) = kreg[i];
+                *reinterpret_cast<u32x4*>(&Vs[buf][swzv(v / (D / 8), v % (D / 8), KS)]) = vreg[i];
             }
         };
         // V^T fragment (A operand) of dims 16 df .. 16 df + 15 over the key group's 32
@@ -259,7 +268,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
         // gives the same lane in the P^T B operand.
         auto vt_frag = [&](int buf, int df) {
             const int row = kg * 32 + 4 * g4 + r16 / 4, dim = df * 16 + 4 * (r16 % 4);
-            const int o0 = swz(row, dim / 8, KS) + dim % 8, o1 = swz(row + 16, dim / 8, KS) + dim % 8;
+            const int o0 = swzv(row, dim / 8, KS) + dim % 8, o1 = swzv(row + 16, dim / 8, KS) + dim % 8;
             typedef short s16x4 __attribute__((ext_vector_type(4)));
             typedef short s16x8 __attribute__((ext_vector_type(8)));
             const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(

@@ -526,7 +526,11 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
 // l % 16, K elements (l / 16) * 8 .. + 8), so every weight byte is read once;
 // the few activation rows (bf16 high and low parts) are the A fragments,
 // re-read from L2 by every workgroup. Loads run PD K-steps ahead.
-template <int EPI, int RF, int CF>
+// NORM: the rows' RMSNorm is done here (STORE and SWIGLU, whose workgroups each
+// cover all of K): the A fragments are the fp32 rows times the gain, split into
+// bf16 high + low parts in registers, the sums of squares come from the same
+// loads, and the outputs are scaled by each row's 1 / rms.
+template <int EPI, int RF, int CF, bool NORM>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     // K-steps of 32 per load batch (8, in flight twice the bytes, measured slower
     // at 16 rows: gate_up 17.4 -> 18.0 us, down 10.8 -> 11.7 us; two alternating
@@ -534,6 +538,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     // QKV 7.6 -> 9.0 us, down 10.8 -> 13.0 us, from the higher register count)
     constexpr int PD = 4;
     __shared__ float red[4][RF * 16][CF * 16 + 1];
+    __shared__ float ssred[NORM ? 4 : 1][RF * 16];
     clock_begin(g.clk);
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
     const int ct = blockIdx.x;
@@ -559,13 +564,21 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     }
     const uint16_t* arow[RF];
     const uint16_t* alrow[RF];
+    const float* xrow[RF];
 #pragma unroll
     for (int r = 0; r < RF; ++r) {
         const int m = min(r * 16 + lane % 16, g.M - 1);
-        arow[r] = g.A + (int64_t)m * g.lda;
-        alrow[r] = (g.A_lo ? g.A_lo : g.A) + (int64_t)m * g.lda;
+        if (NORM) {
+            xrow[r] = g.X + (int64_t)m * g.ldx;
+        } else {
+            arow[r] = g.A + (int64_t)m * g.lda;
+            alrow[r] = (g.A_lo ? g.A_lo : g.A) + (int64_t)m * g.lda;
+        }
     }
-    const bool lo = g.A_lo != nullptr;
+    const bool lo = NORM ? g.x_lo : g.A_lo != nullptr;
+    float ss[RF];
+#pragma unroll
+    for (int r = 0; r < RF; ++r) ss[r] = 0.f;
     // this wave's K-steps: [s0, s1) of K / 32
     const int n_steps = g.K / 32;
     const int parts = gridDim.y * 4;
@@ -580,7 +593,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
         for (int f = 0; f < CF; ++f) acc[r][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 wb[PD][CF], ab[PD][RF], alb[PD][RF];
+    u32x4 wb[PD][CF], ab[PD][RF], alb[PD][RF], gb[PD];
+    f32x4 xa[PD][RF], xb[PD][RF];
     for (int s = s0; s < s1; s += PD) {
         // a batch of PD steps (clamped reads past s1 are loaded but not used)
 #pragma unroll
@@ -588,15 +602,45 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
             const int k = min(s + p, n_steps - 1) * 32 + koff;
 #pragma unroll
             for (int f = 0; f < CF; ++f) wb[p][f] = *reinterpret_cast<const u32x4*>(wrow[f] + k);
+            if (NORM) {
+                gb[p] = *reinterpret_cast<const u32x4*>(g.gain + k);
 #pragma unroll
-            for (int r = 0; r < RF; ++r) {
-                ab[p][r] = *reinterpret_cast<const u32x4*>(arow[r] + k);
-                if (lo) alb[p][r] = *reinterpret_cast<const u32x4*>(alrow[r] + k);
+                for (int r = 0; r < RF; ++r) {
+                    xa[p][r] = *reinterpret_cast<const f32x4*>(xrow[r] + k);
+                    xb[p][r] = *reinterpret_cast<const f32x4*>(xrow[r] + k + 4);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < RF; ++r) {
+                    ab[p][r] = *reinterpret_cast<const u32x4*>(arow[r] + k);
+                    if (lo) alb[p][r] = *reinterpret_cast<const u32x4*>(alrow[r] + k);
+                }
             }
         }
 #pragma unroll
         for (int p = 0; p < PD; ++p) {
             if (s + p >= s1) break;
+            if (NORM) {  // x * gain as bf16 high + low parts; x^2 into the row's sum
+                const uint32_t gw[4] = {gb[p].x, gb[p].y, gb[p].z, gb[p].w};
+#pragma unroll
+                for (int r = 0; r < RF; ++r) {
+                    const float xv[8] = {xa[p][r].x, xa[p][r].y, xa[p][r].z, xa[p][r].w,
+                                         xb[p][r].x, xb[p][r].y, xb[p][r].z, xb[p][r].w};
+                    uint32_t hw[4], lw[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        ss[r] = fmaf(xv[2 * i], xv[2 * i], ss[r]);
+                        ss[r] = fmaf(xv[2 * i + 1], xv[2 * i + 1], ss[r]);
+                        uint16_t h0, l0, h1, l1;
+                        split_bf16(xv[2 * i] * __uint_as_float(gw[i] << 16), h0, l0);
+                        split_bf16(xv[2 * i + 1] * __uint_as_float(gw[i] & 0xFFFF0000u), h1, l1);
+                        hw[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                        lw[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+                    }
+                    ab[p][r] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+                    alb[p][r] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+                }
+            }
 #pragma unroll
             for (int r = 0; r < RF; ++r)
 #pragma unroll
@@ -610,26 +654,40 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
                 }
         }
     }
-    // merge the 4 waves' K shares
+    // merge the 4 waves' K shares (and the rows' sums of squares: lanes l, l + 16,
+    // l + 32, l + 48 hold row l % 16's)
 #pragma unroll
     for (int r = 0; r < RF; ++r)
 #pragma unroll
         for (int f = 0; f < CF; ++f)
 #pragma unroll
             for (int i = 0; i < 4; ++i) red[wave][r * 16 + (lane / 16) * 4 + i][f * 16 + lane % 16] = acc[r][f][i];
+    if (NORM) {
+#pragma unroll
+        for (int r = 0; r < RF; ++r) {
+            float t = ss[r] + xor16(ss[r]);
+            t += xor32(t);
+            if (lane < 16) ssred[wave][r * 16 + lane] = t;
+        }
+    }
     __syncthreads();
     constexpr int OUTS = RF * 16 * CF * 16;
     for (int o = tid; o < OUTS; o += 256) {
         const int row = o / (CF * 16), col = o % (CF * 16);
         if (row >= g.M) continue;
-        const float v = red[0][row][col] + red[1][row][col] + red[2][row][col] + red[3][row][col];
+        float v = red[0][row][col] + red[1][row][col] + red[2][row][col] + red[3][row][col];
+        float rs = 1.f;
+        if (NORM) {
+            rs = 1.0f / sqrtf((ssred[0][row] + ssred[1][row] + ssred[2][row] + ssred[3][row]) / (float)g.K + g.eps);
+            v *= rs;
+        }
         if (EPI == GEMM_SWIGLU) {
             constexpr int GC = CF / 2 * 16;  // gate columns of the tile; the up ones follow
             if (col >= GC) continue;  // the up half is read with its gate
             const int c = ct * GC + col;
             if (c >= g.N) continue;
-            const float up = red[0][row][col + GC] + red[1][row][col + GC] + red[2][row][col + GC] +
-                             red[3][row][col + GC];
+            const float up = (red[0][row][col + GC] + red[1][row][col + GC] + red[2][row][col + GC] +
+                              red[3][row][col + GC]) * rs;
             const float a = v / (1.0f + expf(-v)) * up;
             uint16_t hi, lo16;
             split_bf16(a, hi, lo16);
@@ -647,6 +705,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     clock_end(g.clk);
 }
 
+#ifndef STTD_SKINNY_RESID_WGS
+#define STTD_SKINNY_RESID_WGS 256
+#endif
+
 // Rows a skinny launch takes (16 per row fragment, up to 4 fragments).
 #ifndef STTD_SKINNY_MAX_ROWS
 constexpr int kSkinnyMaxRows = 64;
@@ -654,24 +716,26 @@ constexpr int kSkinnyMaxRows = 64;
 constexpr int kSkinnyMaxRows = STTD_SKINNY_MAX_ROWS;
 #endif
 
-template <int EPI, int CF>
+template <int EPI, int CF, bool NORM = false>
 static void launch_skinny_rf(const GemmArgs& g, dim3 grid, hipStream_t s) {
-    if (g.M <= 16) launch_kernel(gemm_skinny_kernel<EPI, 1, CF>, grid, 256, 0, s, g);
-    else if (g.M <= 32) launch_kernel(gemm_skinny_kernel<EPI, 2, CF>, grid, 256, 0, s, g);
-    else launch_kernel(gemm_skinny_kernel<EPI, 4, CF>, grid, 256, 0, s, g);
+    if (g.M <= 16) launch_kernel(gemm_skinny_kernel<EPI, 1, CF, NORM>, grid, 256, 0, s, g);
+    else if (g.M <= 32) launch_kernel(gemm_skinny_kernel<EPI, 2, CF, NORM>, grid, 256, 0, s, g);
+    else launch_kernel(gemm_skinny_kernel<EPI, 4, CF, NORM>, grid, 256, 0, s, g);
 }
 
 static void launch_gemm_skinny(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     if (epi == GEMM_SWIGLU) {
-        launch_skinny_rf<GEMM_SWIGLU, 4>(g, dim3((g.N + 31) / 32, 1), s);
+        if (g.X) launch_skinny_rf<GEMM_SWIGLU, 4, true>(g, dim3((g.N + 31) / 32, 1), s);
+        else launch_skinny_rf<GEMM_SWIGLU, 4>(g, dim3((g.N + 31) / 32, 1), s);
         return;
     }
     const int tiles = (g.N + 15) / 16;
     // RESID may split K over workgroups (atomic adds) until about 256 workgroups run
     int ks = 1;
     if (epi == GEMM_RESID)
-        while (tiles * ks * 2 <= 256 && g.K / 32 >= ks * 2 * 4 * 4) ks *= 2;
+        while (tiles * ks * 2 <= STTD_SKINNY_RESID_WGS && g.K / 32 >= ks * 2 * 4 * 4) ks *= 2;
     if (epi == GEMM_RESID) launch_skinny_rf<GEMM_RESID, 1>(g, dim3(tiles, ks), s);
+    else if (g.X) launch_skinny_rf<GEMM_STORE, 1, true>(g, dim3(tiles, 1), s);
     else launch_skinny_rf<GEMM_STORE, 1>(g, dim3(tiles, 1), s);
 }
 
@@ -714,11 +778,15 @@ static hipError_t launch_gemm_t(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     return launch_gemm_bm<64, SPLIT>(g, epi, s);
 }
 
+bool gemm_fuses_norm(int M, int K) { return M <= kSkinnyMaxRows && K % 32 == 0; }
+
 hipError_t launch_gemm(const GemmArgs& args, GemmEpi epi, hipStream_t s) {
     if (args.M <= 0) return hipSuccess;
     GemmArgs g = args;
     g.clk = clock_slot();
     if (epi == GEMM_QKROPE && !big_tiles_fit(g, epi)) return hipErrorInvalidValue;
+    // the fused RMSNorm: STORE / SWIGLU on the few-row path only
+    if (g.X && (epi == GEMM_RESID || epi == GEMM_QKROPE || !gemm_fuses_norm(g.M, g.K))) return hipErrorInvalidValue;
     if (g.M <= kSkinnyMaxRows && g.K % 32 == 0) launch_gemm_skinny(g, epi, s);
     else if (big_tiles_fit(g, epi)) launch_gemm_big(g, epi, s);
     else if (g.A_lo) {

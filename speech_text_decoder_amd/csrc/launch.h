@@ -196,9 +196,20 @@ struct GemmArgs {
     uint16_t* Cb_lo;     // optional low half of the SWIGLU output
     int64_t ldcb;
     QkRope qk;           // GEMM_QKROPE: gains, table, row map, cache and q output (q_f16)
+    // RMSNorm in front (STORE / SWIGLU on few rows, see gemm_fuses_norm): with X set,
+    // A / A_lo are not read; the operand is X (fp32, ldx) times gain, split into bf16
+    // high + low parts when x_lo, and each output row is scaled by 1 / rms of its X row
+    const float* X;
+    int64_t ldx;
+    const uint16_t* gain;
+    float eps;
+    bool x_lo;
     uint64_t* clk;
 };
 hipError_t launch_gemm(const GemmArgs& g, GemmEpi epi, hipStream_t s);
+// Whether launch_gemm takes the RMSNorm of X itself (GemmArgs::X) for M rows over K:
+// the few-row weight-stationary path. Otherwise the caller norms the rows first.
+bool gemm_fuses_norm(int M, int K);
 // Whether launch_gemm takes GEMM_QKROPE for this shape: at least 1024 rows,
 // head_dim 128, and enough 256 x 256 tiles to fill the CUs.
 bool gemm_qkrope_fits(int M, int N, int K, int head_dim);
