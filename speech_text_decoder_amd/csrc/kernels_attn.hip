@@ -149,9 +149,6 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
 // 8g + j holds key 4g + j (j < 4) or 16 + 4g + j - 4 (j >= 4). K and V^T are
 // double-buffered in LDS; the next block's rows load while the current one
 // computes. Exponentials in base 2 on scores scaled by log2(e) / sqrt(d).
-#ifndef STTD_FLASH_VSWZ
-#define STTD_FLASH_VSWZ 0
-#endif
 constexpr float kLazy = 8.f;  // lazy-rescale threshold of the flash kernel (base-2 exponent)
 
 template <int D>
@@ -172,13 +169,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
     __shared__ float ml[2][RF][256];
     // element offset of 16-byte chunk c of an LDS row r of `stride` elements
     auto swz = [](int r, int c, int stride) { return r * stride + ((c ^ (r & 7)) * 8); };
-    // V rows: a transpose read takes two chunks from each of 4 consecutive rows per
-    // 16 lanes; with STTD_FLASH_VSWZ rows are XOR-ed by 2r, which in a 32- or 64-bank
-    // model of LDS sends those 8 chunks (and the other 16-lane groups' rows) to
-    // distinct banks for 256-byte rows
-    auto swzv = [](int r, int c, int stride) {
-        return r * stride + ((c ^ (STTD_FLASH_VSWZ && D >= 128 ? (2 * r) & (D / 8 - 1) : r & 7)) * 8);
-    };
+
 
     clock_begin(clk);
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
@@ -255,7 +246,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
             for (int i = 0; i < KVECS; ++i) {
                 const int v = tid + i * NT;
                 *reinterpret_cast<u32x4*>(&Ks[buf][swz(v / (D / 8), v % (D / 8), KS)]) = kreg[i];
-                *reinterpret_cast<u32x4*>(&Vs[buf][swzv(v / (D / 8), v % (D / 8), KS)]) = vreg[i];
+                *reinterpret_cast<u32x4*>(&Vs[buf][swz(v / (D / 8), v % (D / 8), KS)]) = vreg[i];
             }
         };
         // V^T fragment (A operand) of dims 16 df .. 16 df + 15 over the key group's 32
@@ -265,10 +256,12 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
         // the device). Lane (g4, r16) hands in key row 4 g4 + r16 / 4 (then + 16) at
         // dims 16 df + 4 (r16 % 4) .. + 3, so it receives dim 16 df + r16 of keys
         // 4 g4 .. 4 g4 + 3 and 16 + 4 g4 .. 16 + 4 g4 + 3: the keys the S^T fragment
-        // gives the same lane in the P^T B operand.
+        // gives the same lane in the P^T B operand. (V rows XOR-swizzled by 2r instead
+        // of r, which spreads these reads over distinct banks in a 32- or 64-bank
+        // model, measured no faster at 4096 rows: 108-109 against 104-107 us.)
         auto vt_frag = [&](int buf, int df) {
             const int row = kg * 32 + 4 * g4 + r16 / 4, dim = df * 16 + 4 * (r16 % 4);
-            const int o0 = swzv(row, dim / 8, KS) + dim % 8, o1 = swzv(row + 16, dim / 8, KS) + dim % 8;
+            const int o0 = swz(row, dim / 8, KS) + dim % 8, o1 = swz(row + 16, dim / 8, KS) + dim % 8;
             typedef short s16x4 __attribute__((ext_vector_type(4)));
             typedef short s16x8 __attribute__((ext_vector_type(8)));
             const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(

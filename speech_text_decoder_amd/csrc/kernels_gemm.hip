@@ -705,6 +705,11 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     clock_end(g.clk);
 }
 
+// Grid bound of few-row RESID launches that split K (atomic adds). At 16 rows,
+// 512 and 1024 measured slower (down 12.3 -> 12.8 and 15.8 us): every split adds
+// rows x N atomics. Splitting the K of STORE and SWIGLU launches too, with the
+// column tile's last workgroup merging the published partials, measured slower at
+// 384-1024 workgroups (gate_up 18.0 -> 23.8-25.7 us, QKV 8.2 -> 10.4-11.2 us).
 #ifndef STTD_SKINNY_RESID_WGS
 #define STTD_SKINNY_RESID_WGS 256
 #endif
