@@ -160,7 +160,8 @@ sttd_status sttd_workspace_free(sttd_workspace *ws);
  * SwiGLU output). Measured on the 28-block 1.7B-shaped stack (8 packed
  * prompts of 153 rows, 1224 rows per call) against the fp64 oracle: with all
  * four plain the final logits move by 11% of their RMS, beyond the 3e-2
- * bound on hidden states; all four split, 1.2%; any one plain, 4% or more.
+ * bound on hidden states; all four split, 1.2%; only the attention output or
+ * only the Q|K|V input plain, 4.2% and 7.1%.
  * One block stays within the bound with all four plain (its 4096-row parity
  * test), so a caller running a single block or a shallow stack may set 0 to
  * halve the MFMA work of long prefills. */
@@ -169,6 +170,18 @@ sttd_status sttd_workspace_free(sttd_workspace *ws);
 #define STTD_SPLIT_O 2
 #define STTD_SPLIT_GATE_UP 4
 #define STTD_SPLIT_DOWN 8
+/* STTD_OPT_QKV_ATTN, default 1: a single-row block_step with bf16 weights, an
+ * f16 cache, head_dim 128, groups of 1 or 2 query heads per KV head, hidden up
+ * to 4096 and attention splits of at most 128 cache rows runs its Q|K|V
+ * projection and its attention as one launch: the projection's workgroups
+ * publish each column as a 64-bit word tagged with a per-launch number, and
+ * the attention workgroups, which start with them, fetch their cache rows and
+ * then poll their head's words (a poll gives up after 200 ms and records
+ * STTD_DEVERR_SYNC). The arithmetic is that of the two-launch form (value
+ * 0): from the same cache state the results are bit-identical. Measured on
+ * the 28-block 1.7B-shaped greedy job: 1.077 -> 1.066 ms per token. Calls
+ * that share a workspace must not run concurrently. */
+#define STTD_OPT_QKV_ATTN 3
 /* Sets `option` to `value`. Unknown option or value: STTD_ERR_INVALID_ARG. */
 sttd_status sttd_workspace_set_option(sttd_workspace *ws, int option, int value);
 
@@ -342,7 +355,8 @@ typedef enum {
     STTD_KERN_DOWN_GEMM = 11,
     STTD_KERN_LM_HEAD = 12,     /* final RMSNorm + tied head + argmax */
     STTD_KERN_BLOCK_STEP = 13,  /* the fused single-row decode step of one block (STTD_OPT_FUSED_STEP) */
-    STTD_KERN_COUNT = 14
+    STTD_KERN_QKV_ATTN = 14,    /* single decode row: Q|K|V projection + attention in one launch (STTD_OPT_QKV_ATTN) */
+    STTD_KERN_COUNT = 15
 } sttd_kernel;
 
 sttd_status sttd_profile_enable(uint32_t mask);

@@ -45,7 +45,11 @@ struct sttd_workspace {
     int32_t* rowseq;               // [max_rows]: per-row slabs of a packed batched prefill
     uint32_t* sync;                // [kStepSyncWords] hand-off counters of the fused step (zero between launches)
     uint32_t* merge_ctr;           // [max_rows][n_kv] attention split counts (zero between launches)
+    uint64_t* qtag;                // [(nq + 2 nkv) d] tagged projection words of a single decode row
+    uint32_t* tag_gen;             // [1] the next hand-off tag (never 0)
+    uint32_t* tag_done;            // [1] hand-off consumers counted out (zero between launches)
     bool fused_step;               // STTD_OPT_FUSED_STEP
+    bool qkv_attn;                 // STTD_OPT_QKV_ATTN
     uint32_t split_mask;           // STTD_OPT_ACT_SPLIT: GEMM inputs kept as bf16 high + low parts at any row count
 };
 
@@ -266,6 +270,16 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
             return STTD_OK;
         }
     }
+    // --- a single decode row: the Q|K|V projection and the attention in one launch
+    // (tagged hand-off), when the shape allows and the attention splits merge in the
+    // O projection
+    int qa_splits = 0;
+    bool qkv_attn = false;
+    if (!prefill && R == 1 && !mfma && wt == W_BF16 && ws->qkv_attn) {
+        qa_splits = choose_splits(R, nkv, pos_bound, ws->part_cap);
+        const int span = (pos_bound + qa_splits - 1) / qa_splits;
+        qkv_attn = qa_splits > 1 && qkv_attn_fits(nq, nkv, d, H, qa_splits, span, kl.type);
+    }
     // --- attention half: norm + QKV projection
     bool qk_fused = false;  // the Q|K|V GEMM's epilogue does the Q/K norm, RoPE and cache write
     QkRope qr{};
@@ -289,7 +303,7 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
         if (qk_fused) g.qk = qr;
         ProfScope ps(STTD_KERN_QKV_GEMM, s);
         TRY(launch_gemm(g, qk_fused ? GEMM_QKROPE : GEMM_STORE, s));
-    } else {
+    } else if (!qkv_attn) {
         GemvArgs a{};
         a.w[0] = w->wq; a.w[1] = w->wk; a.w[2] = w->wv;
         a.seg_end[0] = qd; a.seg_end[1] = qd + kvd; a.seg_end[2] = qkv_cols;
@@ -329,6 +343,16 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
     } else if (flash) {
         ProfScope ps(STTD_KERN_ATTN_PREFILL, s);
         TRY(launch_attn_prefill((const uint16_t*)ws->qbuf, qd, R, rm.pos0, rm.seq0, nq, kl, ao, ao_lo, qd, s));
+    } else if (qkv_attn) {
+        splits = qa_splits;
+        defer = true;
+        QkvTagArgs p{};
+        p.wq = (const uint16_t*)w->wq; p.wk = (const uint16_t*)w->wk; p.wv = (const uint16_t*)w->wv;
+        p.gain = (const uint16_t*)w->attn_norm; p.x = x; p.K = H; p.nq = nq; p.nkv = nkv; p.d = d; p.eps = eps;
+        p.qtag = ws->qtag;
+        ProfScope ps(STTD_KERN_QKV_ATTN, s);
+        TRY(launch_qkv_attn(p, rm, kl, splits, (pos_bound + splits - 1) / splits, ws->part, ws->err, qr, ws->tag_gen,
+                            ws->tag_done, s));
     } else {
         splits = choose_splits(R, nkv, pos_bound, ws->part_cap);
         // GEMV path: a split result stays as partials and the O projection merges them on load
@@ -536,6 +560,8 @@ sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int m
     const size_t o_rowpos = take(R * sizeof(int32_t));
     const size_t o_rowseq = take(R * sizeof(int32_t));
     const size_t o_merge = take(R * nkv * sizeof(uint32_t));
+    const size_t o_qtag = take((size_t)(nq + 2 * nkv) * d * sizeof(uint64_t));
+    const size_t o_tag = take(2 * sizeof(uint32_t));
     sttd_workspace* ws = new (std::nothrow) sttd_workspace();
     if (!ws) return STTD_ERR_OOM;
     ws->p = *p;
@@ -565,7 +591,11 @@ sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int m
     ws->rowpos = (int32_t*)(b + o_rowpos);
     ws->rowseq = (int32_t*)(b + o_rowseq);
     ws->merge_ctr = (uint32_t*)(b + o_merge);
+    ws->qtag = (uint64_t*)(b + o_qtag);
+    ws->tag_gen = (uint32_t*)(b + o_tag);
+    ws->tag_done = ws->tag_gen + 1;
     ws->fused_step = false;
+    ws->qkv_attn = true;
     ws->split_mask = STTD_SPLIT_QKV | STTD_SPLIT_O | STTD_SPLIT_GATE_UP | STTD_SPLIT_DOWN;
     // RoPE table in fp64 on the host: pair i of position pos turns by pos * theta^(-2i/d)
     std::vector<float> table((size_t)max_pos * d);
@@ -580,7 +610,9 @@ sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int m
     }
     std::vector<int32_t> iota(R);
     for (size_t i = 0; i < R; ++i) iota[i] = (int32_t)i;
+    const uint32_t first_tag = 1;  // the zeroed words carry tag 0, which no launch uses
     if (hipMemset(ws->base, 0, off) != hipSuccess ||
+        hipMemcpy(ws->tag_gen, &first_tag, sizeof(uint32_t), hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(ws->rope, table.data(), table.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(ws->iota, iota.data(), R * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess) {
         (void)hipFree(ws->base);
@@ -602,6 +634,10 @@ sttd_status sttd_workspace_set_option(sttd_workspace* ws, int option, int value)
     if (!ws) return STTD_ERR_INVALID_ARG;
     if (option == STTD_OPT_FUSED_STEP && (value == 0 || value == 1)) {
         ws->fused_step = value == 1;
+        return STTD_OK;
+    }
+    if (option == STTD_OPT_QKV_ATTN && (value == 0 || value == 1)) {
+        ws->qkv_attn = value == 1;
         return STTD_OK;
     }
     if (option == STTD_OPT_ACT_SPLIT && value >= 0 && value <= 15) {

@@ -51,8 +51,20 @@ struct RowsArgs {
     // non-null with several splits and an output to write: [rows][n_kv] zeroed
     // counts; the last split of a (row, KV head) to finish merges all of them
     uint32_t* merge_ctr;
+    // Tagged hand-off (the single-row projection + attention launch): the raw
+    // projection row arrives as 64-bit words (tag << 32 | value bits) in qtag,
+    // written while this workgroup already runs; it polls until every word it
+    // reads carries `tag`. The last of n_consumers workgroups to finish reading
+    // advances *tag_gen (never to 0) and zeroes *tag_done for the next launch.
+    const uint64_t* qtag;
+    uint32_t tag;
+    uint32_t* tag_gen;
+    uint32_t* tag_done;
+    int n_consumers;
     uint64_t* clk;
 };
+
+constexpr uint64_t kTagSpinTicks = 20000000;  // a hand-off poll gives up after 200 ms (100 MHz clock)
 
 // Eight cache elements as loaded (16 bytes of f16, or 32 of fp32), widened at use,
 // so a wave holds twice the rows in flight for the registers of fp32 copies.
@@ -121,8 +133,9 @@ __device__ __forceinline__ float group_sum(float v) {
     return LPK == 16 ? row16_sum(v) : row8_sum(v);
 }
 
-template <class KT, class GT, int D, int G, int NW, bool FUSE, class MEM = PlainMem>
+template <class KT, class GT, int D, int G, int NW, bool FUSE, class MEM = PlainMem, bool TAGGED = false>
 __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, const int j, const int split) {
+    static_assert(!TAGGED || FUSE, "the tagged hand-off carries raw projection rows");
     typedef typename KT::T T;
     constexpr int LPK = D / 8;                 // lanes per cache row
     constexpr int GPW = WAVE / LPK;            // groups per wave
@@ -150,16 +163,23 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
     const int lc = lane < HALF ? lane : 0;
     float u0[IPW], u1[IPW];
     typename GT::T g0r[IPW], g1r[IPW];
+    // projection column of this wave's item k
+    auto item_col = [&](int k) {
+        const int it = wave + k * NW;
+        const int itc = it < G + 2 ? it : 0;
+        return itc < G ? (j * G + itc) * D : (itc == G ? (a.n_heads + j) * D : (a.n_heads + a.kv.n_kv + j) * D);
+    };
     if (FUSE) {
         const float* src = a.q + (int64_t)r * a.ldq;
 #pragma unroll
         for (int k = 0; k < IPW; ++k) {
             const int it = wave + k * NW;
             const int itc = it < G + 2 ? it : 0;
-            const int col = itc < G ? (j * G + itc) * D
-                                    : (itc == G ? (a.n_heads + j) * D : (a.n_heads + a.kv.n_kv + j) * D);
-            u0[k] = MEM::ld(src + col + lc);
-            u1[k] = MEM::ld(src + col + lc + HALF);
+            const int col = item_col(k);
+            if (!TAGGED) {
+                u0[k] = MEM::ld(src + col + lc);
+                u1[k] = MEM::ld(src + col + lc + HALF);
+            }
             const typename GT::T* gain = (const typename GT::T*)(itc < G ? a.q_gain : a.k_gain);
             g0r[k] = gain[lc];
             g1r[k] = gain[lc + HALF];
@@ -202,6 +222,30 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
         vr[q].load(Vp + (int64_t)cq * D);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // 2b. tagged hand-off: with the cache rows above in flight, poll this wave's
+    //     raw head items until each word carries this launch's tag (bounded wait)
+    if (TAGGED) {
+        const uint64_t* src = a.qtag + (int64_t)r * a.ldq;
+        const uint64_t t0 = wall_clock64();
+        while (true) {
+            bool good = true;
+#pragma unroll
+            for (int k = 0; k < IPW; ++k) {
+                const int col = item_col(k);
+                const uint64_t w0 = __hip_atomic_load(src + col + lc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t w1 = __hip_atomic_load(src + col + lc + HALF, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                good = good && (uint32_t)(w0 >> 32) == a.tag && (uint32_t)(w1 >> 32) == a.tag;
+                u0[k] = __uint_as_float((uint32_t)w0);
+                u1[k] = __uint_as_float((uint32_t)w1);
+            }
+            if (__all(good)) break;
+            if (wall_clock64() - t0 > kTagSpinTicks) {
+                if (lane == 0) record_error(a.err, kDevErrSync);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
     // 3. finish the head items: RMSNorm + rotation (queries, key); the owner
     //    writes key and value to cache row pos
     if (FUSE) {
@@ -237,6 +281,16 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
             q_lds[t / D][t % D] = ok ? MEM::ld(a.q + (int64_t)r * a.ldq + (j * G + t / D) * D + t % D) * scale : 0.f;
     }
     __syncthreads();
+    // every wave of this workgroup is done with the tagged words: count out; the
+    // last consumer of the launch moves the tag on and re-arms the count
+    if (TAGGED && tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(a.tag_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == (uint32_t)(a.n_consumers - 1)) {
+            __hip_atomic_store(a.tag_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.tag_gen, a.tag + 1u == 0u ? 1u : a.tag + 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 
     float qv[G][8];
 #pragma unroll

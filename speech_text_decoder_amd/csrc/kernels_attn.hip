@@ -8,6 +8,7 @@
 // Exponentials run in base 2 on scores pre-scaled by log2(e)/sqrt(d).
 #include "attn_rows.h"
 #include "common.h"
+#include "gemv_ops.h"
 #include "launch.h"
 
 namespace sttd {
@@ -127,6 +128,102 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
         return gt == W_BF16 ? rows_dispatch_kv<BF16, true>(a, R, wide, s) : rows_dispatch_kv<F32, true>(a, R, wide, s);
     }
     return rows_dispatch_kv<BF16, false>(a, R, false, s);
+}
+
+// ------------------------------------------------------------------ one decode row: projection + attention
+// One launch for the Q|K|V projection of a single decode row and its attention.
+// Workgroups [0, n_prod) each compute 4 columns of the fused-RMSNorm projection
+// with the GEMV's arithmetic (the same loads, dot products and merge, so the
+// values are bit-identical to the GEMV's), ordered KV head major: tiles
+// j * TPH .. of head j
+// are its G query heads' columns, then its key's, then its value's. Each column
+// is published as one 64-bit word (tag << 32 | value bits) with a device-scope
+// store. Workgroups [n_prod, n_prod + n_kv * n_splits) are the attention items
+// (KV head, split): they load the position, rotation row and first cache rows,
+// then poll their head's words until they carry the launch's tag (the word a
+// launch's last consumer advances; attn_rows_item, TAGGED). Producers precede
+// consumers in dispatch order, so a poll only ever waits on producers that are
+// running or done; it still gives up after 200 ms and flags SYNC. Measured on
+// the 1.7B shape (1024 producers, 64 consumers): 8.8 us for the launch against
+// 4.2 + 3.6 us for the two kernels and the ~1.5 us gap between them; the
+// attention work left after the hand-off (the poll's round trip, the second
+// half of each split's cache rows, the partials) is what remains exposed.
+template <int KCH, int G, int D>
+__global__ __launch_bounds__(256) void qkv_attn_kernel(QkvTagArgs p, RowsArgs a, int n_prod) {
+    clock_begin(a.clk);
+    const uint32_t tag = __builtin_amdgcn_readfirstlane(*a.tag_gen);
+    if ((int)blockIdx.x < n_prod) {
+        constexpr int NR = 4, TQ = G * D / NR, TK = D / NR, TPH = TQ + 2 * TK;
+        __shared__ float red[4][NR + 1];
+        const int t = blockIdx.x, j = t / TPH, u = t % TPH;
+        const uint16_t* W;
+        int row0, col0;
+        if (u < TQ) {
+            W = p.wq; row0 = j * G * D + u * NR; col0 = row0;
+        } else if (u < TQ + TK) {
+            W = p.wk; row0 = j * D + (u - TQ) * NR; col0 = p.nq * D + row0;
+        } else {
+            W = p.wv; row0 = j * D + (u - TQ - TK) * NR; col0 = (p.nq + p.nkv) * D + row0;
+        }
+        const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE;
+        int kk[KCH];
+        Raw8<BF16> w[KCH][NR];
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+            kk[c] = (c * 4 + wave) * CHUNK + lane * 8;
+            const int k = kk[c] < p.K ? kk[c] : 0;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) w[c][r].load(W + (int64_t)(row0 + r) * p.K + k);
+        }
+        float xv[KCH][1][8], ss[1];
+        load_activations<BF16, KCH, 1, true>(p.x, p.K, 1, p.K, p.gain, kk, xv, ss);
+        float acc[NR];
+        chunk_dots<BF16, KCH, NR, 1>(w, xv, acc);
+        float dot, rs[1];
+        block_merge<NR, 1, true>(acc, ss, red, p.K, p.eps, dot, rs);
+        if ((int)threadIdx.x < NR) {
+            const float v = dot * rs[0];
+            __hip_atomic_store(p.qtag + col0 + threadIdx.x, ((uint64_t)tag << 32) | __float_as_uint(v),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        clock_end(a.clk);
+        return;
+    }
+    const int c = blockIdx.x - n_prod;
+    RowsArgs b = a;
+    b.tag = tag;
+    attn_rows_item<F16, BF16, D, G, 4, true, PlainMem, true>(b, 0, c / a.n_splits, c % a.n_splits);
+    clock_end(a.clk);
+}
+
+bool qkv_attn_fits(int n_heads, int n_kv, int d, int K, int n_splits, int span_bound, KVType kv) {
+    const int G = n_kv > 0 ? n_heads / n_kv : 0;
+    return kv == KV_F16 && d == 128 && (G == 1 || G == 2) && G * n_kv == n_heads && K % 8 == 0 && K <= 2 * 4 * CHUNK &&
+           n_splits >= 1 && n_splits <= kMergeMaxSplits && span_bound <= 128;
+}
+
+hipError_t launch_qkv_attn(const QkvTagArgs& p, RowMap rm, KVLayer kv, int n_splits, int span_bound, float* part,
+                           uint32_t* err, const QkRope& fuse, uint32_t* tag_gen, uint32_t* tag_done, hipStream_t s) {
+    if (!qkv_attn_fits(p.nq, p.nkv, p.d, p.K, n_splits, span_bound, kv.type) || !rm.pos || !rm.seq)
+        return hipErrorInvalidValue;
+    RowsArgs a{};
+    a.q = nullptr; a.ldq = (p.nq + 2 * p.nkv) * p.d; a.n_heads = p.nq; a.rm = rm; a.kv = kv; a.n_splits = n_splits;
+    a.part = part; a.err = err;
+    a.q_gain = fuse.q_gain; a.k_gain = fuse.k_gain; a.eps = fuse.eps; a.rope = fuse.rope; a.max_pos = fuse.max_pos;
+    a.qtag = p.qtag; a.tag_gen = tag_gen; a.tag_done = tag_done; a.n_consumers = p.nkv * n_splits;
+    a.clk = clock_slot();
+    const int n_prod = (p.nq + 2 * p.nkv) * p.d / 4;
+    const int grid = n_prod + a.n_consumers;
+    const int G = p.nq / p.nkv;
+    const bool k1 = p.K <= 4 * CHUNK;
+    if (G == 1) {
+        if (k1) launch_kernel(qkv_attn_kernel<1, 1, 128>, grid, 256, 0, s, p, a, n_prod);
+        else launch_kernel(qkv_attn_kernel<2, 1, 128>, grid, 256, 0, s, p, a, n_prod);
+    } else {
+        if (k1) launch_kernel(qkv_attn_kernel<1, 2, 128>, grid, 256, 0, s, p, a, n_prod);
+        else launch_kernel(qkv_attn_kernel<2, 2, 128>, grid, 256, 0, s, p, a, n_prod);
+    }
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ causal prefill (MFMA flash)

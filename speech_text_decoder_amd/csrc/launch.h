@@ -229,6 +229,24 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
                             int span_bound, float* part, float* out_f32, uint16_t* out_bf16, uint16_t* out_bf16_lo,
                             int64_t ldo, uint32_t* err, const QkRope* fuse, WType gt, hipStream_t s,
                             uint32_t* merge_ctr = nullptr);
+// One decode row: the fused-RMSNorm Q|K|V projection and the split attention in
+// one launch (kernels_attn.hip, qkv_attn_kernel), handing the projection over
+// through 64-bit tagged words in qtag. The splits' partial records go to `part`
+// for the O-projection GEMV to merge. tag_gen: a device word, never 0, that the
+// launch advances; tag_done: a device word, zero between launches.
+struct QkvTagArgs {
+    const uint16_t* wq;
+    const uint16_t* wk;
+    const uint16_t* wv;
+    const uint16_t* gain;  // attention RMSNorm gain (bf16)
+    const float* x;        // the row, [K] fp32
+    int K, nq, nkv, d;
+    float eps;
+    uint64_t* qtag;  // [(nq + 2 nkv) d] tagged projection words
+};
+bool qkv_attn_fits(int n_heads, int n_kv, int d, int K, int n_splits, int span_bound, KVType kv);
+hipError_t launch_qkv_attn(const QkvTagArgs& p, RowMap rm, KVLayer kv, int n_splits, int span_bound, float* part,
+                           uint32_t* err, const QkRope& fuse, uint32_t* tag_gen, uint32_t* tag_done, hipStream_t s);
 // Causal flash attention (MFMA, f16 cache) of T rows of one slab at positions pos0..
 hipError_t launch_attn_prefill(const uint16_t* q16, int64_t ldq, int T, int pos0, int seq, int n_heads, KVLayer kv,
                                uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo, hipStream_t s);

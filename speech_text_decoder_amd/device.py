@@ -122,6 +122,10 @@ class DecoderSession:
         """STTD_OPT_FUSED_STEP: single-row steps as one persistent launch per block (default off)."""
         B.workspace_set_option(self.ws, B.OPT_FUSED_STEP, 1 if enabled else 0)
 
+    def set_qkv_attn(self, enabled: bool):
+        """STTD_OPT_QKV_ATTN: a single decode row's projection and attention in one launch (default on)."""
+        B.workspace_set_option(self.ws, B.OPT_QKV_ATTN, 1 if enabled else 0)
+
     def set_act_split(self, mask: int):
         """STTD_OPT_ACT_SPLIT: GEMM inputs (B.SPLIT_* bits) kept as bf16 high + low parts above 512 rows."""
         B.workspace_set_option(self.ws, B.OPT_ACT_SPLIT, int(mask))
