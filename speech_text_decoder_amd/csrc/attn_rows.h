@@ -209,8 +209,9 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
     const int cend = owner ? pos : c1;  // the new key (owner) is folded in from LDS below
     // RIF rows per group in flight: row c + q * NG for q < RIF (clamped to row 0 past the end)
     // (8 per group for G <= 2 with f16 rows kept packed measured slower for one
-    // decode row: 5.4 -> 6.3 us per launch; and for splits over 256 rows, 16 rows
-    // of 150-1500 positions: 8 and 12 took 18.0 -> 20.7 and 23.4 us)
+    // decode row: 5.4 -> 6.3 us per launch, and in the one-launch projection +
+    // attention 8.8 -> 10.0 us; for splits over 256 rows, 16 rows of 150-1500
+    // positions: 8 and 12 took 18.0 -> 20.7 and 23.4 us)
     constexpr int RIF = G <= 2 ? 4 : (G == 4 ? 2 : 1);
     constexpr int STEP = RIF * NG;
     int c = c0 + grp;

@@ -132,11 +132,11 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
 
 // ------------------------------------------------------------------ one decode row: projection + attention
 // One launch for the Q|K|V projection of a single decode row and its attention.
-// Workgroups [0, n_prod) each compute 4 columns of the fused-RMSNorm projection
-// with the GEMV's arithmetic (the same loads, dot products and merge, so the
-// values are bit-identical to the GEMV's), ordered KV head major: tiles
-// j * TPH .. of head j
-// are its G query heads' columns, then its key's, then its value's. Each column
+// Workgroups [0, n_prod) each compute STTD_QA_NR columns of the fused-RMSNorm
+// projection with the GEMV's arithmetic (the same loads, dot products and merge,
+// so the values are bit-identical to the GEMV's), ordered KV head major: tiles
+// j * TPH .. of head j are its G query heads' columns, then its key's, then its
+// value's. Each column
 // is published as one 64-bit word (tag << 32 | value bits) with a device-scope
 // store. Workgroups [n_prod, n_prod + n_kv * n_splits) are the attention items
 // (KV head, split): they load the position, rotation row and first cache rows,
@@ -144,16 +144,22 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
 // launch's last consumer advances; attn_rows_item, TAGGED). Producers precede
 // consumers in dispatch order, so a poll only ever waits on producers that are
 // running or done; it still gives up after 200 ms and flags SYNC. Measured on
-// the 1.7B shape (1024 producers, 64 consumers): 8.8 us for the launch against
+// the 1.7B shape (512 producers, 64 consumers): 8.5 us for the launch against
 // 4.2 + 3.6 us for the two kernels and the ~1.5 us gap between them; the
 // attention work left after the hand-off (the poll's round trip, the second
 // half of each split's cache rows, the partials) is what remains exposed.
+// Projection columns per producer workgroup: on the 28-block greedy job 8 (512
+// producers) measured 8.51 us per launch, 4 measured 8.69 and 2 measured 10.1.
+#ifndef STTD_QA_NR
+#define STTD_QA_NR 8
+#endif
+
 template <int KCH, int G, int D>
 __global__ __launch_bounds__(256) void qkv_attn_kernel(QkvTagArgs p, RowsArgs a, int n_prod) {
     clock_begin(a.clk);
     const uint32_t tag = __builtin_amdgcn_readfirstlane(*a.tag_gen);
     if ((int)blockIdx.x < n_prod) {
-        constexpr int NR = 4, TQ = G * D / NR, TK = D / NR, TPH = TQ + 2 * TK;
+        constexpr int NR = STTD_QA_NR, TQ = G * D / NR, TK = D / NR, TPH = TQ + 2 * TK;
         __shared__ float red[4][NR + 1];
         const int t = blockIdx.x, j = t / TPH, u = t % TPH;
         const uint16_t* W;
@@ -212,7 +218,7 @@ hipError_t launch_qkv_attn(const QkvTagArgs& p, RowMap rm, KVLayer kv, int n_spl
     a.q_gain = fuse.q_gain; a.k_gain = fuse.k_gain; a.eps = fuse.eps; a.rope = fuse.rope; a.max_pos = fuse.max_pos;
     a.qtag = p.qtag; a.tag_gen = tag_gen; a.tag_done = tag_done; a.n_consumers = p.nkv * n_splits;
     a.clk = clock_slot();
-    const int n_prod = (p.nq + 2 * p.nkv) * p.d / 4;
+    const int n_prod = (p.nq + 2 * p.nkv) * p.d / STTD_QA_NR;
     const int grid = n_prod + a.n_consumers;
     const int G = p.nq / p.nkv;
     const bool k1 = p.K <= 4 * CHUNK;

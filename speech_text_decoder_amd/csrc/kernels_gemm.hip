@@ -709,7 +709,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 // 512 and 1024 measured slower (down 12.3 -> 12.8 and 15.8 us): every split adds
 // rows x N atomics. Splitting the K of STORE and SWIGLU launches too, with the
 // column tile's last workgroup merging the published partials, measured slower at
-// 384-1024 workgroups (gate_up 18.0 -> 23.8-25.7 us, QKV 8.2 -> 10.4-11.2 us).
+// 384-1024 workgroups (gate_up 18.0 -> 23.8-25.7 us, QKV 8.2 -> 10.4-11.2 us). So
+// did staging the 16 activation rows once per workgroup in LDS (128 KB, normed and
+// split on the way in) with only weight loads in the K loop, two batches in
+// flight: gate_up 17.4 -> 21.4 us, QKV (32 columns per workgroup) 8.1 -> 15.0 us.
 #ifndef STTD_SKINNY_RESID_WGS
 #define STTD_SKINNY_RESID_WGS 256
 #endif

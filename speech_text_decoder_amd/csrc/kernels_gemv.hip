@@ -133,6 +133,18 @@ static hipError_t launch_k(const GemvArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Weight rows per workgroup of the RESID projections without a split merge (the
+// down projection of a decode row): 4 measured best on the 28-block greedy job
+// (down 5.97 us with 2 rows, 5.64 with 4, 6.73 with 1)
+// Weight rows per workgroup of the SwiGLU projection (gate and up rows of half as
+// many act columns): 4 measured 9.50 us for a decode row, 8 measured 10.28, 2 9.96
+#ifndef STTD_GEMV_SWIGLU_NR
+#define STTD_GEMV_SWIGLU_NR 4
+#endif
+#ifndef STTD_GEMV_RESID_NR
+#define STTD_GEMV_RESID_NR 4
+#endif
+
 template <class WT>
 static hipError_t launch_wt(const GemvArgs& a, GemvEpi epi, hipStream_t s) {
     // Rows per workgroup, measured on the decode shapes: more, shorter workgroups
@@ -143,12 +155,14 @@ static hipError_t launch_wt(const GemvArgs& a, GemvEpi epi, hipStream_t s) {
     // (gate_up 9.6 -> 9.9-13.6 us, QKV 4.2 -> 5.0-6.7 us).
     const bool norm = a.gain != nullptr;
     if (epi == GEMV_SWIGLU)
-        return norm ? launch_k<WT, GEMV_SWIGLU, 4, true>(a, s) : launch_k<WT, GEMV_SWIGLU, 4, false>(a, s);
+        return norm ? launch_k<WT, GEMV_SWIGLU, STTD_GEMV_SWIGLU_NR, true>(a, s)
+                    : launch_k<WT, GEMV_SWIGLU, STTD_GEMV_SWIGLU_NR, false>(a, s);
     if (epi == GEMV_RESID) {
         // merging the attention splits on load costs n_splits times the activation
         // reads of a plain row, so fewer, wider workgroups pay it fewer times
         if (a.xpart) return launch_k<WT, GEMV_RESID, 8, false, true>(a, s);
-        return norm ? launch_k<WT, GEMV_RESID, 2, true>(a, s) : launch_k<WT, GEMV_RESID, 2, false>(a, s);
+        return norm ? launch_k<WT, GEMV_RESID, STTD_GEMV_RESID_NR, true>(a, s)
+                    : launch_k<WT, GEMV_RESID, STTD_GEMV_RESID_NR, false>(a, s);
     }
     return norm ? launch_k<WT, GEMV_STORE, 4, true>(a, s) : launch_k<WT, GEMV_STORE, 4, false>(a, s);
 }
@@ -306,9 +320,16 @@ __global__ __launch_bounds__(256) void lm_head_finalize_kernel(HeadArgs a, int n
     clock_end(a.clk, 1);
 }
 
+// Vocabulary rows per block of the persistent head (each workgroup fetches the
+// next block while it reduces one): 4 measured 105.3 us per single-row head on
+// the 28-block greedy job, 8 measured 111.0 and 16 measured 127.9.
+#ifndef STTD_HEAD_NR
+#define STTD_HEAD_NR 4
+#endif
+
 template <class WT, int KCH>
 static void launch_head_k(const HeadArgs& a, dim3 grid, hipStream_t s) {
-    constexpr int NR = 8;
+    constexpr int NR = STTD_HEAD_NR;
     if (a.rows == 1) launch_kernel(lm_head_kernel<WT, 1, NR, KCH>, grid, 256, 0, s, a);
     else if (a.rows == 2) launch_kernel(lm_head_kernel<WT, 2, NR, KCH>, grid, 256, 0, s, a);
     else {
@@ -319,7 +340,7 @@ static void launch_head_k(const HeadArgs& a, dim3 grid, hipStream_t s) {
 
 template <class WT>
 static hipError_t launch_head_wt(const HeadArgs& a, hipStream_t s) {
-    constexpr int NR = 8;
+    constexpr int NR = STTD_HEAD_NR;
     const int n_blocks = (a.vocab + NR - 1) / NR;
     const int grid_x = n_blocks < a.max_partials ? n_blocks : a.max_partials;
     const dim3 grid(grid_x, 1);
