@@ -33,13 +33,16 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
 # 256 MiB copy (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0); valid only for the kernel
 # sources they were taken on (sha256 of the listed files).
 _GEMV_SRC = {"files": ["kernels_gemv.hip", "gemv_ops.h", "common.h"],
-             "sha256": "5c3f3a0eb495645108d3801ab9343f144ba3e5351713a47653d76b1f5ddb349c",
+             "sha256": "5074de34d4c5191f4503036246fd861744278baa79dddd23fa15bdc1047169aa",
              "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
+_QA_SRC = {"files": ["kernels_attn.hip", "attn_rows.h", "gemv_ops.h", "common.h"],
+           "sha256": "c9da32352429a20ee513097b8bfb64a9c9d920be755072860b1adc0723e30dbc",
+           "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
 TRAFFIC = {
-    "qkv_gemv": dict(_GEMV_SRC, rows=1, bytes=16958604),
-    "o_gemv": dict(_GEMV_SRC, rows=1, bytes=8676391),
-    "gateup_gemv": dict(_GEMV_SRC, rows=1, bytes=50579421),
-    "down_gemv": dict(_GEMV_SRC, rows=1, bytes=25509195),
+    "o_gemv": dict(_GEMV_SRC, rows=1, bytes=8676417),
+    "gateup_gemv": dict(_GEMV_SRC, rows=1, bytes=50579443),
+    "down_gemv": dict(_GEMV_SRC, rows=1, bytes=25508068),
+    "qkv_attn": dict(_QA_SRC, rows=1, bytes=18083938),
 }
 
 
