@@ -238,21 +238,33 @@ __device__ __forceinline__ int big_lds_off(int r, int c) { return r * BIG_BK + (
 #ifndef STTD_BIG_WM
 #define STTD_BIG_WM 4
 #endif
+#ifndef STTD_BIG_SPLIT
+#define STTD_BIG_SPLIT 1  // split activations (hi/lo) take the large tiles too
+#endif
 // WM: waves along M (4: 8 waves of 64 x BN/2; 2: 4 waves of 128 x BN/2, one per
 // SIMD, with the accumulators in AGPRs). One wave per SIMD reads a third less LDS
 // per MFMA but measured much slower at 4096 rows (gate_up 189 -> 284 us, down
 // 113 -> 175 us): a single wave cannot hide its LDS and global latency.
-template <int EPI, int BN, int KSPLIT = 1, int WM = STTD_BIG_WM>
+// SPLIT: the activations come as bf16 high and low planes (A, A_lo); both are
+// staged and every B fragment feeds two MFMAs, one per plane. The K-step per
+// tile is 32 then, so the three staged tiles fit LDS twice over; rows of 32
+// elements (4 chunks) need no swizzle: a fragment read (16 rows x 4 chunks) and a
+// staging write (16 rows x 4 chunks) each cover 1 KB of consecutive LDS.
+template <int EPI, int BN, int KSPLIT = 1, int WM = STTD_BIG_WM, bool SPLIT = false>
 __global__ __launch_bounds__(WM * 128) void gemm_big_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     static_assert(EPI != GEMM_SWIGLU || BN == BIG_BN, "SwiGLU pairs gate and up inside 256-row weight tiles");
     static_assert(KSPLIT == 1 || EPI == GEMM_RESID, "split K adds into a residual");
+    static_assert(!SPLIT || EPI != GEMM_QKROPE, "the Q/K epilogue takes plain activations");
+    constexpr int BK = SPLIT ? 32 : BIG_BK;          // K per staged tile
     constexpr int NT = WM * 128;                     // threads
     constexpr int WR = BIG_BM / WM;                  // rows per wave
     constexpr int FM = WR / 16, FN = BN / 32;
-    constexpr int VECS = BIG_BM * BIG_BK / 8 / NT;   // 16-byte vectors per thread and step: A
-    constexpr int BVECS = BN * BIG_BK / 8 / NT;      // and B
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BIG_BM * BIG_STR];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BIG_STR];
+    constexpr int VECS = BIG_BM * BK / 8 / NT;       // 16-byte vectors per thread and step: A
+    constexpr int BVECS = BN * BK / 8 / NT;          // and B
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BIG_BM * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t Als[SPLIT ? 2 : 1][SPLIT ? BIG_BM * BK : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
+    auto lds_off = [](int r, int c) { return SPLIT ? r * BK + c * 8 : big_lds_off(r, c); };
 
     clock_begin(g.clk);
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
@@ -267,19 +279,21 @@ __global__ __launch_bounds__(WM * 128) void gemm_big_kernel(GemmArgs g, int tile
     const int m0 = tile_m * BIG_BM;
 
     const uint16_t* aptr[VECS];
+    const uint16_t* alptr[VECS];
     const uint16_t* bptr[BVECS];
     bool bok[BVECS];
 #pragma unroll
     for (int i = 0; i < VECS; ++i) {
         const int v = tid + i * NT;
-        const int r = v / (BIG_BK / 8), ck = (v % (BIG_BK / 8)) * 8;
+        const int r = v / (BK / 8), ck = (v % (BK / 8)) * 8;
         const int am = m0 + r < g.M ? m0 + r : 0;
         aptr[i] = g.A + (int64_t)am * g.lda + k_begin + ck;
+        alptr[i] = (SPLIT ? g.A_lo : g.A) + (int64_t)am * g.lda + k_begin + ck;
     }
 #pragma unroll
     for (int i = 0; i < BVECS; ++i) {
         const int v = tid + i * NT;
-        const int r = v / (BIG_BK / 8), ck = (v % (BIG_BK / 8)) * 8;
+        const int r = v / (BK / 8), ck = (v % (BK / 8)) * 8;
         int grow;
         const uint16_t* W;
         bok[i] = true;
@@ -298,10 +312,14 @@ __global__ __launch_bounds__(WM * 128) void gemm_big_kernel(GemmArgs g, int tile
         }
         bptr[i] = W + (int64_t)grow * g.K + k_begin + ck;
     }
-    u32x4 areg[VECS], breg[BVECS];
+    u32x4 areg[VECS], alreg[SPLIT ? VECS : 1], breg[BVECS];
     auto fetch = [&](int64_t k0) {
 #pragma unroll
         for (int i = 0; i < VECS; ++i) areg[i] = *reinterpret_cast<const u32x4*>(aptr[i] + k0);
+        if (SPLIT) {
+#pragma unroll
+            for (int i = 0; i < VECS; ++i) alreg[SPLIT ? i : 0] = *reinterpret_cast<const u32x4*>(alptr[i] + k0);
+        }
 #pragma unroll
         for (int i = 0; i < BVECS; ++i)
             breg[i] = bok[i] ? *reinterpret_cast<const u32x4*>(bptr[i] + k0) : u32x4{0u, 0u, 0u, 0u};
@@ -310,8 +328,9 @@ __global__ __launch_bounds__(WM * 128) void gemm_big_kernel(GemmArgs g, int tile
 #pragma unroll
         for (int i = 0; i < VECS; ++i) {
             const int v = tid + i * NT;
-            const int o = big_lds_off(v / (BIG_BK / 8), v % (BIG_BK / 8));
+            const int o = lds_off(v / (BK / 8), v % (BK / 8));
             *reinterpret_cast<u32x4*>(&As[buf][o]) = areg[i];
+            if (SPLIT) *reinterpret_cast<u32x4*>(&Als[SPLIT ? buf : 0][o]) = alreg[SPLIT ? i : 0];
             if (i < BVECS) *reinterpret_cast<u32x4*>(&Bs[buf][o]) = breg[i < BVECS ? i : 0];
         }
     };
@@ -322,36 +341,44 @@ __global__ __launch_bounds__(WM * 128) void gemm_big_kernel(GemmArgs g, int tile
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = g.K / BIG_BK / KSPLIT;
+    const int nk = g.K / BK / KSPLIT;
     fetch(0);
     stash(0);
-    if (nk > 1) fetch(BIG_BK);
+    if (nk > 1) fetch(BK);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
         const uint16_t* Ab = As[buf];
+        const uint16_t* Alb = Als[SPLIT ? buf : 0];
         const uint16_t* Bb = Bs[buf];
 #pragma unroll
-        for (int ks = 0; ks < BIG_BK / 32; ++ks) {
+        for (int ks = 0; ks < BK / 32; ++ks) {
             const int kc = ks * 32 + (lane / 16) * 8;
-            bf16x8 af[FM], bfr[FN];
+            bf16x8 af[FM], al[SPLIT ? FM : 1], bfr[FN];
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(&Ab[big_lds_off(wm * WR + i * 16 + lane % 16, kc / 8)]);
+            for (int i = 0; i < FM; ++i) {
+                af[i] = *reinterpret_cast<const bf16x8*>(&Ab[lds_off(wm * WR + i * 16 + lane % 16, kc / 8)]);
+                if (SPLIT)
+                    al[SPLIT ? i : 0] =
+                        *reinterpret_cast<const bf16x8*>(&Alb[lds_off(wm * WR + i * 16 + lane % 16, kc / 8)]);
+            }
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(&Bb[big_lds_off(wn * (BN / 2) + j * 16 + lane % 16, kc / 8)]);
+                bfr[j] = *reinterpret_cast<const bf16x8*>(&Bb[lds_off(wn * (BN / 2) + j * 16 + lane % 16, kc / 8)]);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
+                for (int j = 0; j < FN; ++j) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    if (SPLIT)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[SPLIT ? i : 0], bfr[j], acc[i][j], 0, 0, 0);
+                }
             // between the two K-steps: stage the next tile (the other buffer was last read
             // before the previous barrier) and start loading the one after, so the LDS
             // writes and the global loads overlap the second step's MFMAs
             if (ks == 0 && kt + 1 < nk) {
                 stash(buf ^ 1);
-                if (kt + 2 < nk) fetch((int64_t)(kt + 2) * BIG_BK);
+                if (kt + 2 < nk) fetch((int64_t)(kt + 2) * BK);
             }
         }
         __syncthreads();
@@ -467,7 +494,7 @@ __global__ __launch_bounds__(WM * 128) void gemm_big_kernel(GemmArgs g, int tile
     clock_end(g.clk);
 }
 
-// Whether the large tiles apply: many rows, no split activations, shapes that tile.
+// Whether the large tiles apply: many rows and shapes that tile.
 bool gemm_qkrope_fits(int M, int N, int K, int head_dim) {
     return head_dim == 128 && M >= 1024 && K % BIG_BK == 0 && N % BIG_BN == 0 &&
            ((M + BIG_BM - 1) / BIG_BM) * (N / BIG_BN) >= 256;
@@ -475,20 +502,22 @@ bool gemm_qkrope_fits(int M, int N, int K, int head_dim) {
 
 static bool big_tiles_fit(const GemmArgs& g, GemmEpi epi) {
     if (epi == GEMM_QKROPE) return !g.A_lo && gemm_qkrope_fits(g.M, g.N, g.K, g.qk.d);
-    if (g.A_lo || g.M < 1024 || g.K % BIG_BK) return false;
+    if (g.M < 1024 || g.K % BIG_BK || (g.A_lo && !STTD_BIG_SPLIT)) return false;
+    // split activations into a residual: the large tiles only when 256 x 128 tiles
+    // fill the CUs; narrower grids lose to the 64-row tiles' split K (1224 rows,
+    // 2048 columns: O 48 -> 58 us, down 122 -> 147 us on the large tiles)
+    if (g.A_lo && epi == GEMM_RESID && ((g.M + BIG_BM - 1) / BIG_BM) * ((g.N + 127) / 128) < 256) return false;
     return !(epi == GEMM_SWIGLU && g.N % 128);
 }
 
-static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
+template <bool SPLIT>
+static void launch_gemm_big_t(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
+    constexpr int WM = STTD_BIG_WM;
     const int tiles_m = (g.M + BIG_BM - 1) / BIG_BM;
     if (epi == GEMM_SWIGLU) {
         const int tiles_n = g.N / 128;
-        launch_kernel(gemm_big_kernel<GEMM_SWIGLU, BIG_BN>, tiles_m * tiles_n, STTD_BIG_WM * 128, 0, s, g, tiles_m, tiles_n);
-        return;
-    }
-    if (epi == GEMM_QKROPE) {
-        const int tiles_n = g.N / BIG_BN;
-        launch_kernel(gemm_big_kernel<GEMM_QKROPE, BIG_BN>, tiles_m * tiles_n, STTD_BIG_WM * 128, 0, s, g, tiles_m, tiles_n);
+        launch_kernel(gemm_big_kernel<GEMM_SWIGLU, BIG_BN, 1, WM, SPLIT>, tiles_m * tiles_n, WM * 128, 0, s, g, tiles_m,
+                      tiles_n);
         return;
     }
     // residual outputs too narrow to fill the CUs even with 256 x 128 tiles: two
@@ -500,7 +529,8 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     const int tiles128 = tiles_m * ((g.N + 127) / 128);
     if (epi == GEMM_RESID && tiles128 < 256 && tiles256 % 8 == 0 && (g.K / BIG_BK) % 2 == 0 &&
         g.K / BIG_BK >= 16) {
-        launch_kernel(gemm_big_kernel<GEMM_RESID, BIG_BN, 2>, tiles256 * 2, STTD_BIG_WM * 128, 0, s, g, tiles_m, (g.N + BIG_BN - 1) / BIG_BN);
+        launch_kernel(gemm_big_kernel<GEMM_RESID, BIG_BN, 2, WM, SPLIT>, tiles256 * 2, WM * 128, 0, s, g, tiles_m,
+                      (g.N + BIG_BN - 1) / BIG_BN);
         return;
     }
     // narrow outputs: 128-column tiles so that about a full wave of workgroups runs
@@ -509,12 +539,23 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     const int tiles_n = (g.N + bn - 1) / bn;
     const int grid = tiles_m * tiles_n;
     if (epi == GEMM_RESID) {
-        if (narrow) launch_kernel(gemm_big_kernel<GEMM_RESID, 128>, grid, STTD_BIG_WM * 128, 0, s, g, tiles_m, tiles_n);
-        else launch_kernel(gemm_big_kernel<GEMM_RESID, BIG_BN>, grid, STTD_BIG_WM * 128, 0, s, g, tiles_m, tiles_n);
+        if (narrow) launch_kernel(gemm_big_kernel<GEMM_RESID, 128, 1, WM, SPLIT>, grid, WM * 128, 0, s, g, tiles_m, tiles_n);
+        else launch_kernel(gemm_big_kernel<GEMM_RESID, BIG_BN, 1, WM, SPLIT>, grid, WM * 128, 0, s, g, tiles_m, tiles_n);
     } else {
-        if (narrow) launch_kernel(gemm_big_kernel<GEMM_STORE, 128>, grid, STTD_BIG_WM * 128, 0, s, g, tiles_m, tiles_n);
-        else launch_kernel(gemm_big_kernel<GEMM_STORE, BIG_BN>, grid, STTD_BIG_WM * 128, 0, s, g, tiles_m, tiles_n);
+        if (narrow) launch_kernel(gemm_big_kernel<GEMM_STORE, 128, 1, WM, SPLIT>, grid, WM * 128, 0, s, g, tiles_m, tiles_n);
+        else launch_kernel(gemm_big_kernel<GEMM_STORE, BIG_BN, 1, WM, SPLIT>, grid, WM * 128, 0, s, g, tiles_m, tiles_n);
     }
+}
+
+static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
+    if (epi == GEMM_QKROPE) {
+        const int tiles_m = (g.M + BIG_BM - 1) / BIG_BM, tiles_n = g.N / BIG_BN;
+        launch_kernel(gemm_big_kernel<GEMM_QKROPE, BIG_BN>, tiles_m * tiles_n, STTD_BIG_WM * 128, 0, s, g, tiles_m,
+                      tiles_n);
+        return;
+    }
+    if (g.A_lo && STTD_BIG_SPLIT) launch_gemm_big_t<true>(g, epi, s);
+    else launch_gemm_big_t<false>(g, epi, s);
 }
 
 // ------------------------------------------------------------------ few rows (decode batches)

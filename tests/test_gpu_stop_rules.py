@@ -71,12 +71,17 @@ def test_stop_rules_planted_streams_match_the_oracle_loop():
     log(f"rows {got} truncated {trunc}")
 
 
-def test_stop_rules_in_a_replayed_batched_greedy_loop():
+@pytest.mark.parametrize("Bn", [3, 1])
+def test_stop_rules_in_a_replayed_batched_greedy_loop(Bn):
+    """Bn = 1 with a 256-position cache runs each step's projection and attention
+    as one launch (two attention splits): a stopped row (position -1) must leave
+    its cache alone there too."""
     sh = replace(DecoderShape(hidden=256, n_heads=4, n_kv_heads=2, head_dim=128, ffn=512), n_layers=2, vocab=2000)
     layers = [synth.block_weights(61, l, sh) for l in range(2)]
     E = synth.embedding(61, sh)
     g = synth.final_norm(61, sh)
-    Bn, T, n_ctx, max_new = 3, 12, 64, 20
+    T, max_new = 12, 20
+    n_ctx = 64 if Bn > 1 else 256
     x0 = synth.prefill_rows(61, Bn * T, sh.hidden)
 
     def loop(rules):
