@@ -299,7 +299,7 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
         g.seg_end[0] = qd; g.seg_end[1] = qd + kvd; g.seg_end[2] = qkv_cols;
         g.N = qkv_cols; g.C = ws->qkv; g.ldc = qkv_cols;
         // long prefills: per-head norm, RoPE and the cache write in the projection's epilogue
-        qk_fused = flash && !xn_lo && gemm_qkrope_fits(R, qkv_cols, H, d);
+        qk_fused = flash && gemm_qkrope_fits(R, qkv_cols, H, d) && (!xn_lo || gemm_split_large_tiles());
         if (qk_fused) g.qk = qr;
         ProfScope ps(STTD_KERN_QKV_GEMM, s);
         TRY(launch_gemm(g, qk_fused ? GEMM_QKROPE : GEMM_STORE, s));

@@ -254,7 +254,6 @@ template <int EPI, int BN, int KSPLIT = 1, int WM = STTD_BIG_WM, bool SPLIT = fa
 __global__ __launch_bounds__(WM * 128) void gemm_big_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     static_assert(EPI != GEMM_SWIGLU || BN == BIG_BN, "SwiGLU pairs gate and up inside 256-row weight tiles");
     static_assert(KSPLIT == 1 || EPI == GEMM_RESID, "split K adds into a residual");
-    static_assert(!SPLIT || EPI != GEMM_QKROPE, "the Q/K epilogue takes plain activations");
     constexpr int BK = SPLIT ? 32 : BIG_BK;          // K per staged tile
     constexpr int NT = WM * 128;                     // threads
     constexpr int WR = BIG_BM / WM;                  // rows per wave
@@ -500,8 +499,10 @@ bool gemm_qkrope_fits(int M, int N, int K, int head_dim) {
            ((M + BIG_BM - 1) / BIG_BM) * (N / BIG_BN) >= 256;
 }
 
+bool gemm_split_large_tiles() { return STTD_BIG_SPLIT != 0; }
+
 static bool big_tiles_fit(const GemmArgs& g, GemmEpi epi) {
-    if (epi == GEMM_QKROPE) return !g.A_lo && gemm_qkrope_fits(g.M, g.N, g.K, g.qk.d);
+    if (epi == GEMM_QKROPE) return (!g.A_lo || STTD_BIG_SPLIT) && gemm_qkrope_fits(g.M, g.N, g.K, g.qk.d);
     if (g.M < 1024 || g.K % BIG_BK || (g.A_lo && !STTD_BIG_SPLIT)) return false;
     // split activations into a residual: the large tiles only when 256 x 128 tiles
     // fill the CUs; narrower grids lose to the 64-row tiles' split K (1224 rows,
@@ -550,8 +551,12 @@ static void launch_gemm_big_t(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
 static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     if (epi == GEMM_QKROPE) {
         const int tiles_m = (g.M + BIG_BM - 1) / BIG_BM, tiles_n = g.N / BIG_BN;
-        launch_kernel(gemm_big_kernel<GEMM_QKROPE, BIG_BN>, tiles_m * tiles_n, STTD_BIG_WM * 128, 0, s, g, tiles_m,
-                      tiles_n);
+        if (g.A_lo)
+            launch_kernel(gemm_big_kernel<GEMM_QKROPE, BIG_BN, 1, STTD_BIG_WM, true>, tiles_m * tiles_n,
+                          STTD_BIG_WM * 128, 0, s, g, tiles_m, tiles_n);
+        else
+            launch_kernel(gemm_big_kernel<GEMM_QKROPE, BIG_BN>, tiles_m * tiles_n, STTD_BIG_WM * 128, 0, s, g, tiles_m,
+                          tiles_n);
         return;
     }
     if (g.A_lo && STTD_BIG_SPLIT) launch_gemm_big_t<true>(g, epi, s);

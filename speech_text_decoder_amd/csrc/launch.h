@@ -213,6 +213,8 @@ bool gemm_fuses_norm(int M, int K);
 // Whether launch_gemm takes GEMM_QKROPE for this shape: at least 1024 rows,
 // head_dim 128, and enough 256 x 256 tiles to fill the CUs.
 bool gemm_qkrope_fits(int M, int N, int K, int head_dim);
+// Whether the large tiles take split (hi/lo) activations (then GEMM_QKROPE does too).
+bool gemm_split_large_tiles();
 
 // ---- attention (kernels_attn.hip)
 // Split-K GQA attention of independent rows (decode, and prefill on f32 caches):
