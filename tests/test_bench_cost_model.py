@@ -40,6 +40,12 @@ def test_decode_attention_counts_real_cache_rows_only():
     assert cost("attn_rows", S, 1, 154) == (647_168, 1_261_568.0)
 
 
+def test_one_launch_projection_attention_is_the_sum_of_its_parts():
+    # the Q|K|V projection (16,805,888 B) and the attention over 154 keys (647,168 B)
+    # of one decode row in one launch: their bytes and flops add, nothing more
+    assert cost("qkv_attn", S, 1, 154) == (16_805_888 + 647_168, 16_777_216.0 + 1_261_568.0)
+
+
 def test_prefill_4096_rows_flops():
     T = 4096
     # causal: 4 x 2048 x 4096 x 4097 / 2
