@@ -7,7 +7,9 @@
 * the packed prefill job: 8 injected prompts of 153 rows (1224 rows per block
   call, above the 512-row precision switch) through 28 blocks, then one head
   call over each prompt's last row picked by row index on the device;
-* the same with ragged prompt lengths.
+* the same with ragged prompt lengths;
+* the batched-decode job: 16 rows with cache lengths 150-1500 through the
+  captured graph the benchmark replays, every row of 6 replays checked.
 
 Tolerances: per row, max |gpu - oracle| / RMS(oracle row) <= 3e-2 on hidden
 states and logits; ids equal wherever the oracle's top-2 margin exceeds 1e-2,
@@ -185,3 +187,69 @@ def test_stack28_packed_prefill_ragged_prompts_one_head_call():
         dense_h[a:b] = rng.standard_normal((b - a, sh.hidden)).astype(np.float32)
         start += Tb
     packed_stack_case(wl, Ts, ids_h, keep_h, dense_h)
+
+
+def test_batched_decode_b16_all_rows_through_the_replayed_graph():
+    """The batched-decode job as benchmarked: 16 rows with seeded cache lengths
+    150-1500 through the captured graph (28 block steps + head with device token
+    feedback and position bump), 6 replays. Every row of every replay is checked:
+    the oracle steps each row through its own slab, following the GPU's tokens,
+    and must agree on the logits (C-20) and on the ids (C-21)."""
+    wl = WORKLOADS["qwen3_1p7b_stack28_batched_decode_b16"]
+    sh = wl.shape
+    Bn, n_ctx, steps = wl.batch, wl.n_ctx, 6
+    lens = synth.context_lengths(wl.cfg_id, Bn, *wl.ctx_len_range)
+    layers, E, g, ol, Ef, gf = stack_weights(wl)
+    sess = DecoderSession(sh, layers, embed=E, final_norm=g, n_ctx=n_ctx, n_seq=Bn, max_rows=Bn)
+    stored = {}
+    for l in range(sh.n_layers):
+        for b in range(Bn):
+            k, v = synth.kv_fill(wl.cfg_id, l, b, int(lens[b]), sh, n_ctx)
+            kq, vq = synth.kv_stored(k, sh.kvdtype), synth.kv_stored(v, sh.kvdtype)
+            gk, gv = sess.kv_slab(l, b)
+            gk[:, :lens[b], :] = dev(kq.view(np.int16)).permute(1, 0, 2)
+            gv[:, :lens[b], :] = dev(vq.view(np.int16)).permute(1, 0, 2)
+            stored[l, b] = (kq, vq)
+    log("KV slabs filled")
+    x0 = synth.step_rows(wl.cfg_id, 0, Bn, sh.hidden)
+    x = dev(x0)
+    pos = dev(lens.astype(np.int32))
+    ids = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    logits = torch.zeros(Bn, sh.vocab, device="cuda")
+    bound = int(lens.max()) + steps + 1
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            sess.step(x, pos, pos_bound=bound)
+            sess.head(x, ids, logits=logits, next_x=x, pos=pos)
+    torch.cuda.synchronize()
+    g_logits, g_ids = [], []
+    for _ in range(steps):
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
+        g_logits.append(logits.cpu().numpy().copy())
+        g_ids.append(ids.cpu().numpy().copy())
+    assert pos.cpu().numpy().tolist() == (lens + steps).tolist()
+    assert sess.error_bits() == 0
+    sess.close()
+    errs = []
+    for b in range(Bn):
+        L = int(lens[b])
+        cache = O.KVCache(sh.n_layers, 1, L + steps + 1, sh.n_kv_heads, sh.head_dim)
+        for l in range(sh.n_layers):
+            kq, vq = stored[l, b]
+            cache.k[l, 0, :L] = synth.kv_widen(kq)
+            cache.v[l, 0, :L] = synth.kv_widen(vq)
+        xo = x0[b:b + 1].astype(np.float64)
+        o_logits = []
+        for k in range(steps):
+            xo = O.step_stack(xo, [L + k], [0], ol, sh, cache)
+            o_logits.append(O.final_logits(xo, gf, Ef, sh.rms_eps)[0])
+            xo = Ef[int(g_ids[k][b])][None]          # follow the GPU's token
+        errs += [check(g_logits[k][b:b + 1], o_logits[k][None], False, f"row {b} step {k} logits")
+                 for k in range(steps)]
+        check_ids([int(g_ids[k][b]) for k in range(steps)], o_logits, f"row {b} step")
+    log(f"16 rows x {steps} replays: logits max row-rel err {max(errs):.3g} (mean {np.mean(errs):.3g})")
