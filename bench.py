@@ -59,7 +59,7 @@ def traffic_bytes(name, rows):
 
 
 KERNEL_NAMES = ["rmsnorm", "qkv_gemv", "qkv_gemm", "qk_rope_kv", "attn_rows", "attn_prefill", "o_gemv", "o_gemm",
-                "gateup_gemv", "gateup_gemm", "down_gemv", "down_gemm", "lm_head", "block_step", "qkv_attn"]
+                "gateup_gemv", "gateup_gemm", "down_gemv", "down_gemm", "lm_head", "qkv_attn"]
 
 
 def parse():
@@ -79,8 +79,6 @@ def parse():
                     help="skip the 4096-row single-block prefill figure carried on the default line")
     ap.add_argument("--no-qkv-attn", action="store_true",
                     help="single decode rows: Q|K|V projection and attention as two launches (STTD_OPT_QKV_ATTN 0)")
-    ap.add_argument("--fused-step", action="store_true",
-                    help="single-row decode steps as one persistent launch per block (STTD_OPT_FUSED_STEP)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 3 times (scales HBM byte counters)")
     return ap.parse_args()
@@ -113,10 +111,6 @@ def kernel_cost(name, sh, rows, mean_keys=0.0):
         return rows * H * (4 + 4) + H * wb, 4.0 * rows * H
     if name == "qkv_attn":       # one decode row: Q|K|V projection and attention in one launch
         parts = [kernel_cost(n, sh, rows, mean_keys) for n in ("qkv_gemv", "attn_rows")]
-        return sum(p[0] for p in parts), sum(p[1] for p in parts)
-    if name == "block_step":     # the fused single-row step: every stage of one block in one launch
-        parts = [kernel_cost(n, sh, rows, mean_keys) for n in ("qkv_gemv", "attn_rows", "o_gemv", "gateup_gemv",
-                                                               "down_gemv")]
         return sum(p[0] for p in parts), sum(p[1] for p in parts)
     return 0, 0.0
 
@@ -304,7 +298,6 @@ def bench_greedy_stack(args, wl):
     g = synth.final_norm(wl.cfg_id, sh)
     x_host = synth.prefill_rows(wl.cfg_id, T, sh.hidden)
     sess = DecoderSession(sh, layers, embed=E, final_norm=g, n_ctx=wl.n_ctx, max_rows=T)
-    sess.set_fused_step(args.fused_step)
     sess.set_qkv_attn(not args.no_qkv_attn)
     if args.act_split is not None:
         sess.set_act_split(args.act_split)
@@ -378,7 +371,7 @@ def bench_greedy_stack(args, wl):
         "config": {"workload": wl.name, "layers": sh.n_layers, "hidden": sh.hidden, "heads": sh.n_heads,
                    "kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim, "ffn": sh.ffn, "vocab": sh.vocab,
                    "prefill_rows": T, "new_tokens": new_tokens, "batch": 1, "kv_dtype": sh.kvdtype,
-                   "n_ctx": wl.n_ctx, "parallelism": "none (1 GPU)", "fused_step": args.fused_step, "qkv_attn": not args.no_qkv_attn,
+                   "n_ctx": wl.n_ctx, "parallelism": "none (1 GPU)", "qkv_attn": not args.no_qkv_attn,
                    "act_split_above_512_rows": args.act_split if args.act_split is not None else 15},
     }
     if not args.no_kernel_profile:
@@ -562,7 +555,6 @@ def bench_block(args, wl):
     x_host = synth.prefill_rows(wl.cfg_id, T, sh.hidden)
     rows_host = np.stack([synth.step_rows(wl.cfg_id, k, 1, sh.hidden)[0] for k in range(n_steps)])
     sess = DecoderSession(sh, layers, n_ctx=wl.n_ctx, max_rows=T)
-    sess.set_fused_step(args.fused_step)
     sess.set_qkv_attn(not args.no_qkv_attn)
     # one block (the replicas are independent single blocks): plain bf16 activations
     # above 512 rows stay within the parity bound for a single block
@@ -627,7 +619,7 @@ def bench_block(args, wl):
         "config": {"workload": wl.name, "replicas": R, "hidden": sh.hidden, "heads": sh.n_heads,
                    "kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim, "ffn": sh.ffn, "prefill_rows": T,
                    "decode_steps": n_steps, "batch": 1, "kv_dtype": sh.kvdtype, "wdtype": sh.wdtype,
-                   "parallelism": "none (1 GPU)", "fused_step": args.fused_step, "qkv_attn": not args.no_qkv_attn,
+                   "parallelism": "none (1 GPU)", "qkv_attn": not args.no_qkv_attn,
                    "act_split_above_512_rows": args.act_split if args.act_split is not None else 0},
     }
     if R > 1:
@@ -778,7 +770,7 @@ def bench_batched(args, wl):
         "decode_step_hbm_frac": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "config": {"workload": wl.name, "layers": sh.n_layers, "batch": Bn, "steps": n_steps,
                    "ctx_len_range": list(wl.ctx_len_range), "mean_ctx": float(lens.mean()), "n_ctx": n_ctx,
-                   "kv_dtype": sh.kvdtype, "parallelism": "none (1 GPU)", "fused_step": args.fused_step, "qkv_attn": not args.no_qkv_attn},
+                   "kv_dtype": sh.kvdtype, "parallelism": "none (1 GPU)", "qkv_attn": not args.no_qkv_attn},
     }
     if not args.no_kernel_profile:
         with torch.cuda.stream(stream):

@@ -86,7 +86,7 @@ typedef struct sttd_workspace sttd_workspace; /* opaque */
 #define STTD_DEVERR_POSITION 1u /* a position was < 0 or >= the cache's n_ctx */
 #define STTD_DEVERR_SLAB 2u     /* a slab id was < 0 or >= the cache's n_seq */
 #define STTD_DEVERR_TOKEN 4u    /* a token id was < 0 or >= vocab */
-#define STTD_DEVERR_SYNC 8u     /* a fused decode step's stage hand-off timed out (200 ms); its outputs are invalid */
+#define STTD_DEVERR_SYNC 8u     /* a single-row projection + attention hand-off timed out (200 ms); its outputs are invalid */
 #define STTD_DEVERR_ROW 16u     /* a head row index was < 0 or >= n_x_rows */
 
 /* block_prefill flag: the FFN (and so the block output) is computed for the
@@ -134,20 +134,7 @@ sttd_status sttd_kv_cache_view(const sttd_kv_cache *kv, int layer, int seq, void
 sttd_status sttd_workspace_alloc(const sttd_block_params *p /* host */, int max_rows, int max_pos, int vocab,
                                  sttd_workspace **out /* host */);
 sttd_status sttd_workspace_free(sttd_workspace *ws);
-/* Workspace options (sttd_workspace_set_option).
- * STTD_OPT_FUSED_STEP, default 0: when 1, a single-row block_step with bf16 weights,
- * an f16 cache, head_dim 128, hidden and n_heads * head_dim up to 2048 and a
- * cache span of at most 1024 positions runs as one persistent launch whose
- * workgroups hand the five stages (Q|K|V projection, attention, O projection,
- * gate_up + SwiGLU, down projection) to one another through counters in the
- * workspace, in place of one launch per stage. The step graph on the Qwen3-ASR
- * decoder page (build_step_graph) is the same computation; this is a
- * scheduling choice; on MI355X it measured 33.9 us per 1.7B-shaped block
- * against 34.5 us for one launch per stage, hence the default. Results agree
- * with the per-stage launches to fp32 rounding (partial sums in another
- * order). Calls that share a workspace must not run concurrently: the
- * counters are per workspace. */
-#define STTD_OPT_FUSED_STEP 1
+/* Workspace options (sttd_workspace_set_option). */
 /* STTD_OPT_ACT_SPLIT, default 15: precision of the activations that feed the
  * bf16-weight MFMA projections. A split activation is carried as two bf16
  * parts, hi = bf16(v) and lo = bf16(v - hi), so the product sees about 16
@@ -354,9 +341,8 @@ typedef enum {
     STTD_KERN_DOWN_GEMV = 10,   /* down projection + residual, decode rows */
     STTD_KERN_DOWN_GEMM = 11,
     STTD_KERN_LM_HEAD = 12,     /* final RMSNorm + tied head + argmax */
-    STTD_KERN_BLOCK_STEP = 13,  /* the fused single-row decode step of one block (STTD_OPT_FUSED_STEP) */
-    STTD_KERN_QKV_ATTN = 14,    /* single decode row: Q|K|V projection + attention in one launch (STTD_OPT_QKV_ATTN) */
-    STTD_KERN_COUNT = 15
+    STTD_KERN_QKV_ATTN = 13,    /* single decode row: Q|K|V projection + attention in one launch (STTD_OPT_QKV_ATTN) */
+    STTD_KERN_COUNT = 14
 } sttd_kernel;
 
 sttd_status sttd_profile_enable(uint32_t mask);

@@ -16,7 +16,7 @@ OK, ERR_INVALID_ARG, ERR_OOM, ERR_BACKEND, ERR_CONTEXT_FULL, ERR_UNSUPPORTED = r
 F32, BF16, F16 = 0, 1, 2
 LAST_ROW_FFN_ONLY = 1
 DEVERR_POSITION, DEVERR_SLAB, DEVERR_TOKEN, DEVERR_SYNC, DEVERR_ROW = 1, 2, 4, 8, 16
-OPT_FUSED_STEP, OPT_ACT_SPLIT, OPT_QKV_ATTN = 1, 2, 3
+OPT_ACT_SPLIT, OPT_QKV_ATTN = 2, 3
 SPLIT_QKV, SPLIT_O, SPLIT_GATE_UP, SPLIT_DOWN = 1, 2, 4, 8
 SPLIT_ALL = 15
 

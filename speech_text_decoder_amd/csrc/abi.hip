@@ -40,15 +40,12 @@ struct sttd_workspace {
     unsigned long long* partials;  // [max_rows][kHeadPartials] head argmax partials
     uint32_t* err;                 // [1]
     int32_t* iota;                 // [max_rows]: 0, 1, ... (slab b of row b when no slab ids are given)
-    float* hbuf;                   // [hidden]: the fused step's attention residual
     int32_t* rowpos;               // [max_rows]: per-row positions of a packed batched prefill
     int32_t* rowseq;               // [max_rows]: per-row slabs of a packed batched prefill
-    uint32_t* sync;                // [kStepSyncWords] hand-off counters of the fused step (zero between launches)
     uint32_t* merge_ctr;           // [max_rows][n_kv] attention split counts (zero between launches)
     uint64_t* qtag;                // [(nq + 2 nkv) d] tagged projection words of a single decode row
     uint32_t* tag_gen;             // [1] the next hand-off tag (never 0)
     uint32_t* tag_done;            // [1] hand-off consumers counted out (zero between launches)
-    bool fused_step;               // STTD_OPT_FUSED_STEP
     bool qkv_attn;                 // STTD_OPT_QKV_ATTN
     uint32_t split_mask;           // STTD_OPT_ACT_SPLIT: GEMM inputs kept as bf16 high + low parts at any row count
 };
@@ -144,7 +141,6 @@ constexpr int kGemvMaxRows = 4;    // rows beyond this take the MFMA GEMMs (bf16
 constexpr int kSplitMaxRows = 512; // up to here the GEMMs are HBM-bound: split activations (hi + lo)
 constexpr int kMaxSplits = 64;
 constexpr int kHeadPartials = 1024;  // workgroups of the persistent head GEMV
-constexpr int kFusedMaxSpan = 1024;  // cache span of the fused step: at most 8 attention splits of 128 rows
 
 sttd_status from_hip(hipError_t e) {
     if (e == hipSuccess) return STTD_OK;
@@ -252,27 +248,6 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
     uint16_t* act = (uint16_t*)ws->act;
     uint16_t* act_lo = split_all || (sm & STTD_SPLIT_DOWN) ? act + (size_t)ws->max_rows * I : nullptr;
 
-    // --- a single decode row: the whole block as one persistent launch
-    if (!prefill && R == 1 && ws->fused_step) {
-        // attention splits of 64 cache rows (128 past 512 rows), at most 8: the
-        // O stage merges the partials as it loads them
-        const int span = pos_bound <= 8 * 64 ? 64 : 128;
-        const int splits = (pos_bound + span - 1) / span;
-        if (pos_bound <= kFusedMaxSpan &&
-            step_fused_supported(H, nq, nkv, d, I, splits, wt, kl.type)) {
-            StepFusedArgs a{};
-            a.attn_norm = w->attn_norm; a.wq = w->wq; a.wk = w->wk; a.wv = w->wv; a.q_norm = w->q_norm;
-            a.k_norm = w->k_norm; a.wo = w->wo; a.ffn_norm = w->ffn_norm; a.w_gate_up = w->w_gate_up;
-            a.w_down = w->w_down;
-            a.H = H; a.n_heads = nq; a.n_kv = nkv; a.d = d; a.I = I; a.eps = eps;
-            a.rope = ws->rope; a.max_pos = ws->max_pos; a.rm = rm; a.kv = kl; a.n_splits = splits;
-            a.x = x; a.qkv = ws->qkv; a.part = ws->part; a.attn_o = ws->attn_o; a.act = ws->act;
-            a.h = ws->hbuf; a.sync = ws->sync; a.err = ws->err;
-            ProfScope ps(STTD_KERN_BLOCK_STEP, s);
-            TRY(launch_step_fused(a, s));
-            return STTD_OK;
-        }
-    }
     // --- a single decode row: the Q|K|V projection and the attention in one launch
     // (tagged hand-off), when the shape allows and the attention splits merge in the
     // O projection
@@ -558,8 +533,6 @@ sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int m
     const size_t o_partials = take(R * kHeadPartials * sizeof(unsigned long long));
     const size_t o_err = take(sizeof(uint32_t));
     const size_t o_iota = take(R * sizeof(int32_t));
-    const size_t o_sync = take(kStepSyncWords * sizeof(uint32_t));
-    const size_t o_h = take((size_t)H * sizeof(float));
     const size_t o_rowpos = take(R * sizeof(int32_t));
     const size_t o_rowseq = take(R * sizeof(int32_t));
     const size_t o_merge = take(R * nkv * sizeof(uint32_t));
@@ -589,15 +562,12 @@ sttd_status sttd_workspace_alloc(const sttd_block_params* p, int max_rows, int m
     ws->partials = (unsigned long long*)(b + o_partials);
     ws->err = (uint32_t*)(b + o_err);
     ws->iota = (int32_t*)(b + o_iota);
-    ws->sync = (uint32_t*)(b + o_sync);
-    ws->hbuf = (float*)(b + o_h);
     ws->rowpos = (int32_t*)(b + o_rowpos);
     ws->rowseq = (int32_t*)(b + o_rowseq);
     ws->merge_ctr = (uint32_t*)(b + o_merge);
     ws->qtag = (uint64_t*)(b + o_qtag);
     ws->tag_gen = (uint32_t*)(b + o_tag);
     ws->tag_done = ws->tag_gen + 1;
-    ws->fused_step = false;
     ws->qkv_attn = true;
     ws->split_mask = STTD_SPLIT_QKV | STTD_SPLIT_O | STTD_SPLIT_GATE_UP | STTD_SPLIT_DOWN;
     // RoPE table in fp64 on the host: pair i of position pos turns by pos * theta^(-2i/d)
@@ -635,10 +605,6 @@ sttd_status sttd_workspace_free(sttd_workspace* ws) {
 
 sttd_status sttd_workspace_set_option(sttd_workspace* ws, int option, int value) {
     if (!ws) return STTD_ERR_INVALID_ARG;
-    if (option == STTD_OPT_FUSED_STEP && (value == 0 || value == 1)) {
-        ws->fused_step = value == 1;
-        return STTD_OK;
-    }
     if (option == STTD_OPT_QKV_ATTN && (value == 0 || value == 1)) {
         ws->qkv_attn = value == 1;
         return STTD_OK;

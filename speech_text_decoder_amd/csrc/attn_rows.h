@@ -1,6 +1,6 @@
 // attn_rows.h - split-K grouped-query attention of independent rows (one
 // workgroup item: row r, KV head j, split), used by the rows attention
-// kernel and by the fused decode-step kernel.
+// kernel and by the single-row projection + attention launch.
 #pragma once
 
 #include <type_traits>

@@ -79,12 +79,9 @@ __device__ __forceinline__ void load8(const float* p, float* o, F32) {
 // Access policies for fp32 data exchanged between workgroups. PlainMem uses
 // ordinary loads and stores. PubMem ("publish") uses ordinary loads but
 // device-scope relaxed atomic stores (sc1 on gfx950), which write through the
-// writer's L2 to memory. The fused decode step writes every value that another
-// workgroup of the same launch reads with PubMem, waits for the stores to
-// complete, then counts the hand-off. Each such buffer is written once per
-// launch, in one stage, and read only after that stage's hand-off. Kernel
-// boundaries invalidate the L2s, so no L2 holds a stale copy of its lines, and
-// the readers' plain loads fill from memory and share the fill across the XCD.
+// writer's L2 to memory. The attention splits publish their partial records
+// this way, wait for the stores to complete, then count themselves in; the last
+// one of a (row, KV head) reads them all with device-scope loads and merges them.
 struct PlainMem {
     static __device__ __forceinline__ float ld(const float* p) { return *p; }
     static __device__ __forceinline__ void ld8(const float* p, float* o) { load8(p, o, F32()); }

@@ -1,7 +1,7 @@
 // gemv_ops.h - device pieces of the bandwidth-bound projections (decode
 // rows): 16-byte weight loads, activation chunks with the RMSNorm
 // statistics, dot products and the cross-wave merge. Used by the GEMV
-// kernels and by the fused decode-step kernel.
+// kernels and by the single-row projection + attention launch.
 #pragma once
 
 #include "common.h"

@@ -253,32 +253,6 @@ hipError_t launch_qkv_attn(const QkvTagArgs& p, RowMap rm, KVLayer kv, int n_spl
 hipError_t launch_attn_prefill(const uint16_t* q16, int64_t ldq, int T, int pos0, int seq, int n_heads, KVLayer kv,
                                uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo, hipStream_t s);
 
-// ---- fused decode step (kernels_step.hip): one block for one decode row in
-// a single persistent launch. Workgroups hand the stages (Q|K|V projection,
-// attention, O projection, gate_up + SwiGLU, down projection) to one another
-// through counters in `sync` instead of kernel boundaries.
-constexpr uint32_t kDevErrSync = 8u;  // a stage hand-off timed out (STTD_DEVERR_SYNC)
-constexpr int kStepSyncWords = 6 * 64 * 64;  // counters: 6 rows of 64 sub-counters, 256 bytes apart
-struct StepFusedArgs {
-    const void *attn_norm, *wq, *wk, *wv, *q_norm, *k_norm, *wo, *ffn_norm, *w_gate_up, *w_down;
-    int H, n_heads, n_kv, d, I;
-    float eps;
-    const float* rope;
-    int max_pos;
-    RowMap rm;       // device position and slab of the row
-    KVLayer kv;
-    int n_splits;    // attention splits of the row's cache span
-    float* x;        // [1, H] fp32, in/out
-    float* qkv;      // [1, (n_heads + 2 n_kv) d] scratch
-    float* part;     // [n_heads][n_splits][d + 4] split partials
-    float* attn_o;   // [1, n_heads d] (one split)
-    float* act;      // [1, I] scratch
-    float* h;        // [1, H] scratch: the attention residual x + o W_o^T
-    uint32_t* sync;  // kStepSyncWords words, zero before the launch and zero again after it
-    uint32_t* err;
-};
-// Whether the fused step is built for this shape (bf16 weights, f16 cache).
-bool step_fused_supported(int H, int n_heads, int n_kv, int d, int I, int n_splits, WType wt, KVType kt);
-hipError_t launch_step_fused(const StepFusedArgs& a, hipStream_t s);
+constexpr uint32_t kDevErrSync = 8u;  // a tagged hand-off poll timed out (STTD_DEVERR_SYNC)
 
 }  // namespace sttd

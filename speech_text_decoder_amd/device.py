@@ -118,10 +118,6 @@ class DecoderSession:
         return (_wrap(k, n, dt, self.device).view(sh.n_kv_heads, self.n_ctx, sh.head_dim),
                 _wrap(v, n, dt, self.device).view(sh.n_kv_heads, self.n_ctx, sh.head_dim))
 
-    def set_fused_step(self, enabled: bool):
-        """STTD_OPT_FUSED_STEP: single-row steps as one persistent launch per block (default off)."""
-        B.workspace_set_option(self.ws, B.OPT_FUSED_STEP, 1 if enabled else 0)
-
     def set_qkv_attn(self, enabled: bool):
         """STTD_OPT_QKV_ATTN: a single decode row's projection and attention in one launch (default on)."""
         B.workspace_set_option(self.ws, B.OPT_QKV_ATTN, 1 if enabled else 0)

@@ -47,7 +47,7 @@ def test_null_and_bad_arguments_rejected_on_host():
     assert L.sttd_embed_gather(None, B.BF16, 10, 256, 1, None, None, None, None) == B.ERR_INVALID_ARG
     assert L.sttd_kv_cache_free(None) == B.ERR_INVALID_ARG
     assert L.sttd_workspace_free(None) == B.ERR_INVALID_ARG
-    assert L.sttd_workspace_set_option(None, B.OPT_FUSED_STEP, 0) == B.ERR_INVALID_ARG
+    assert L.sttd_workspace_set_option(None, B.OPT_QKV_ATTN, 0) == B.ERR_INVALID_ARG
     out = ctypes.c_void_p()
     assert L.sttd_kv_cache_alloc(0, 1, 16, 2, 64, B.F16, ctypes.byref(out)) == B.ERR_INVALID_ARG
     assert L.sttd_kv_cache_alloc(1, 1, 16, 2, 96, B.F16, ctypes.byref(out)) == B.ERR_UNSUPPORTED
