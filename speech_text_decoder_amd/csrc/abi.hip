@@ -204,7 +204,10 @@ KVLayer kv_layer(const sttd_kv_cache* kv, int layer) {
 // 150-1500 positions: 256 workgroups of 8 waves beat 512 of 4 and any larger grid;
 // 256 workgroups dealt to the rows by length (22.8 us per block) and one split per
 // row (27.8 us) both lost to two equal splits per row (21.0 us): the split merge
-// costs a write-through, an atomic and a reload, not the streaming).
+// costs a write-through, an atomic and a reload, not the streaming). Splits per
+// row that follow each row's own length (ceil(keys / span), up to 8, the spare
+// workgroups exiting at once) lost too: 17.9 us per block against 22.9, 25.5 and
+// 28.0 us at spans of 384, 512 and 256 rows.
 int choose_splits(int rows, int n_kv, int pos_bound, int part_cap) {
     int s = (pos_bound + 127) / 128;
     // long single rows: fewer, longer splits (8-wave workgroups) and one combine
