@@ -204,6 +204,194 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 }
 
 
+// ------------------------------------------------------------------ mid-M, weights streamed
+// C = A W^T for a few hundred rows, where one K-step in flight per workgroup
+// leaves each step waiting on its loads. Tile (16 FM) x (64 FN) per workgroup of
+// 4 waves; every wave owns all 16 FM rows and FN column fragments of its own, so
+// its weight rows go from global memory straight into B fragments (lane l:
+// column l % 16, K elements (l / 16) * 8 .. + 8 of each 32-deep half-step) and
+// only A (bf16 high and low planes) is staged, through two LDS buffers, once per
+// workgroup. Loads run D K-steps of 64 ahead in a register ring: the loads of
+// step t + D are issued as soon as step t has fed the MFMAs, so D - 1 steps of
+// MFMA work cover each load's latency. Per 32-deep half-step a wave reads 2 FM
+// A fragments from LDS for 2 FM FN MFMAs.
+// SWIGLU: fragments [0, FN/2) of a wave are gate columns, [FN/2, FN) the up
+// columns of the same act columns.
+template <int EPI, int FM, int FN, int D, bool SPLIT>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
+    constexpr int BM = FM * 16, BN = FN * 64;
+    constexpr int AVT = BM * BK / 8;            // 16-byte vectors of one A plane per K-step
+    constexpr int AV = (AVT + 255) / 256;       // per thread
+    constexpr int NP = SPLIT ? 2 : 1;           // A planes
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][NP][BM * LDS_STRIDE];
+
+    clock_begin(g.clk);
+    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
+    const int m0 = blockIdx.y * BM;
+    const int tile_n = blockIdx.x;
+
+    // weight row of each of this lane's column fragments
+    const uint16_t* wrow[FN];
+    bool wok[FN];
+#pragma unroll
+    for (int f = 0; f < FN; ++f) {
+        if (EPI == GEMM_SWIGLU) {
+            const int c = tile_n * (BN / 2) + wave * (FN / 2) * 16 + (f % (FN / 2)) * 16 + lane % 16;
+            wok[f] = c < g.N;
+            const int cc = wok[f] ? c : 0;
+            wrow[f] = g.w[0] + (int64_t)(f < FN / 2 ? cc : g.N + cc) * g.K;
+        } else {
+            const int n0 = tile_n * BN + wave * FN * 16 + f * 16 + lane % 16;
+            wok[f] = n0 < g.N;
+            const int n = wok[f] ? n0 : 0;
+            const bool s2 = n >= g.seg_end[1], s1 = n >= g.seg_end[0];
+            const int grow = n - (s2 ? g.seg_end[1] : (s1 ? g.seg_end[0] : 0));
+            wrow[f] = (s2 ? g.w[2] : (s1 ? g.w[1] : g.w[0])) + (int64_t)grow * g.K;
+        }
+        wrow[f] += (lane / 16) * 8;
+    }
+    // A rows this thread stages: vector v = tid + 256 i is row v / 8, 16-byte chunk v % 8
+    const uint16_t* aptr[AV];
+    const uint16_t* alptr[AV];
+    bool aok[AV], astage[AV];
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+        const int v = tid + i * 256;
+        astage[i] = v < AVT;
+        const int r = astage[i] ? v / 8 : 0;
+        aok[i] = astage[i] && m0 + r < g.M;
+        const int64_t off = (int64_t)(aok[i] ? m0 + r : 0) * g.lda + (v % 8) * 8;
+        aptr[i] = g.A + off;
+        alptr[i] = SPLIT ? g.A_lo + off : g.A + off;
+    }
+
+    // K range of this workgroup: split over gridDim.z (partial sums add with atomics)
+    const int nk_all = g.K / BK;
+    const int nk_per = (nk_all + gridDim.z - 1) / gridDim.z;
+    const int kt0 = min((int)blockIdx.z * nk_per, nk_all);
+    const int nk = min(nk_per, nk_all - kt0);
+    const int64_t kbase = (int64_t)kt0 * BK;
+
+    u32x4 ra[D][NP][AV], rb[D][FN][2];
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int f = 0; f < FN; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Every fetch is unconditional (steps past the end reload the last one, rows
+    // past M reload a valid row and are zeroed when staged), so the number of
+    // loads issued after each ring slot is fixed and each wait covers only its
+    // own slot.
+#define STREAM_FETCH(U, KT)                                                                  \
+    do {                                                                                     \
+        const int64_t k0_ = kbase + (int64_t)min((KT), nk - 1) * BK;                         \
+        _Pragma("unroll") for (int i = 0; i < AV; ++i) {                                     \
+            ra[U][0][i] = *reinterpret_cast<const u32x4*>(aptr[i] + k0_);                    \
+            if (SPLIT) ra[U][NP - 1][i] = *reinterpret_cast<const u32x4*>(alptr[i] + k0_);   \
+        }                                                                                    \
+        _Pragma("unroll") for (int f = 0; f < FN; ++f) {                                     \
+            rb[U][f][0] = *reinterpret_cast<const u32x4*>(wrow[f] + k0_);                     \
+            rb[U][f][1] = *reinterpret_cast<const u32x4*>(wrow[f] + k0_ + 32);                \
+        }                                                                                    \
+    } while (0)
+
+    if (nk > 0) {
+        // slot by slot, so the oldest slot's loads are the oldest in flight on every pass
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            STREAM_FETCH(u, u);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int kb = 0; kb < nk; kb += D) {
+#pragma unroll
+            for (int u = 0; u < D; ++u) {
+                const int kt = kb + u;
+                // stage this step's A planes (buffer kt & 1 was last read two steps
+                // ago, before every wave passed the previous step's barrier)
+                uint16_t(*buf)[BM * LDS_STRIDE] = As[kt & 1];
+#pragma unroll
+                for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+                    for (int i = 0; i < AV; ++i) {
+                        if (!astage[i]) continue;
+                        const int v = tid + i * 256;
+                        const u32x4 z{0u, 0u, 0u, 0u};
+                        *reinterpret_cast<u32x4*>(&buf[pl][lds_off(v / 8, v % 8)]) = aok[i] ? ra[u][pl][i] : z;
+                    }
+                __syncthreads();
+                __builtin_amdgcn_sched_barrier(0);
+                if (kt < nk) {
+                    // all of the step's A fragments are read first (one wave per SIMD has
+                    // no other wave to cover LDS latency), then the MFMAs run plane by
+                    // plane, so FM FN independent products separate two on one accumulator
+                    bf16x8 af[2][NP][FM];
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                        for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+                            for (int i = 0; i < FM; ++i)
+                                af[ks][pl][i] = *reinterpret_cast<const bf16x8*>(
+                                    &buf[pl][lds_off(i * 16 + lane % 16, ks * 4 + lane / 16)]);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                        for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+                            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                                for (int f = 0; f < FN; ++f)
+                                    acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                        af[ks][pl][i], __builtin_bit_cast(bf16x8, rb[u][f][ks]), acc[i][f], 0, 0, 0);
+                }
+                // keep the compiler from moving this slot's refetch above its use
+                __builtin_amdgcn_sched_barrier(0);
+                STREAM_FETCH(u, kt + D);
+            }
+        }
+    }
+#undef STREAM_FETCH
+
+    // epilogue: lane l holds column l % 16 and rows (l / 16) * 4 + rr of each fragment
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int m = m0 + i * 16 + (lane / 16) * 4 + rr;
+            if (m >= g.M) continue;
+            if (EPI == GEMM_SWIGLU) {
+#pragma unroll
+                for (int f = 0; f < FN / 2; ++f) {
+                    if (!wok[f]) continue;
+                    const int c = tile_n * (BN / 2) + wave * (FN / 2) * 16 + f * 16 + lane % 16;
+                    const float gt = acc[i][f][rr], up = acc[i][f + FN / 2][rr];
+                    const float a = gt / (1.0f + expf(-gt)) * up;
+                    uint16_t hi, lo;
+                    split_bf16(a, hi, lo);
+                    g.Cb[(int64_t)m * g.ldcb + c] = hi;
+                    if (g.Cb_lo) g.Cb_lo[(int64_t)m * g.ldcb + c] = lo;
+                }
+            } else {
+#pragma unroll
+                for (int f = 0; f < FN; ++f) {
+                    if (!wok[f]) continue;
+                    const int n = tile_n * BN + wave * FN * 16 + f * 16 + lane % 16;
+                    float* dst = g.C + (int64_t)m * g.ldc + n;
+                    if (EPI == GEMM_RESID) {
+                        if (gridDim.z == 1) *dst += acc[i][f][rr];
+                        else atomicAdd(dst, acc[i][f][rr]);
+                    } else {
+                        *dst = acc[i][f][rr];
+                    }
+                }
+            }
+        }
+    }
+    clock_end(g.clk);
+}
+
 // ------------------------------------------------------------------ large-M tiles
 // For prefills of many rows (the GEMMs are MFMA-bound there): 256 x 256 output
 // tiles, 8 waves in 4 x 2 each owning 64 x 128 (4 x 8 fragments of
@@ -823,12 +1011,61 @@ static hipError_t launch_gemm_bm(const GemmArgs& g, GemmEpi epi, hipStream_t s) 
     return hipSuccess;
 }
 
+#ifndef STTD_STREAM_D
+#define STTD_STREAM_D 4
+#endif
+#ifndef STTD_STREAM_WGS
+#define STTD_STREAM_WGS 256
+#endif
+#ifndef STTD_STREAM_FM
+#define STTD_STREAM_FM 0
+#endif
+#ifndef STTD_STREAM_MAX_ROWS
+#define STTD_STREAM_MAX_ROWS 320
+#endif
+
+template <int FM, bool SPLIT>
+static hipError_t launch_gemm_stream_fm(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
+    constexpr int FN = 2, BN = FN * 64, D = STTD_STREAM_D;
+    const unsigned gy = (g.M + FM * 16 - 1) / (FM * 16);
+    if (epi == GEMM_SWIGLU) {
+        launch_kernel(gemm_stream_kernel<GEMM_SWIGLU, FM, FN, D, SPLIT>, dim3((g.N + BN / 2 - 1) / (BN / 2), gy, 1),
+                      256, 0, s, g);
+        return hipSuccess;
+    }
+    dim3 grid((g.N + BN - 1) / BN, gy, 1);
+    // split K over workgroups (atomic adds into C, which a STORE zeroes first) while
+    // the grid stays within about STTD_STREAM_WGS and each split keeps 2 D K-steps
+    while (grid.x * grid.y * grid.z * 2 <= STTD_STREAM_WGS && g.K / BK >= (int)grid.z * 2 * 2 * D) grid.z *= 2;
+    if (epi == GEMM_STORE && grid.z > 1 && g.ldc != g.N) grid.z = 1;  // zeroing needs contiguous rows
+    if (epi == GEMM_STORE && grid.z > 1) {
+        const hipError_t e = launch_fill_zero(g.C, (size_t)g.M * g.N * sizeof(float), s);
+        if (e != hipSuccess) return e;
+        launch_kernel(gemm_stream_kernel<GEMM_RESID, FM, FN, D, SPLIT>, grid, 256, 0, s, g);
+    } else if (epi == GEMM_RESID) {
+        launch_kernel(gemm_stream_kernel<GEMM_RESID, FM, FN, D, SPLIT>, grid, 256, 0, s, g);
+    } else {
+        launch_kernel(gemm_stream_kernel<GEMM_STORE, FM, FN, D, SPLIT>, grid, 256, 0, s, g);
+    }
+    return hipSuccess;
+}
+
+// 80-row tiles where they pad fewer rows than 64-row ones (153 rows: 160 against 192)
+template <bool SPLIT>
+static hipError_t launch_gemm_stream(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
+    const int pad64 = (g.M + 63) / 64 * 64, pad80 = (g.M + 79) / 80 * 80;
+    if (STTD_STREAM_FM == 4) return launch_gemm_stream_fm<4, SPLIT>(g, epi, s);
+    if (STTD_STREAM_FM == 5) return launch_gemm_stream_fm<5, SPLIT>(g, epi, s);
+    return pad80 < pad64 ? launch_gemm_stream_fm<5, SPLIT>(g, epi, s) : launch_gemm_stream_fm<4, SPLIT>(g, epi, s);
+}
+
 // 64-row tiles. One 160-row tile per workgroup (every row of a 153-row prefill, so
 // each weight tile streams once) measured slower at 153 rows: gate_up 42.8 -> 59.4 us,
 // QKV 19.3 -> 26.2, O 14.3 -> 18.2, down 24.7 -> 31.5 (fewer, larger workgroups at
 // one or two waves per SIMD hide less of each K-step's load latency).
 template <bool SPLIT>
 static hipError_t launch_gemm_t(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
+    if (g.M <= STTD_STREAM_MAX_ROWS) return launch_gemm_stream<SPLIT>(g, epi, s);
     return launch_gemm_bm<64, SPLIT>(g, epi, s);
 }
 
