@@ -217,6 +217,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 // A fragments from LDS for 2 FM FN MFMAs.
 // SWIGLU: fragments [0, FN/2) of a wave are gate columns, [FN/2, FN) the up
 // columns of the same act columns.
+// What bounds it (153 rows, gate_up): the bytes each CU requests. With one
+// workgroup per CU a CU keeps about 32 KB of loads in flight, which at loaded
+// latencies is ~20 GB/s from HBM and ~40 GB/s from L2; each workgroup requests
+// 512 KB of weights and 640 KB of A planes. Timed alone (in an 8-wave form of
+// this kernel), the weight loads took
+// 27 us, the A loads 17 us, the LDS staging and MFMAs without global loads 24 us,
+// and the loads alone (no LDS, no MFMA) 34.5 us, about the whole kernel. Measured
+// and not kept: 8 waves with the K-step halves split between wave pairs (two
+// waves per SIMD), each K-half wave walking a contiguous K range, and per-
+// workgroup rotation of the K order (all within 1 us); ring depth 3, 4 and 6
+// (36, 36 and 40 us against 34 us at 2); 64-row tiles at 153 rows (three row
+// tiles, 288 workgroups: 46 us).
 template <int EPI, int FM, int FN, int D, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
     constexpr int BM = FM * 16, BN = FN * 64;
@@ -1012,7 +1024,7 @@ static hipError_t launch_gemm_bm(const GemmArgs& g, GemmEpi epi, hipStream_t s) 
 }
 
 #ifndef STTD_STREAM_D
-#define STTD_STREAM_D 4
+#define STTD_STREAM_D 2
 #endif
 #ifndef STTD_STREAM_WGS
 #define STTD_STREAM_WGS 256
