@@ -33,16 +33,16 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
 # 256 MiB copy (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0); valid only for the kernel
 # sources they were taken on (sha256 of the listed files).
 _GEMV_SRC = {"files": ["kernels_gemv.hip", "gemv_ops.h", "common.h"],
-             "sha256": "5074de34d4c5191f4503036246fd861744278baa79dddd23fa15bdc1047169aa",
+             "sha256": "61559bc4b654f52a712d932bd64df4c51df3266b13d70bdf7e85e84edd853489",
              "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
 _QA_SRC = {"files": ["kernels_attn.hip", "attn_rows.h", "gemv_ops.h", "common.h"],
-           "sha256": "c9da32352429a20ee513097b8bfb64a9c9d920be755072860b1adc0723e30dbc",
+           "sha256": "9a0d081da452f27fc37b5a634707e49644b689b074a618640f0a666bfb51de34",
            "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
 TRAFFIC = {
-    "o_gemv": dict(_GEMV_SRC, rows=1, bytes=8676417),
-    "gateup_gemv": dict(_GEMV_SRC, rows=1, bytes=50579443),
-    "down_gemv": dict(_GEMV_SRC, rows=1, bytes=25508068),
-    "qkv_attn": dict(_QA_SRC, rows=1, bytes=18083938),
+    "o_gemv": dict(_GEMV_SRC, rows=1, bytes=8676515),
+    "gateup_gemv": dict(_GEMV_SRC, rows=1, bytes=50579903),
+    "down_gemv": dict(_GEMV_SRC, rows=1, bytes=25508355),
+    "qkv_attn": dict(_QA_SRC, rows=1, bytes=18083250),
 }
 
 
