@@ -153,6 +153,9 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
 // Taking the O projection into this launch too (its workgroups polling per-split
 // ready words) measured 20.7 us against 10.6 + 6.5 us for the two launches: they
 // saw the last split's word 2-5 us after it was set, then needed 2.6 us more.
+// Merging the splits in this launch instead (the last split of each KV head merges
+// them, as the batched rows do) took the O projection from 4.58 to 2.54 us but this
+// launch from 8.53 to 11.15 us: 949 -> 926 tok/s on the 28-block greedy job.
 // Fewer, longer attention splits (4 of 256 cache rows, or 2 of 512) halve what the
 // O projection merges (4.51 -> 4.11 us) but lengthen this launch (8.45 -> 8.64 and
 // 9.34 us): 950 against 943 and 918 tok/s, so splits stay at 128 rows.
