@@ -965,6 +965,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 // flight: gate_up 17.4 -> 21.4 us, QKV (32 columns per workgroup) 8.1 -> 15.0 us.
 // So did 8 waves per workgroup splitting K eight ways (two waves per SIMD, twice
 // the loads in flight per CU): 16 rows, 7.99k -> 7.93k tok/s, down 10.8 -> 11.7 us.
+// So did two batch buffers again with every load unconditional and the waits
+// checked in the ISA to cover one step each (batches of 4, 3 and 2 steps): gate_up
+// 16.8 -> 19.6, 20.1 and 18.0 us, 8.05k -> 7.38k, 7.25k and 7.88k tok/s.
 #ifndef STTD_SKINNY_RESID_WGS
 #define STTD_SKINNY_RESID_WGS 256
 #endif
