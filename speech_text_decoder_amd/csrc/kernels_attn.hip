@@ -156,6 +156,10 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
 // Merging the splits in this launch instead (the last split of each KV head merges
 // them, as the batched rows do) took the O projection from 4.58 to 2.54 us but this
 // launch from 8.53 to 11.15 us: 949 -> 926 tok/s on the 28-block greedy job.
+// Taking the split count per launch from the row's position (ceil((pos + 1) / 128)
+// splits, so the O projection merges 2-4 records instead of 8 at 153-408 cached
+// rows) took the O projection from 4.26 to 4.10 us but this launch from 8.54 to
+// 9.42 us: eight short splits finish sooner than a few long ones (953 -> 932 tok/s).
 // Fewer, longer attention splits (4 of 256 cache rows, or 2 of 512) halve what the
 // O projection merges (4.51 -> 4.11 us) but lengthen this launch (8.45 -> 8.64 and
 // 9.34 us): 950 against 943 and 918 tok/s, so splits stay at 128 rows.
