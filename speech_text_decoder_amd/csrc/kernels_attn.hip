@@ -265,6 +265,10 @@ hipError_t launch_qkv_attn(const QkvTagArgs& p, RowMap rm, KVLayer kv, int n_spl
 // 8g + j holds key 4g + j (j < 4) or 16 + 4g + j - 4 (j >= 4). K and V^T are
 // double-buffered in LDS; the next block's rows load while the current one
 // computes. Exponentials in base 2 on scores scaled by log2(e) / sqrt(d).
+// One 16-row fragment per wave instead of two (64-row tiles, half the O and score
+// registers) measured slower at 4096 rows: 121 -> 160 us, and 139 us with the
+// registers held to 128 for two workgroups per CU (four waves per SIMD): each K and
+// V^T fragment read then feeds one MFMA instead of two.
 constexpr float kLazy = 8.f;  // lazy-rescale threshold of the flash kernel (base-2 exponent)
 
 template <int D>
