@@ -268,7 +268,10 @@ hipError_t launch_qkv_attn(const QkvTagArgs& p, RowMap rm, KVLayer kv, int n_spl
 // One 16-row fragment per wave instead of two (64-row tiles, half the O and score
 // registers) measured slower at 4096 rows: 121 -> 160 us, and 139 us with the
 // registers held to 128 for two workgroups per CU (four waves per SIMD): each K and
-// V^T fragment read then feeds one MFMA instead of two.
+// V^T fragment read then feeds one MFMA instead of two. Computing each block's
+// scores one iteration ahead (K staged a block ahead of V, so the S MFMAs of block
+// kb + 1 could overlap block kb's softmax; 240 VGPRs, no spills) measured slower
+// too: 126 -> 130-135 us.
 constexpr float kLazy = 8.f;  // lazy-rescale threshold of the flash kernel (base-2 exponent)
 
 template <int D>
