@@ -36,13 +36,13 @@ _GEMV_SRC = {"files": ["kernels_gemv.hip", "gemv_ops.h", "common.h"],
              "sha256": "61559bc4b654f52a712d932bd64df4c51df3266b13d70bdf7e85e84edd853489",
              "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
 _QA_SRC = {"files": ["kernels_attn.hip", "attn_rows.h", "gemv_ops.h", "common.h"],
-           "sha256": "9a0d081da452f27fc37b5a634707e49644b689b074a618640f0a666bfb51de34",
+           "sha256": "eb43cd1591210cc9f152c4b708dea536017311b151dda4ea12a8c161b23d632b",
            "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
 TRAFFIC = {
-    "o_gemv": dict(_GEMV_SRC, rows=1, bytes=8676515),
-    "gateup_gemv": dict(_GEMV_SRC, rows=1, bytes=50579903),
-    "down_gemv": dict(_GEMV_SRC, rows=1, bytes=25508355),
-    "qkv_attn": dict(_QA_SRC, rows=1, bytes=18083250),
+    "o_gemv": dict(_GEMV_SRC, rows=1, bytes=8676511),
+    "gateup_gemv": dict(_GEMV_SRC, rows=1, bytes=50580089),
+    "down_gemv": dict(_GEMV_SRC, rows=1, bytes=25508367),
+    "qkv_attn": dict(_QA_SRC, rows=1, bytes=18083790),
 }
 
 
