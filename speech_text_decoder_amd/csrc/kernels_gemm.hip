@@ -767,6 +767,9 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     else launch_gemm_big_t<false>(g, epi, s);
 }
 
+#ifndef STTD_SKINNY_CA
+#define STTD_SKINNY_CA 1
+#endif
 // ------------------------------------------------------------------ few rows (decode batches)
 // C[R, N] (+)= A[R, K] W[N, K]^T for R <= 16 RF rows: weight-stationary MFMA.
 // Each workgroup owns CF column fragments of 16 (SWIGLU: the gate and the up
@@ -789,6 +792,15 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     constexpr int PD = 4;
     __shared__ float red[4][RF * 16][CF * 16 + 1];
     __shared__ float ssred[NORM ? 4 : 1][RF * 16];
+    // CA: the activation rows come in whole-row pieces (two fp32 rows or four bf16 rows
+    // of a batch per wave instruction) into a wave-private LDS area, and the fragments
+    // are read from there: a fragment-shaped load (16 rows x 64 B per instruction)
+    // reads L2 at about a third of the rate of row-shaped ones. Rows padded by 16 B so
+    // the 16 rows of a fragment read fall in distinct banks.
+    constexpr bool CA = STTD_SKINNY_CA && RF <= 2;
+    constexpr int AROWS = RF * 16, AXS = PD * 32 + 4, AHS = PD * 32 + 8;
+    constexpr int ABYTES = CA ? (NORM ? AROWS * AXS * 4 : 2 * AROWS * AHS * 2) : 16;
+    __shared__ __attribute__((aligned(16))) unsigned char a_lds[4][ABYTES];
     clock_begin(g.clk);
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
     const int ct = blockIdx.x;
@@ -847,12 +859,32 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     f32x4 xa[PD][RF], xb[PD][RF];
     for (int s = s0; s < s1; s += PD) {
         // a batch of PD steps (clamped reads past s1 are loaded but not used)
+        constexpr int NAI = CA ? AROWS / 2 : 1;  // row-piece loads per lane (fp32: 2 rows, bf16: 2 planes x 4 rows each)
+        u32x4 areg[NAI];
+        if constexpr (CA) {
+            // row pieces, issued before the weight loads so their wait leaves those in flight
+#pragma unroll
+            for (int i = 0; i < NAI; ++i) {
+                if (NORM) {  // fp32 rows: lane l takes row 2 i + l / 32, floats 4 (l % 32) ..
+                    const int row = min(2 * i + lane / 32, g.M - 1), c = (lane % 32) * 4;
+                    areg[i] = *reinterpret_cast<const u32x4*>(g.X + (int64_t)row * g.ldx +
+                                                              min(s + c / 32, n_steps - 1) * 32 + c % 32);
+                } else {     // bf16 planes: i < AROWS / 4 high, then low; lane l takes row 4 i' + l / 16, elements 8 (l % 16) ..
+                    const int ii = i % (AROWS / 4), row = min(4 * ii + lane / 16, g.M - 1), c = (lane % 16) * 8;
+                    const uint16_t* base = i < AROWS / 4 ? g.A : (g.A_lo ? g.A_lo : g.A);
+                    areg[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)row * g.lda +
+                                                              min(s + c / 32, n_steps - 1) * 32 + c % 32);
+                }
+            }
+        }
 #pragma unroll
         for (int p = 0; p < PD; ++p) {
             const int k = min(s + p, n_steps - 1) * 32 + koff;
 #pragma unroll
             for (int f = 0; f < CF; ++f) wb[p][f] = *reinterpret_cast<const u32x4*>(wrow[f] + k);
-            if (NORM) {
+            if (CA) {
+                if (NORM) gb[p] = *reinterpret_cast<const u32x4*>(g.gain + k);
+            } else if (NORM) {
                 gb[p] = *reinterpret_cast<const u32x4*>(g.gain + k);
 #pragma unroll
                 for (int r = 0; r < RF; ++r) {
@@ -865,6 +897,39 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
                     ab[p][r] = *reinterpret_cast<const u32x4*>(arow[r] + k);
                     if (lo) alb[p][r] = *reinterpret_cast<const u32x4*>(alrow[r] + k);
                 }
+            }
+        }
+        if constexpr (CA) {
+            // the wave's own LDS area: write the row pieces, read the fragments back
+            // (a wave's LDS operations complete in order, so no barrier)
+            if (NORM) {
+                float* ax = reinterpret_cast<float*>(a_lds[wave]);
+#pragma unroll
+                for (int i = 0; i < NAI; ++i)
+                    *reinterpret_cast<u32x4*>(&ax[(2 * i + lane / 32) * AXS + (lane % 32) * 4]) = areg[i];
+#pragma unroll
+                for (int p = 0; p < PD; ++p)
+#pragma unroll
+                    for (int r = 0; r < RF; ++r) {
+                        const float* src = &ax[(r * 16 + lane % 16) * AXS + p * 32 + koff];
+                        xa[p][r] = *reinterpret_cast<const f32x4*>(src);
+                        xb[p][r] = *reinterpret_cast<const f32x4*>(src + 4);
+                    }
+            } else {
+                uint16_t* ah = reinterpret_cast<uint16_t*>(a_lds[wave]);
+#pragma unroll
+                for (int i = 0; i < NAI; ++i) {
+                    const int pl = i / (AROWS / 4), ii = i % (AROWS / 4);
+                    *reinterpret_cast<u32x4*>(&ah[(pl * AROWS + 4 * ii + lane / 16) * AHS + (lane % 16) * 8]) = areg[i];
+                }
+#pragma unroll
+                for (int p = 0; p < PD; ++p)
+#pragma unroll
+                    for (int r = 0; r < RF; ++r) {
+                        const int o = (r * 16 + lane % 16) * AHS + p * 32 + koff;
+                        ab[p][r] = *reinterpret_cast<const u32x4*>(&ah[o]);
+                        alb[p][r] = *reinterpret_cast<const u32x4*>(&ah[AROWS * AHS + o]);
+                    }
             }
         }
 #pragma unroll
