@@ -232,7 +232,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 // wave for QKV, O and down, so each weight byte is requested once (QKV 22.4 ->
 // 26.1 us, down 22.6 -> 26.8 us). For calibration, a probe reading the same
 // A-tile pattern (80 rows 4 KB apart, 128 B each per step, a ring with a barrier
-// per step) gets ~130 GB/s per workgroup from L2.
+// per step) gets ~130 GB/s per workgroup from L2. Staging the weight tile through
+// LDS too, loaded in row pieces (the fragment-shaped loads read L2 at a third of
+// that rate, and each weight tile's second row tile finds it in L2), measured
+// slower: gate_up 36.3 -> 38.8 us, the LDS traffic outweighing the faster loads.
 template <int EPI, int FM, int FN, int D, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
     constexpr int BM = FM * 16, BN = FN * 64;
