@@ -773,6 +773,9 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
 #ifndef STTD_SKINNY_CA
 #define STTD_SKINNY_CA 1
 #endif
+#ifndef STTD_SKINNY_PD
+#define STTD_SKINNY_PD 8
+#endif
 // ------------------------------------------------------------------ few rows (decode batches)
 // C[R, N] (+)= A[R, K] W[N, K]^T for R <= 16 RF rows: weight-stationary MFMA.
 // Each workgroup owns CF column fragments of 16 (SWIGLU: the gate and the up
@@ -791,11 +794,13 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
 // loads, and the outputs are scaled by each row's 1 / rms.
 template <int EPI, int RF, int CF, bool NORM>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
-    // K-steps of 32 per load batch (8, in flight twice the bytes, measured slower
-    // at 16 rows: gate_up 17.4 -> 18.0 us, down 10.8 -> 11.7 us; two alternating
-    // batches of 4, loading one while the other feeds the MFMAs, measured slower too:
-    // QKV 7.6 -> 9.0 us, down 10.8 -> 13.0 us, from the higher register count)
-    constexpr int PD = 4;
+    // K-steps of 32 per load batch. With fragment-shaped activation loads, 8 measured
+    // slower (gate_up 17.4 -> 18.0 us, down 10.8 -> 11.7 us), and two alternating
+    // batches of 4 too (QKV 7.6 -> 9.0 us, down 10.8 -> 13.0 us). With row-piece
+    // activation loads (CA): 8 for the single-fragment-row STORE / RESID forms (at 16 rows
+    // QKV 7.62 -> 7.44 us, O 3.66 -> 3.47, down 8.40 -> 8.18 against 4; 8.62k -> 8.69k
+    // tok/s), 4 for SWIGLU and wider row counts (2: slower everywhere)
+    constexpr int PD = (EPI == GEMM_SWIGLU || RF > 1) ? 4 : STTD_SKINNY_PD;
     __shared__ float red[4][RF * 16][CF * 16 + 1];
     __shared__ float ssred[NORM ? 4 : 1][RF * 16];
     // CA: the activation rows come in whole-row pieces (two fp32 rows or four bf16 rows
@@ -803,7 +808,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     // are read from there: a fragment-shaped load (16 rows x 64 B per instruction)
     // reads L2 at about a third of the rate of row-shaped ones. Rows padded by 16 B so
     // the 16 rows of a fragment read fall in distinct banks.
-    constexpr bool CA = STTD_SKINNY_CA && RF <= 2;
+    constexpr bool CA = STTD_SKINNY_CA && RF * PD <= 8;  // the LDS areas fit beside the reduction
     constexpr int AROWS = RF * 16, AXS = PD * 32 + 4, AHS = PD * 32 + 8;
     constexpr int ABYTES = CA ? (NORM ? AROWS * AXS * 4 : 2 * AROWS * AHS * 2) : 16;
     __shared__ __attribute__((aligned(16))) unsigned char a_lds[4][ABYTES];
@@ -865,21 +870,25 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     f32x4 xa[PD][RF], xb[PD][RF];
     for (int s = s0; s < s1; s += PD) {
         // a batch of PD steps (clamped reads past s1 are loaded but not used)
-        constexpr int NAI = CA ? AROWS / 2 : 1;  // row-piece loads per lane (fp32: 2 rows, bf16: 2 planes x 4 rows each)
+        // row-piece loads per lane: a batch of a row is PD * 32 elements, in 16-byte
+        // pieces of 4 fp32 (8 PD per row) or 8 bf16 (4 PD per row and plane)
+        constexpr int PPR = NORM ? 8 * PD : 4 * PD;               // pieces per row (and plane)
+        constexpr int NAP = AROWS * PPR / 64;                      // loads per lane and plane
+        constexpr int NAI = CA ? (NORM ? NAP : 2 * NAP) : 1;
         u32x4 areg[NAI];
         if constexpr (CA) {
             // row pieces, issued before the weight loads so their wait leaves those in flight
 #pragma unroll
             for (int i = 0; i < NAI; ++i) {
-                if (NORM) {  // fp32 rows: lane l takes row 2 i + l / 32, floats 4 (l % 32) ..
-                    const int row = min(2 * i + lane / 32, g.M - 1), c = (lane % 32) * 4;
-                    areg[i] = *reinterpret_cast<const u32x4*>(g.X + (int64_t)row * g.ldx +
-                                                              min(s + c / 32, n_steps - 1) * 32 + c % 32);
-                } else {     // bf16 planes: i < AROWS / 4 high, then low; lane l takes row 4 i' + l / 16, elements 8 (l % 16) ..
-                    const int ii = i % (AROWS / 4), row = min(4 * ii + lane / 16, g.M - 1), c = (lane % 16) * 8;
-                    const uint16_t* base = i < AROWS / 4 ? g.A : (g.A_lo ? g.A_lo : g.A);
-                    areg[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)row * g.lda +
-                                                              min(s + c / 32, n_steps - 1) * 32 + c % 32);
+                // piece e of the plane: row e / PPR, element c of the row's batch
+                const int e = (i % NAP) * 64 + lane;
+                const int row = min(e / PPR, g.M - 1), c = (e % PPR) * (NORM ? 4 : 8);
+                const int64_t kk = (int64_t)min(s + c / 32, n_steps - 1) * 32 + c % 32;
+                if (NORM) {
+                    areg[i] = *reinterpret_cast<const u32x4*>(g.X + (int64_t)row * g.ldx + kk);
+                } else {  // loads [0, NAP) the high plane, then the low one
+                    const uint16_t* base = i < NAP ? g.A : (g.A_lo ? g.A_lo : g.A);
+                    areg[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)row * g.lda + kk);
                 }
             }
         }
@@ -911,8 +920,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
             if (NORM) {
                 float* ax = reinterpret_cast<float*>(a_lds[wave]);
 #pragma unroll
-                for (int i = 0; i < NAI; ++i)
-                    *reinterpret_cast<u32x4*>(&ax[(2 * i + lane / 32) * AXS + (lane % 32) * 4]) = areg[i];
+                for (int i = 0; i < NAI; ++i) {
+                    const int e = i * 64 + lane;
+                    *reinterpret_cast<u32x4*>(&ax[(e / PPR) * AXS + (e % PPR) * 4]) = areg[i];
+                }
 #pragma unroll
                 for (int p = 0; p < PD; ++p)
 #pragma unroll
@@ -925,8 +936,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
                 uint16_t* ah = reinterpret_cast<uint16_t*>(a_lds[wave]);
 #pragma unroll
                 for (int i = 0; i < NAI; ++i) {
-                    const int pl = i / (AROWS / 4), ii = i % (AROWS / 4);
-                    *reinterpret_cast<u32x4*>(&ah[(pl * AROWS + 4 * ii + lane / 16) * AHS + (lane % 16) * 8]) = areg[i];
+                    const int pl = i / NAP, e = (i % NAP) * 64 + lane;
+                    *reinterpret_cast<u32x4*>(&ah[(pl * AROWS + e / PPR) * AHS + (e % PPR) * 8]) = areg[i];
                 }
 #pragma unroll
                 for (int p = 0; p < PD; ++p)
