@@ -776,6 +776,9 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
 #ifndef STTD_SKINNY_PD
 #define STTD_SKINNY_PD 8
 #endif
+#ifndef STTD_SKINNY_PD_SW
+#define STTD_SKINNY_PD_SW 4
+#endif
 // ------------------------------------------------------------------ few rows (decode batches)
 // C[R, N] (+)= A[R, K] W[N, K]^T for R <= 16 RF rows: weight-stationary MFMA.
 // Each workgroup owns CF column fragments of 16 (SWIGLU: the gate and the up
@@ -799,8 +802,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     // batches of 4 too (QKV 7.6 -> 9.0 us, down 10.8 -> 13.0 us). With row-piece
     // activation loads (CA): 8 for the single-fragment-row STORE / RESID forms (at 16 rows
     // QKV 7.62 -> 7.44 us, O 3.66 -> 3.47, down 8.40 -> 8.18 against 4; 8.62k -> 8.69k
-    // tok/s), 4 for SWIGLU and wider row counts (2: slower everywhere)
-    constexpr int PD = (EPI == GEMM_SWIGLU || RF > 1) ? 4 : STTD_SKINNY_PD;
+    // tok/s), 4 for SWIGLU (gate_up 16.0 us against 18.2 with 8 and 16.1 with 2) and
+    // wider row counts (2 measured slower everywhere)
+    constexpr int PD = RF > 1 ? 4 : (EPI == GEMM_SWIGLU ? STTD_SKINNY_PD_SW : STTD_SKINNY_PD);
     __shared__ float red[4][RF * 16][CF * 16 + 1];
     __shared__ float ssred[NORM ? 4 : 1][RF * 16];
     // CA: the activation rows come in whole-row pieces (two fp32 rows or four bf16 rows
