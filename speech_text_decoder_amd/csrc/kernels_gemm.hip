@@ -776,6 +776,12 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
 #ifndef STTD_SKINNY_PD
 #define STTD_SKINNY_PD 8
 #endif
+// SWIGLU column fragments per workgroup (gate + up, so CF / 2 * 16 act columns). 2, with
+// twice the workgroups to fill all 256 CUs, measured slower with row-piece loads as well
+// as with fragment-shaped ones (16-row gate_up 16.0 -> 17.1 us; 17.4 -> 20.1 before)
+#ifndef STTD_SKINNY_SW_CF
+#define STTD_SKINNY_SW_CF 4
+#endif
 #ifndef STTD_SKINNY_PD_SW
 #define STTD_SKINNY_PD_SW 4
 #endif
@@ -1074,8 +1080,9 @@ static void launch_skinny_rf(const GemmArgs& g, dim3 grid, hipStream_t s) {
 
 static void launch_gemm_skinny(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     if (epi == GEMM_SWIGLU) {
-        if (g.X) launch_skinny_rf<GEMM_SWIGLU, 4, true>(g, dim3((g.N + 31) / 32, 1), s);
-        else launch_skinny_rf<GEMM_SWIGLU, 4>(g, dim3((g.N + 31) / 32, 1), s);
+        constexpr int SCF = STTD_SKINNY_SW_CF, ACOLS = SCF / 2 * 16;
+        if (g.X) launch_skinny_rf<GEMM_SWIGLU, SCF, true>(g, dim3((g.N + ACOLS - 1) / ACOLS, 1), s);
+        else launch_skinny_rf<GEMM_SWIGLU, SCF>(g, dim3((g.N + ACOLS - 1) / ACOLS, 1), s);
         return;
     }
     const int tiles = (g.N + 15) / 16;
