@@ -208,13 +208,16 @@ KVLayer kv_layer(const sttd_kv_cache* kv, int layer) {
 // row that follow each row's own length (ceil(keys / span), up to 8, the spare
 // workgroups exiting at once) lost too: 17.9 us per block against 22.9, 25.5 and
 // 28.0 us at spans of 384, 512 and 256 rows.
+#ifndef STTD_ATTN_FILL
+#define STTD_ATTN_FILL 256
+#endif
 int choose_splits(int rows, int n_kv, int pos_bound, int part_cap) {
     int s = (pos_bound + 127) / 128;
     // long single rows: fewer, longer splits (8-wave workgroups) and one combine
     // (at 4096-4352 positions, capping a single row at 16 splits measured within
     // 1% of 32, and at 8, which the O projection then merges, 5% slower)
     if (s > 32) s = 32;
-    const int fill = (256 + rows * n_kv - 1) / (rows * n_kv);
+    const int fill = (STTD_ATTN_FILL + rows * n_kv - 1) / (rows * n_kv);
     if (rows > 1 && s > fill) s = fill;
     if (s > kMaxSplits) s = kMaxSplits;
     if (s > part_cap / rows) s = part_cap / rows;

@@ -8,6 +8,15 @@
 #include "common.h"
 #include "launch.h"
 
+// Cache rows per group per streaming step (0: by query heads per KV head) and
+// the depth of the register ring they stream through.
+#ifndef STTD_ATTN_RIF
+#define STTD_ATTN_RIF 0
+#endif
+#ifndef STTD_ATTN_DEPTH
+#define STTD_ATTN_DEPTH 2
+#endif
+
 namespace sttd {
 
 // ------------------------------------------------------------------ rows attention (decode)
@@ -207,20 +216,39 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
     const T* Kp = (const T*)a.kv.k + slab + sub * 8;
     const T* Vp = (const T*)a.kv.v + slab + sub * 8;
     const int cend = owner ? pos : c1;  // the new key (owner) is folded in from LDS below
-    // RIF rows per group in flight: row c + q * NG for q < RIF (clamped to row 0 past the end)
-    // (8 per group for G <= 2 with f16 rows kept packed measured slower for one
-    // decode row: 5.4 -> 6.3 us per launch, and in the one-launch projection +
-    // attention 8.8 -> 10.0 us; for splits over 256 rows, 16 rows of 150-1500
-    // positions: 8 and 12 took 18.0 -> 20.7 and 23.4 us)
-    constexpr int RIF = G <= 2 ? 4 : (G == 4 ? 2 : 1);
+    // The cache rows stream through a register ring of DEPTH steps of RIF rows per
+    // group (row cb + grp + q * NG of the step at cb); the step DEPTH ahead is fetched
+    // as soon as a step has been used. Every fetch is issued, clamped to the last row
+    // of the span past its end, so the count of loads in flight is the same on every
+    // path and each wait leaves the later steps in flight. (The former form, one step
+    // in flight fetched between a step's scores and its state update, with per-group
+    // trip counts, waited for all loads each step: 18.0 us for 16 rows of 150-1500
+    // positions.)
+    // (16 rows of 151-1535 positions, G = 2, two steps deep: 2 rows per step 14.8 us,
+    // 4 rows 15.7 us, 8 rows 21.1 us; three or four steps deep no faster)
+    // 4-wave workgroups (single rows, and the one-launch projection + attention, whose
+    // sums must match the two-launch form bit for bit: the rescale per step makes the
+    // rounding depend on the step) keep 4
+    constexpr int RIF = STTD_ATTN_RIF > 0 ? STTD_ATTN_RIF
+                                          : (G <= 2 ? (NW == 4 ? 4 : 2) : (G == 4 ? 2 : 1));
+    // (the single-row projection + attention launch: splits of a few dozen rows, within
+    // one step, where a second step only adds loads: 8.5 -> 9.1 us per launch)
+    constexpr int DEPTH = TAGGED ? 1 : STTD_ATTN_DEPTH;
     constexpr int STEP = RIF * NG;
-    int c = c0 + grp;
-    KvRaw<KT> kr[RIF], vr[RIF];
+    const int last = cend > 0 ? cend - 1 : 0;
+    KvRaw<KT> kr[DEPTH][RIF], vr[DEPTH][RIF];
+    auto fetch = [&](KvRaw<KT>(&kk)[RIF], KvRaw<KT>(&vv)[RIF], const int cb) {
 #pragma unroll
-    for (int q = 0; q < RIF; ++q) {
-        const int cq = c + q * NG < cend ? c + q * NG : 0;
-        kr[q].load(Kp + (int64_t)cq * D);
-        vr[q].load(Vp + (int64_t)cq * D);
+        for (int q = 0; q < RIF; ++q) {
+            const int cq = min(cb + grp + q * NG, last);
+            kk[q].load(Kp + (int64_t)cq * D);
+            vv[q].load(Vp + (int64_t)cq * D);
+        }
+    };
+#pragma unroll
+    for (int b = 0; b < DEPTH; ++b) {
+        fetch(kr[b], vr[b], c0 + b * STEP);
+        __builtin_amdgcn_sched_barrier(0);  // the steps in order, as the loop waits for them
     }
     __builtin_amdgcn_sched_barrier(0);
     // 2b. tagged hand-off: with the cache rows above in flight, poll this wave's
@@ -306,40 +334,71 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[g][i] = 0.f;
     }
-    // 4. cache rows [c0, cend): RIF per group per step, the next RIF in flight
-    for (; c < cend; c += STEP) {
+    // 4. cache rows [c0, cend), a step of RIF rows per group at a time: the scores,
+    //    one rescale of the running state to the step's maximum, then the weighted
+    //    values (rows past the end score -inf and weigh 0)
+    auto consume = [&](const KvRaw<KT>(&kk)[RIF], const KvRaw<KT>(&vv)[RIF], const int cb) {
         float sc[RIF][G];
 #pragma unroll
         for (int q = 0; q < RIF; ++q) {
             float kf[8];
-            kr[q].widen(kf);
+            kk[q].widen(kf);
+            const bool valid = cb + grp + q * NG < cend;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 float t = 0.f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) t = fmaf(qv[g][i], kf[i], t);
-                sc[q][g] = group_sum<LPK>(t);
+                t = group_sum<LPK>(t);
+                sc[q][g] = valid ? t : -INFINITY;
             }
         }
-        KvRaw<KT> vcur[RIF];
 #pragma unroll
-        for (int q = 0; q < RIF; ++q) vcur[q] = vr[q];
-        const int cn = c + STEP;
-        if (cn < cend) {
+        for (int g = 0; g < G; ++g) {
+            float M = m[g];
+#pragma unroll
+            for (int q = 0; q < RIF; ++q) M = fmaxf(M, sc[q][g]);
+            const float Ms = M == -INFINITY ? 0.f : M;
+            // v_exp_f32 itself: results below 2^-126 (weights that small against the
+            // running maximum's 1) flush to 0, and exp2(-inf) is 0 (exp2f's denormal
+            // range handling cost 12.7 -> 11.6 us on one 1535-position row). Moving the
+            // reference maximum only when passed by more than 2^8, skipping most
+            // rescales, took 11.6 -> 11.0 us there but nothing on 16 mixed rows: not kept
+            const float alpha = __builtin_amdgcn_exp2f(m[g] - Ms);
+            float lsum = l[g] * alpha;
 #pragma unroll
             for (int q = 0; q < RIF; ++q) {
-                const int cq = cn + q * NG < cend ? cn + q * NG : cn;
-                kr[q].load(Kp + (int64_t)cq * D);
-                vr[q].load(Vp + (int64_t)cq * D);
+                sc[q][g] = __builtin_amdgcn_exp2f(sc[q][g] - Ms);
+                lsum += sc[q][g];
             }
+            l[g] = lsum;
+            m[g] = M;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[g][i] *= alpha;
         }
 #pragma unroll
-        for (int q = 0; q < RIF; ++q)
-            if (c + q * NG < cend) {
-                float vf[8];
-                vcur[q].widen(vf);
-                step_state<G>(m, l, o, sc[q], vf);
-            }
+        for (int q = 0; q < RIF; ++q) {
+            float vf[8];
+            vv[q].widen(vf);
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[g][i] = fmaf(sc[q][g], vf[i], o[g][i]);
+        }
+    };
+    // uniform trip count: every wave runs the same steps
+    for (int cb = c0; cb < cend; cb += DEPTH * STEP) {
+#pragma unroll
+        for (int b = 0; b < DEPTH; ++b) {
+            // a step wholly past the end is not computed (a uniform branch holding no
+            // loads, so the counts of loads in flight stay exact)
+            if (cb + b * STEP < cend) consume(kr[b], vr[b], cb + b * STEP);
+            // keep each refetch right after its step's use (the scheduler would
+            // otherwise sink them all to the end of the loop body)
+            __builtin_amdgcn_sched_barrier(0);
+            fetch(kr[b], vr[b], cb + (b + DEPTH) * STEP);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     // 5. the new key (held in LDS by the owner), folded in by group 0
     if (owner && grp == 0) {
