@@ -36,13 +36,13 @@ _GEMV_SRC = {"files": ["kernels_gemv.hip", "gemv_ops.h", "common.h"],
              "sha256": "61559bc4b654f52a712d932bd64df4c51df3266b13d70bdf7e85e84edd853489",
              "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
 _QA_SRC = {"files": ["kernels_attn.hip", "attn_rows.h", "gemv_ops.h", "common.h"],
-           "sha256": "eb43cd1591210cc9f152c4b708dea536017311b151dda4ea12a8c161b23d632b",
+           "sha256": "a33b91ebc78873fad0c77b03662c70fe666fde5dcd60ebd987dcb044b9a1b250",
            "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
 TRAFFIC = {
     "o_gemv": dict(_GEMV_SRC, rows=1, bytes=8676511),
     "gateup_gemv": dict(_GEMV_SRC, rows=1, bytes=50580089),
     "down_gemv": dict(_GEMV_SRC, rows=1, bytes=25508367),
-    "qkv_attn": dict(_QA_SRC, rows=1, bytes=18083790),
+    "qkv_attn": dict(_QA_SRC, rows=1, bytes=18052892),
 }
 
 
