@@ -776,14 +776,16 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
 #ifndef STTD_SKINNY_PD
 #define STTD_SKINNY_PD 8
 #endif
-// SWIGLU column fragments per workgroup (gate + up, so CF / 2 * 16 act columns). 2, with
-// twice the workgroups to fill all 256 CUs, measured slower with row-piece loads as well
-// as with fragment-shaped ones (16-row gate_up 16.0 -> 17.1 us; 17.4 -> 20.1 before)
+// SWIGLU column fragments per workgroup (gate + up rows, so CF * 8 act columns). 3 makes
+// the 1.7B FFN (6144 act columns) exactly 256 workgroups, one per CU: 16-row gate_up
+// 16.1 -> 13.6 us against 4 (192 workgroups, a quarter of the CUs idle), 8.93k -> 9.34k
+// tok/s batched. 2 (384 workgroups, each re-reading the activation rows) measured slower
+// than 4 (16.0 -> 17.1 us)
 #ifndef STTD_SKINNY_SW_CF
-#define STTD_SKINNY_SW_CF 4
+#define STTD_SKINNY_SW_CF 3
 #endif
 #ifndef STTD_SKINNY_PD_SW
-#define STTD_SKINNY_PD_SW 4
+#define STTD_SKINNY_PD_SW 2
 #endif
 // ------------------------------------------------------------------ few rows (decode batches)
 // C[R, N] (+)= A[R, K] W[N, K]^T for R <= 16 RF rows: weight-stationary MFMA.
@@ -808,8 +810,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     // batches of 4 too (QKV 7.6 -> 9.0 us, down 10.8 -> 13.0 us). With row-piece
     // activation loads (CA): 8 for the single-fragment-row STORE / RESID forms (at 16 rows
     // QKV 7.62 -> 7.44 us, O 3.66 -> 3.47, down 8.40 -> 8.18 against 4; 8.62k -> 8.69k
-    // tok/s), 4 for SWIGLU (gate_up 16.0 us against 18.2 with 8 and 16.1 with 2) and
-    // wider row counts (2 measured slower everywhere)
+    // tok/s), 2 for SWIGLU at 3 fragments (gate_up 13.6 us against 15.0 with 1, 15.5 with 3,
+    // 13.9 with 4 and 15.7 with 8; at 4 fragments 4 was best: 16.0 against 18.2 with 8 and
+    // 16.1 with 2) and 4 for wider row counts (2 measured slower everywhere)
     constexpr int PD = RF > 1 ? 4 : (EPI == GEMM_SWIGLU ? STTD_SKINNY_PD_SW : STTD_SKINNY_PD);
     __shared__ float red[4][RF * 16][CF * 16 + 1];
     __shared__ float ssred[NORM ? 4 : 1][RF * 16];
@@ -831,11 +834,14 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
     for (int f = 0; f < CF; ++f) {
         if (EPI == GEMM_SWIGLU) {
-            // fragments [0, CF/2): gate rows of act columns 16 (ct CF/2 + f) ..; [CF/2, CF): their up rows
-            const int c = (ct * (CF / 2) + f % (CF / 2)) * 16 + lane % 16;  // act column
+            // the tile's CF * 16 weight rows: the gate rows of its CF * 8 act columns,
+            // then their up rows (an odd CF splits the middle fragment between the two)
+            constexpr int GC = CF * 8;
+            const int j = f * 16 + lane % 16;
+            const int c = ct * GC + (j < GC ? j : j - GC);  // act column
             wok[f] = c < g.N;
             const int cc = wok[f] ? c : 0;
-            wrow[f] = g.w[0] + (int64_t)(f < CF / 2 ? cc : g.N + cc) * g.K;
+            wrow[f] = g.w[0] + (int64_t)(j < GC ? cc : g.N + cc) * g.K;
         } else {
             const int n0 = (ct * CF + f) * 16 + lane % 16;
             wok[f] = n0 < g.N;
@@ -1024,7 +1030,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
             v *= rs;
         }
         if (EPI == GEMM_SWIGLU) {
-            constexpr int GC = CF / 2 * 16;  // gate columns of the tile; the up ones follow
+            constexpr int GC = CF * 8;  // gate columns of the tile; the up ones follow
             if (col >= GC) continue;  // the up half is read with its gate
             const int c = ct * GC + col;
             if (c >= g.N) continue;
@@ -1080,7 +1086,7 @@ static void launch_skinny_rf(const GemmArgs& g, dim3 grid, hipStream_t s) {
 
 static void launch_gemm_skinny(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
     if (epi == GEMM_SWIGLU) {
-        constexpr int SCF = STTD_SKINNY_SW_CF, ACOLS = SCF / 2 * 16;
+        constexpr int SCF = STTD_SKINNY_SW_CF, ACOLS = SCF * 8;
         if (g.X) launch_skinny_rf<GEMM_SWIGLU, SCF, true>(g, dim3((g.N + ACOLS - 1) / ACOLS, 1), s);
         else launch_skinny_rf<GEMM_SWIGLU, SCF>(g, dim3((g.N + ACOLS - 1) / ACOLS, 1), s);
         return;
