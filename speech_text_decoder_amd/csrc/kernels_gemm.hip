@@ -787,6 +787,18 @@ static void launch_gemm_big(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
 #ifndef STTD_SKINNY_PD_SW
 #define STTD_SKINNY_PD_SW 2
 #endif
+// Two values split as split_bf16 does (hi = bf16(v), lo = bf16(v - hi), nearest even),
+// each pair packed (element 0 in the low half): one v_cvt_pk_bf16_f32 per pair and
+// part instead of one per value, and no packing shifts (the skinny NORM loop's
+// per-step VALU count 81 -> about 48)
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+    const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xFFFF0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a - ha, b - hb}, bf16x2_t));
+}
+
 // ------------------------------------------------------------------ few rows (decode batches)
 // C[R, N] (+)= A[R, K] W[N, K]^T for R <= 16 RF rows: weight-stationary MFMA.
 // Each workgroup owns CF column fragments of 16 (SWIGLU: the gate and the up
@@ -979,11 +991,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
                     for (int i = 0; i < 4; ++i) {
                         ss[r] = fmaf(xv[2 * i], xv[2 * i], ss[r]);
                         ss[r] = fmaf(xv[2 * i + 1], xv[2 * i + 1], ss[r]);
-                        uint16_t h0, l0, h1, l1;
-                        split_bf16(xv[2 * i] * __uint_as_float(gw[i] << 16), h0, l0);
-                        split_bf16(xv[2 * i + 1] * __uint_as_float(gw[i] & 0xFFFF0000u), h1, l1);
-                        hw[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                        lw[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+                        split_bf16x2(xv[2 * i] * __uint_as_float(gw[i] << 16),
+                                     xv[2 * i + 1] * __uint_as_float(gw[i] & 0xFFFF0000u), hw[i], lw[i]);
                     }
                     ab[p][r] = u32x4{hw[0], hw[1], hw[2], hw[3]};
                     alb[p][r] = u32x4{lw[0], lw[1], lw[2], lw[3]};
@@ -1062,7 +1071,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 // split on the way in) with only weight loads in the K loop, two batches in
 // flight: gate_up 17.4 -> 21.4 us, QKV (32 columns per workgroup) 8.1 -> 15.0 us.
 // So did 8 waves per workgroup splitting K eight ways (two waves per SIMD, twice
-// the loads in flight per CU): 16 rows, 7.99k -> 7.93k tok/s, down 10.8 -> 11.7 us.
+// the loads in flight per CU): 16 rows, 7.99k -> 7.93k tok/s, down 10.8 -> 11.7 us;
+// and again with the row-piece activation loads: QKV 7.43 -> 7.59 us, O 3.44 -> 4.64,
+// down 8.29 -> 9.27, gate_up 13.6 -> 13.9.
 // So did two batch buffers again with every load unconditional and the waits
 // checked in the ISA to cover one step each (batches of 4, 3 and 2 steps): gate_up
 // 16.8 -> 19.6, 20.1 and 18.0 us, 8.05k -> 7.38k, 7.25k and 7.88k tok/s.
