@@ -33,15 +33,15 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
 # 256 MiB copy (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0); valid only for the kernel
 # sources they were taken on (sha256 of the listed files).
 _GEMV_SRC = {"files": ["kernels_gemv.hip", "gemv_ops.h", "common.h"],
-             "sha256": "61559bc4b654f52a712d932bd64df4c51df3266b13d70bdf7e85e84edd853489",
+             "sha256": "4a9ef155e1b0b895a8b75c409161d378c9d1dcfadbcfa8868d7e479d1951cd19",
              "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
 _QA_SRC = {"files": ["kernels_attn.hip", "attn_rows.h", "gemv_ops.h", "common.h"],
            "sha256": "a33b91ebc78873fad0c77b03662c70fe666fde5dcd60ebd987dcb044b9a1b250",
            "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
 TRAFFIC = {
-    "o_gemv": dict(_GEMV_SRC, rows=1, bytes=8676511),
-    "gateup_gemv": dict(_GEMV_SRC, rows=1, bytes=50580089),
-    "down_gemv": dict(_GEMV_SRC, rows=1, bytes=25508367),
+    "o_gemv": dict(_GEMV_SRC, rows=1, bytes=8676512),
+    "gateup_gemv": dict(_GEMV_SRC, rows=1, bytes=50580211),
+    "down_gemv": dict(_GEMV_SRC, rows=1, bytes=25508347),
     "qkv_attn": dict(_QA_SRC, rows=1, bytes=18052892),
 }
 

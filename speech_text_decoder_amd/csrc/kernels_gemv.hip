@@ -361,7 +361,8 @@ static hipError_t launch_head_wt(const HeadArgs& a, hipStream_t s) {
 // pass streams the embedding once for up to 16 rows: each workgroup walks
 // vocabulary tiles of 32 rows; each wave holds the A fragments (rows x its
 // quarter of K, high and low) in registers for the whole walk and feeds the
-// tile's embedding rows straight from global memory as B fragments. The
+// tile's embedding rows straight from global memory as B fragments, the next
+// tile's already in flight while a tile is computed and reduced. The
 // waves' partial logits meet in LDS; each thread keeps the best key of its
 // activation row over its two columns of every tile, and the 16 threads of a
 // row merge their keys at the end into the workgroup's partial.
@@ -386,37 +387,58 @@ __global__ __launch_bounds__(256) void head_mfma_kernel(HeadArgs a, const uint16
             ah[i] = *reinterpret_cast<const u32x4*>(zh + (int64_t)row * a.hidden + k);
             al[i] = *reinterpret_cast<const u32x4*>(zl + (int64_t)row * a.hidden + k);
         }
+        // steps past this wave's share multiply zeros: the step loop below has no
+        // branch (one would let the compiler sink each load to its use, unbatched)
+#pragma unroll
+        for (int i = 0; i < KSW; ++i)
+            if (s0 + i >= s1) ah[i] = al[i] = u32x4{0u, 0u, 0u, 0u};
     }
     const uint16_t* E = (const uint16_t*)a.embed;
     const int n_tiles = (a.vocab + 31) / 32;
     const int my_row = tid / 16, my_col = (tid % 16) * 2;
     unsigned long long best = 0ull;
-    for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-        const uint16_t* er[2];
+    // batch b (PD K-steps) of a tile's 32 embedding rows (clamped to the last tile and
+    // the last vocabulary row), addressed from the base each time
+    constexpr int NB = KSW / PD;
+    u32x4 wb[NB][PD][2];
+    auto fetch = [&](int tile, int b) {
+        const int t = min(tile, n_tiles - 1);
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
-            er[f] = E + (int64_t)min(tile * 32 + f * 16 + lane % 16, a.vocab - 1) * a.hidden + koff;
-        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int i0 = 0; i0 < KSW; i0 += PD) {
-            u32x4 wb[PD][2];
+        for (int f = 0; f < 2; ++f) {
+            const int64_t row = min(t * 32 + f * 16 + lane % 16, a.vocab - 1);
 #pragma unroll
             for (int p = 0; p < PD; ++p)
+                wb[b][p][f] = *reinterpret_cast<const u32x4*>(E + row * a.hidden + koff +
+                                                              min(s0 + b * PD + p, n_steps - 1) * 32);
+        }
+    };
+    // every batch of the next tile is fetched as soon as this tile's MFMAs have used
+    // its registers, so a whole tile is in flight while one is computed and reduced;
+    // the fences keep each batch issued whole (left alone, the compiler issues one
+    // load at a time, each waited on at once)
 #pragma unroll
-                for (int f = 0; f < 2; ++f)
-                    wb[p][f] = *reinterpret_cast<const u32x4*>(er[f] + min(s0 + i0 + p, n_steps - 1) * 32);
+    for (int b = 0; b < NB; ++b) {
+        fetch(blockIdx.x, b);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
 #pragma unroll
             for (int p = 0; p < PD; ++p) {
-                if (s0 + i0 + p >= s1) break;
 #pragma unroll
                 for (int f = 0; f < 2; ++f) {
-                    const bf16x8 bw = __builtin_bit_cast(bf16x8, wb[p][f]);
-                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah[i0 + p]), bw,
+                    const bf16x8 bw = __builtin_bit_cast(bf16x8, wb[b][p][f]);
+                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah[b * PD + p]), bw,
                                                                      acc[f], 0, 0, 0);
-                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al[i0 + p]), bw,
+                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al[b * PD + p]), bw,
                                                                      acc[f], 0, 0, 0);
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            fetch(tile + gridDim.x, b);
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int f = 0; f < 2; ++f)
@@ -445,6 +467,13 @@ __global__ __launch_bounds__(256) void head_mfma_kernel(HeadArgs a, const uint16
     clock_end(a.clk);
 }
 
+// Workgroups of the MFMA head: one per CU, each walking ~19 vocabulary tiles with the
+// next tile's loads in flight (16 rows: 112.9 us at 256 workgroups, 116.5 at 512, 131.4
+// at 1024; 133.4 at 1024 before the cross-tile prefetch, when each K-step's loads were
+// waited on at once and only the grid's width hid the latency)
+#ifndef STTD_HEAD_MFMA_WGS
+#define STTD_HEAD_MFMA_WGS 256
+#endif
 // MFMA head for batches: norm to bf16 planes, then 16-row chunks, then the finalize pass.
 static hipError_t launch_head_mfma(const HeadArgs& a, hipStream_t s) {
     uint16_t* zh = a.zbuf;
@@ -453,7 +482,8 @@ static hipError_t launch_head_mfma(const HeadArgs& a, hipStream_t s) {
                                             a.xrow, a.n_xrows, a.err);
     if (e != hipSuccess) return e;
     const int n_tiles = (a.vocab + 31) / 32;
-    const int grid = n_tiles < a.max_partials ? n_tiles : a.max_partials;
+    const int cap = a.max_partials < STTD_HEAD_MFMA_WGS ? a.max_partials : STTD_HEAD_MFMA_WGS;
+    const int grid = n_tiles < cap ? n_tiles : cap;
     const int ksw = (a.hidden / 32 + 3) / 4;
     for (int b0 = 0; b0 < a.rows; b0 += 16) {
         const int nb = a.rows - b0 < 16 ? a.rows - b0 : 16;
