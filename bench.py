@@ -36,7 +36,7 @@ _GEMV_SRC = {"files": ["kernels_gemv.hip", "gemv_ops.h", "common.h"],
              "sha256": "4a9ef155e1b0b895a8b75c409161d378c9d1dcfadbcfa8868d7e479d1951cd19",
              "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
 _QA_SRC = {"files": ["kernels_attn.hip", "attn_rows.h", "gemv_ops.h", "common.h"],
-           "sha256": "a33b91ebc78873fad0c77b03662c70fe666fde5dcd60ebd987dcb044b9a1b250",
+           "sha256": "af4ac7dfb9015eda7b1af29009f927c85a6dc38524a1f08e6fbc0b01d81d1f1b",
            "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
 TRAFFIC = {
     "o_gemv": dict(_GEMV_SRC, rows=1, bytes=8676512),

@@ -60,6 +60,14 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
     clock_end(clk, 1);
 }
 
+// Waves of a workgroup whose split spans more than 128 cache rows. 16 (1024 threads, 64
+// lane groups per split) measured slower on 16 rows of 151-1535 positions: 14.3 -> 16.4
+// us per launch, one 1535-position row alone 11.5 -> 13.4 us (the slot merge and the
+// barriers grow with the waves); valid only for groups of up to 2 query heads, whose
+// registers fit 4 waves per SIMD
+#ifndef STTD_ATTN_WIDE_NW
+#define STTD_ATTN_WIDE_NW 8
+#endif
 template <class KT, class GT, int D, bool FUSE>
 static hipError_t rows_dispatch(const RowsArgs& a, int R, bool wide, hipStream_t s) {
     const int G = a.n_heads / a.kv.n_kv;
@@ -73,8 +81,9 @@ static hipError_t rows_dispatch(const RowsArgs& a, int R, bool wide, hipStream_t
             if (pub) launch_kernel(attn_rows_kernel<KT, GT, D, G_, 4, FUSE, true>, grid, 4 * 64, 0, s, a);     \
             else launch_kernel(attn_rows_kernel<KT, GT, D, G_, 4, FUSE, false>, grid, 4 * 64, 0, s, a);        \
         } else {                                                                                    \
-            if (pub) launch_kernel(attn_rows_kernel<KT, GT, D, G_, 8, FUSE, true>, grid, 8 * 64, 0, s, a);     \
-            else launch_kernel(attn_rows_kernel<KT, GT, D, G_, 8, FUSE, false>, grid, 8 * 64, 0, s, a);        \
+            constexpr int NWW = STTD_ATTN_WIDE_NW;                                                      \
+            if (pub) launch_kernel(attn_rows_kernel<KT, GT, D, G_, NWW, FUSE, true>, grid, NWW * 64, 0, s, a); \
+            else launch_kernel(attn_rows_kernel<KT, GT, D, G_, NWW, FUSE, false>, grid, NWW * 64, 0, s, a);    \
         }                                                                                           \
     } while (0)
     switch (G) {
