@@ -1077,6 +1077,13 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 // So did two batch buffers again with every load unconditional and the waits
 // checked in the ISA to cover one step each (batches of 4, 3 and 2 steps): gate_up
 // 16.8 -> 19.6, 20.1 and 18.0 us, 8.05k -> 7.38k, 7.25k and 7.88k tok/s.
+// Column fragments per RESID workgroup. 2, with K split twice as often so the grid stays
+// at 256 (half the activation bytes per workgroup, twice the atomic adds), measured
+// slower at 16 rows: O 3.44 -> 4.82 us, down 8.28 -> 9.12 (with batches of 4 K-steps
+// O 3.67, down 8.10, QKV 6.94 -> 7.43: 9.61k -> 9.58k tok/s)
+#ifndef STTD_SKINNY_RESID_CF
+#define STTD_SKINNY_RESID_CF 1
+#endif
 #ifndef STTD_SKINNY_RESID_WGS
 #define STTD_SKINNY_RESID_WGS 256
 #endif
@@ -1102,12 +1109,14 @@ static void launch_gemm_skinny(const GemmArgs& g, GemmEpi epi, hipStream_t s) {
         else launch_skinny_rf<GEMM_SWIGLU, SCF>(g, dim3((g.N + ACOLS - 1) / ACOLS, 1), s);
         return;
     }
+    constexpr int RCF = STTD_SKINNY_RESID_CF;
     const int tiles = (g.N + 15) / 16;
+    const int rtiles = (g.N + 16 * RCF - 1) / (16 * RCF);
     // RESID may split K over workgroups (atomic adds) until about 256 workgroups run
     int ks = 1;
     if (epi == GEMM_RESID)
-        while (tiles * ks * 2 <= STTD_SKINNY_RESID_WGS && g.K / 32 >= ks * 2 * 4 * 4) ks *= 2;
-    if (epi == GEMM_RESID) launch_skinny_rf<GEMM_RESID, 1>(g, dim3(tiles, ks), s);
+        while (rtiles * ks * 2 <= STTD_SKINNY_RESID_WGS && g.K / 32 >= ks * 2 * 4 * 4) ks *= 2;
+    if (epi == GEMM_RESID) launch_skinny_rf<GEMM_RESID, RCF>(g, dim3(rtiles, ks), s);
     else if (g.X) launch_skinny_rf<GEMM_STORE, 1, true>(g, dim3(tiles, 1), s);
     else launch_skinny_rf<GEMM_STORE, 1>(g, dim3(tiles, 1), s);
 }
