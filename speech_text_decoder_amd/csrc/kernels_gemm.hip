@@ -1064,7 +1064,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 
 // Grid bound of few-row RESID launches that split K (atomic adds). At 16 rows,
 // 512 and 1024 measured slower (down 12.3 -> 12.8 and 15.8 us): every split adds
-// rows x N atomics. Splitting the K of STORE and SWIGLU launches too, with the
+// rows x N atomics. Again with the row-piece activation loads: 512 took O 3.44 -> 5.18
+// us and down 8.32 -> 9.51 (with batches of 4 K-steps 4.20 and 8.62). Splitting the K of STORE and SWIGLU launches too, with the
 // column tile's last workgroup merging the published partials, measured slower at
 // 384-1024 workgroups (gate_up 18.0 -> 23.8-25.7 us, QKV 8.2 -> 10.4-11.2 us). So
 // did staging the 16 activation rows once per workgroup in LDS (128 KB, normed and
