@@ -207,7 +207,11 @@ KVLayer kv_layer(const sttd_kv_cache* kv, int layer) {
 // costs a write-through, an atomic and a reload, not the streaming). Splits per
 // row that follow each row's own length (ceil(keys / span), up to 8, the spare
 // workgroups exiting at once) lost too: 17.9 us per block against 22.9, 25.5 and
-// 28.0 us at spans of 384, 512 and 256 rows.
+// 28.0 us at spans of 384, 512 and 256 rows. Re-measured with the register-ring
+// rows loop (one layer's launch, 16 rows of 151-1535 positions): ceil(keys / 600) up
+// to 3 splits 18.1 us and ceil(keys / 400) up to 4 16.7 us, against 14.3 us for two
+// equal splits; a lone 1535-position row 14.9 / 13.1 against 11.5 us, whatever the
+// slab stride of the cache (2048 to 2176 rows).
 #ifndef STTD_ATTN_FILL
 #define STTD_ATTN_FILL 256
 #endif
