@@ -212,6 +212,11 @@ KVLayer kv_layer(const sttd_kv_cache* kv, int layer) {
 // to 3 splits 18.1 us and ceil(keys / 400) up to 4 16.7 us, against 14.3 us for two
 // equal splits; a lone 1535-position row 14.9 / 13.1 against 11.5 us, whatever the
 // slab stride of the cache (2048 to 2176 rows).
+// Packed sequences' flash attention in one launch (8 prompts of 153 rows, 28 blocks:
+// 15.2 -> 11.3 ms, 224 launches of 18 us -> 28 of 19.6 us); 0 launches per sequence
+#ifndef STTD_PACKED_FLASH_ONE_LAUNCH
+#define STTD_PACKED_FLASH_ONE_LAUNCH 1
+#endif
 #ifndef STTD_ATTN_FILL
 #define STTD_ATTN_FILL 256
 #endif
@@ -309,7 +314,14 @@ sttd_status run_block(const sttd_block_params* p, const sttd_block_weights* w, s
     }
     int splits = 1;
     bool defer = false;
-    if (segs) {
+    if (segs && flash && STTD_PACKED_FLASH_ONE_LAUNCH) {
+        // packed sequences, each attending its own slab causally from its pos0: every
+        // sequence's query tiles in one launch (one launch per sequence gave each of
+        // them 2 x n_heads workgroups at 153 rows, a few dozen CUs of 256)
+        ProfScope ps(STTD_KERN_ATTN_PREFILL, s);
+        TRY(launch_attn_prefill_packed((const uint16_t*)ws->qbuf, qd, *segs, nq, kl, mfma ? ao : nullptr,
+                                       mfma ? ao_lo : nullptr, qd, s));
+    } else if (segs) {
         // packed sequences: each attends its own slab, causally from its pos0
         for (int i = 0; i < segs->n; ++i) {
             const int r0 = segs->start[i], Ti = segs->len[i], p0 = segs->pos0[i];

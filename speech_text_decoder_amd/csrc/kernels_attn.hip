@@ -283,11 +283,14 @@ hipError_t launch_qkv_attn(const QkvTagArgs& p, RowMap rm, KVLayer kv, int n_spl
 // too: 126 -> 130-135 us.
 constexpr float kLazy = 8.f;  // lazy-rescale threshold of the flash kernel (base-2 exponent)
 
-template <int D>
+// SEG: packed sequences in one launch, sequence blockIdx.z of `sg` (rows, length,
+// first position and slab from the table; its tiles are the first of gridDim.x,
+// the workgroups past them leave at once).
+template <int D, bool SEG>
 __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __restrict__ q16, int64_t ldq, int T,
                                                            int pos0, int seq, int n_heads, KVLayer kv,
                                                            uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo,
-                                                           int64_t ldo, int paired, uint64_t* clk) {
+                                                           int64_t ldo, int paired, uint64_t* clk, Segments sg) {
     constexpr int NT = 512;                // 8 waves: 4 row groups x 2 key groups
     constexpr int RF = 2;                  // 16-row fragments per wave
     constexpr int KB = 64, TQ = 4 * 16 * RF;
@@ -304,6 +307,15 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
 
 
     clock_begin(clk);
+    if constexpr (SEG) {
+        const int si = blockIdx.z, r0 = sg.start[si];
+        q16 += (int64_t)r0 * ldq;
+        out += (int64_t)r0 * ldo;
+        if (out_lo) out_lo += (int64_t)r0 * ldo;
+        T = sg.len[si];
+        pos0 = sg.pos0[si];
+        seq = sg.seq[si];
+    }
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
     const int g4 = lane / 16, r16 = lane % 16;
     const int kg = wave / 4, wr = wave % 4;  // key group, row group
@@ -324,6 +336,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
         // paired: tiles x and n - 1 - x; otherwise one tile each, the heavy (late) ones first
         const int tile = !paired ? n_tiles - 1 - px : (pass == 0 ? px : n_tiles - 1 - px);
         if (pass == 1 && (!paired || tile <= px)) break;  // an odd count leaves the middle tile single
+        if (tile < 0) break;                              // (SEG) past this sequence's tiles
         __syncthreads();                                  // the LDS buffers are free again
         const int t0 = tile * TQ + wr * 16 * RF;          // this wave's first query row
 
@@ -543,10 +556,32 @@ hipError_t launch_attn_prefill(const uint16_t* q16, int64_t ldq, int T, int pos0
     // pairing evens out causal work once there are enough tiles to fill the chip
     const int paired = n_tiles * n_heads >= 512;
     dim3 grid(paired ? (n_tiles + 1) / 2 : n_tiles, n_heads);
+    const Segments none{};
     if (kv.d == 128)
-        launch_kernel(attn_prefill_kernel<128>, grid, 512, 0, s, q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, paired, clock_slot());
+        launch_kernel(attn_prefill_kernel<128, false>, grid, 512, 0, s, q16, ldq, T, pos0, seq, n_heads, kv, out_bf16,
+                      out_bf16_lo, ldo, paired, clock_slot(), none);
     else if (kv.d == 64)
-        launch_kernel(attn_prefill_kernel<64>, grid, 512, 0, s, q16, ldq, T, pos0, seq, n_heads, kv, out_bf16, out_bf16_lo, ldo, paired, clock_slot());
+        launch_kernel(attn_prefill_kernel<64, false>, grid, 512, 0, s, q16, ldq, T, pos0, seq, n_heads, kv, out_bf16,
+                      out_bf16_lo, ldo, paired, clock_slot(), none);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill_packed(const uint16_t* q16, int64_t ldq, const Segments& sg, int n_heads, KVLayer kv,
+                                      uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo, hipStream_t s) {
+    if (sg.n <= 0) return hipSuccess;
+    if (sg.n > kMaxSegments) return hipErrorInvalidValue;
+    int max_len = 0;
+    for (int i = 0; i < sg.n; ++i) max_len = sg.len[i] > max_len ? sg.len[i] : max_len;
+    if (max_len <= 0) return hipSuccess;
+    const dim3 grid((max_len + 127) / 128, n_heads, sg.n);
+    if (kv.d == 128)
+        launch_kernel(attn_prefill_kernel<128, true>, grid, 512, 0, s, q16, ldq, 0, 0, 0, n_heads, kv, out_bf16,
+                      out_bf16_lo, ldo, 0, clock_slot(), sg);
+    else if (kv.d == 64)
+        launch_kernel(attn_prefill_kernel<64, true>, grid, 512, 0, s, q16, ldq, 0, 0, 0, n_heads, kv, out_bf16,
+                      out_bf16_lo, ldo, 0, clock_slot(), sg);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

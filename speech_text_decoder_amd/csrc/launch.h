@@ -252,6 +252,11 @@ hipError_t launch_qkv_attn(const QkvTagArgs& p, RowMap rm, KVLayer kv, int n_spl
 // Causal flash attention (MFMA, f16 cache) of T rows of one slab at positions pos0..
 hipError_t launch_attn_prefill(const uint16_t* q16, int64_t ldq, int T, int pos0, int seq, int n_heads, KVLayer kv,
                                uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo, hipStream_t s);
+// The same for packed sequences, all in one launch: sequence i's rows start at row
+// sg.start[i] of q16 and of the output, sg.len[i] of them, at positions sg.pos0[i]..
+// of slab sg.seq[i].
+hipError_t launch_attn_prefill_packed(const uint16_t* q16, int64_t ldq, const Segments& sg, int n_heads, KVLayer kv,
+                                      uint16_t* out_bf16, uint16_t* out_bf16_lo, int64_t ldo, hipStream_t s);
 
 constexpr uint32_t kDevErrSync = 8u;  // a tagged hand-off poll timed out (STTD_DEVERR_SYNC)
 
