@@ -36,13 +36,13 @@ _GEMV_SRC = {"files": ["kernels_gemv.hip", "gemv_ops.h", "common.h"],
              "sha256": "4a9ef155e1b0b895a8b75c409161d378c9d1dcfadbcfa8868d7e479d1951cd19",
              "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
 _QA_SRC = {"files": ["kernels_attn.hip", "attn_rows.h", "gemv_ops.h", "common.h"],
-           "sha256": "af4ac7dfb9015eda7b1af29009f927c85a6dc38524a1f08e6fbc0b01d81d1f1b",
+           "sha256": "fa99be7e49fec2cbd00515819deffd1d4119674c4caf46383471c3d5f37c1ec6",
            "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
 TRAFFIC = {
     "o_gemv": dict(_GEMV_SRC, rows=1, bytes=8676512),
     "gateup_gemv": dict(_GEMV_SRC, rows=1, bytes=50580211),
     "down_gemv": dict(_GEMV_SRC, rows=1, bytes=25508347),
-    "qkv_attn": dict(_QA_SRC, rows=1, bytes=18052892),
+    "qkv_attn": dict(_QA_SRC, rows=1, bytes=18062996),
 }
 
 
