@@ -65,6 +65,12 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
 // us per launch, one 1535-position row alone 11.5 -> 13.4 us (the slot merge and the
 // barriers grow with the waves); valid only for groups of up to 2 query heads, whose
 // registers fit 4 waves per SIMD
+// Split span (cache rows) above which a rows-attention workgroup has 8 waves, not 4:
+// 160 lets the 4097-4352-position decode row's 32 splits of ~136 rows keep 4 waves
+// (10.98 -> 10.86 us per launch, 405.5k -> 407k tok/s on that block's job)
+#ifndef STTD_ATTN_WIDE_ROWS
+#define STTD_ATTN_WIDE_ROWS 160
+#endif
 #ifndef STTD_ATTN_WIDE_NW
 #define STTD_ATTN_WIDE_NW 8
 #endif
@@ -73,7 +79,8 @@ static hipError_t rows_dispatch(const RowsArgs& a, int R, bool wide, hipStream_t
     const int G = a.n_heads / a.kv.n_kv;
     const dim3 grid(R, a.kv.n_kv, a.n_splits);
     // 4 waves per workgroup for groups of up to 2 query heads (the shorter merge tail beats
-    // the extra rows in flight) unless a split spans more than 128 cache rows; 8 for larger groups
+    // the extra rows in flight) unless a split spans more than STTD_ATTN_WIDE_ROWS cache rows; 8 for
+    // larger groups
     const bool pub = a.merge_ctr != nullptr;
 #define ROWS_LAUNCH(G_)                                                                             \
     do {                                                                                            \
@@ -133,7 +140,7 @@ hipError_t launch_attn_rows(const float* q, int64_t ldq, int R, int n_heads, Row
     if (fuse) {
         a.q_gain = fuse->q_gain; a.k_gain = fuse->k_gain; a.eps = fuse->eps; a.rope = fuse->rope;
         a.max_pos = fuse->max_pos;
-        const bool wide = span_bound > 128;
+        const bool wide = span_bound > STTD_ATTN_WIDE_ROWS;
         return gt == W_BF16 ? rows_dispatch_kv<BF16, true>(a, R, wide, s) : rows_dispatch_kv<F32, true>(a, R, wide, s);
     }
     return rows_dispatch_kv<BF16, false>(a, R, false, s);
