@@ -33,8 +33,9 @@ namespace sttd {
 // (prefill rows on an f32 cache).
 //
 // Groups of LPK = d/8 lanes read one cache row (16 bytes per lane for f16,
-// coalesced), two rows per step, and keep a running (max, sum, output) per
-// query head; groups merge by shuffles inside a wave and through LDS across
+// coalesced), RIF rows per step through a register ring two steps deep, and
+// keep a running (max, sum, output) per query head, rescaled once per step;
+// groups merge by shuffles inside a wave and through LDS across
 // waves. One split: the workgroup writes o = O / L. Several: it writes the
 // partial (M, L, O); attn_combine merges the splits into o, or, when no
 // output is given, the consumer (the O-projection GEMV) merges them as it
