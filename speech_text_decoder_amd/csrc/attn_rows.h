@@ -226,8 +226,8 @@ __device__ __forceinline__ void attn_rows_item(const RowsArgs& a, const int r, c
     // trip counts, waited for all loads each step: 18.0 us for 16 rows of 150-1500
     // positions.)
     // (per launch in a 28-block decode of 16 rows at 151-1535 positions, G = 2, two
-    // steps deep: 2 rows per step 16.2 us, 4 rows 16.7, 8 rows 21.1; three or four
-    // steps deep 16.4-17.7)
+    // steps deep: 2 rows per step 16.2 us, 4 rows 16.7, 8 rows 21.1, 1 row 16.9 (a
+    // rescale per row; four steps deep 16.4); three or four steps deep 16.4-17.7)
     // 4-wave workgroups (single rows, and the one-launch projection + attention, whose
     // sums must match the two-launch form bit for bit: the rescale per step makes the
     // rounding depend on the step) keep 4
