@@ -36,7 +36,7 @@ _GEMV_SRC = {"files": ["kernels_gemv.hip", "gemv_ops.h", "common.h"],
              "sha256": "4a9ef155e1b0b895a8b75c409161d378c9d1dcfadbcfa8868d7e479d1951cd19",
              "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
 _QA_SRC = {"files": ["kernels_attn.hip", "attn_rows.h", "gemv_ops.h", "common.h"],
-           "sha256": "f8da20d4821a3c24f9a44df29c6e029bc834ff8051ad054e6e1b5c941e72c8c3",
+           "sha256": "489dfd92a79e7aaaa6db74cc679175c6aaebe43ce03d5e45eb8af3bb055838ab",
            "summary": "profiles/decode_gemv_block_t153_hbm_traffic.md"}
 TRAFFIC = {
     "o_gemv": dict(_GEMV_SRC, rows=1, bytes=8676512),
